@@ -1,0 +1,77 @@
+"""Plant plausible mistakes in copies of the oracle and require the pins to see them.
+
+Every mutant is a textual edit of ``oracle/oracle.c`` (a dropped term, a wrong
+sign, a wrong index or ordering, a transposed operand).  Each mutant is
+compiled into a temporary library and all pin checks run against it in a child
+process; at least one check must fail (or the child must crash).
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+MUTANTS = {
+    "phi_missing_plus_one": [("return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x);")],
+    "la_normalizer_dropped": [("ot[i] = num / den;", "ot[i] = num;")],
+    "la_normalizer_not_accumulated": [("z[c] += fk[c];", "z[c] = fk[c];")],
+    "la_read_before_update": [
+        ("for (int c = 0; c < dk; ++c) {\n                for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] += fk[c] * vt[i];",
+         "for (int c = 0; c < dk; ++c) {\n                for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] += 0.0;"),
+        ("ot[i] = num / den;", "ot[i] = num / den;\n                for (int c = 0; c < dk; ++c) S[(size_t)c * dv + i] += fk[c] * vt[i];"),
+    ],
+    "gla_gate_on_value_index": [("gt[c] * S[(size_t)c * dv + i]", "gt[i % dk] * S[(size_t)c * dv + i]")],
+    "gla_gate_also_decays_new_write": [
+        ("S[(size_t)c * dv + i] = gt[c] * S[(size_t)c * dv + i] + fk[c] * vt[i];",
+         "S[(size_t)c * dv + i] = gt[c] * (S[(size_t)c * dv + i] + fk[c] * vt[i]);")],
+    "gdr_predict_from_undecayed_state": [
+        ("for (size_t e = 0; e < (size_t)dv * dk; ++e) S[e] *= a;", ""),
+        ("S[(size_t)i * dk + c] += e * kt[c];", "S[(size_t)i * dk + c] = a * S[(size_t)i * dk + c] + e * kt[c];"),
+    ],
+    "gdr_error_sign": [("double e = b * (vt[i] - pred[i]);", "double e = b * (vt[i] + pred[i]);")],
+    "gdr_beta_dropped": [("double e = b * (vt[i] - pred[i]);", "double e = (vt[i] - pred[i]);")],
+    "gdr_gate_index_shift": [("const double a = gate[t];", "const double a = gate[t > 0 ? t - 1 : 0];")],
+    "gdr_read_transposed": [("o += S[(size_t)i * dk + c] * qt[c];",
+                             "o += S[(size_t)(c % dv) * dk + (i % dk)] * qt[c];")],
+    "state_written_transposed": [(": S[(size_t)c * dv + i];", ": S[(size_t)(i % dk) * dv + (c % dv)];")],
+    "initial_state_ignored_for_gla": [("if (variant == 2) S[(size_t)i * dk + c] = s;\n            else              S[(size_t)c * dv + i] = s;",
+                                       "if (variant == 2) S[(size_t)i * dk + c] = s;\n            else              S[(size_t)c * dv + i] = (variant == 1) ? 0.0 : s;")],
+}
+
+CHILD = r"""
+import sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import oracle
+from oracle_pin_checks import ALL_CHECKS
+orc = oracle.load({lib!r})
+failed = []
+for chk in ALL_CHECKS:
+    try:
+        chk(orc)
+    except Exception as e:
+        failed.append(chk.__name__)
+print("FAILED:" + ",".join(failed))
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(SRC).read()
+    for old, new in MUTANTS[name]:
+        assert src.count(old) == 1, "mutation target not found exactly once: %r" % old
+        src = src.replace(old, new)
+    msrc = tmp_path / "oracle_mutant.c"
+    msrc.write_text(src)
+    lib = oracle.build(force=True, src=str(msrc), out=str(tmp_path / "libmutant.so"))
+    code = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib)
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    if res.returncode != 0:
+        return  # a crash is a detection too
+    line = [l for l in res.stdout.splitlines() if l.startswith("FAILED:")][-1]
+    failed = [f for f in line[len("FAILED:"):].split(",") if f]
+    assert failed, "mutant %s passed every pin" % name
