@@ -1,0 +1,120 @@
+"""Causal linear attention for AMD MI355X (gfx950): Python binding of libla.so.
+
+The entry points carry the names of the C ABI in include/la.h and only
+marshal arguments: shapes become an ``la_desc``, torch tensors become device
+pointers, torch's current HIP stream becomes the stream argument, and missing
+outputs are allocated with torch.  Every step of the computation runs in the
+library's HIP kernels; there is no other code path.
+
+    out, S_T, z_T = la_chunk_fwd(q, k, v, variant=LA_GATED_DELTA, gate=g, beta=b)
+    o = la_decode_step(q, k, v, S, variant=LA_GATED_DELTA, gate=g, beta=b)
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from ._lib import (LA_BF16, LA_EHIP, LA_EINVAL, LA_EUNSUPPORTED, LA_F32, LA_GATED,  # noqa: F401
+                   LA_GATED_DELTA, LA_NORMALIZED, LA_OK, LA_PHI_ELU1, LA_PHI_IDENTITY,
+                   LaDesc, LaError, check, load)
+
+__all__ = ["la_chunk_fwd", "la_decode_step", "la_chunk_fwd_workspace", "la_status_str",
+           "la_last_error", "la_abi_version", "make_desc", "LaDesc", "LaError",
+           "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_F32", "LA_BF16",
+           "LA_PHI_IDENTITY", "LA_PHI_ELU1"]
+
+_DTYPES = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
+
+
+def _default_phi(variant: int) -> int:
+    return LA_PHI_IDENTITY if variant == LA_GATED_DELTA else LA_PHI_ELU1
+
+
+def make_desc(variant: int, dtype: int, B: int, H: int, T: int, d_k: int, d_v: int,
+              chunk: int = 0, phi: int | None = None) -> LaDesc:
+    return LaDesc(variant, dtype, _default_phi(variant) if phi is None else phi,
+                  B, H, T, d_k, d_v, chunk)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor or None")
+    if not t.is_cuda:
+        raise ValueError("tensors must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def la_abi_version() -> int:
+    return load().la_abi_version()
+
+
+def la_status_str(status: int) -> str:
+    return load().la_status_str(status).decode()
+
+
+def la_last_error() -> str:
+    return load().la_last_error().decode()
+
+
+def la_chunk_fwd_workspace(desc: LaDesc) -> int:
+    return int(load().la_chunk_fwd_workspace(ctypes.byref(desc)))
+
+
+def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, chunk=0,
+                 phi=None, out=None, S_T=None, z_T=None, return_state=True, stream=None):
+    """Chunkwise-parallel forward (C: ``la_chunk_fwd``).
+
+    q, k (B,H,T,d_k) and v (B,H,T,d_v) in float32 or bfloat16; gate / beta /
+    S0 / z0 float32 as include/la.h describes.  Outputs that are not passed
+    are allocated: out in q's dtype; S_T (and z_T for LA_NORMALIZED) float32
+    unless return_state is False.  Returns (out, S_T, z_T).
+    """
+    lib = load()
+    if q.dtype not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    B, H, T, d_k = q.shape
+    d_v = v.shape[-1]
+    desc = make_desc(variant, _DTYPES[q.dtype], B, H, T, d_k, d_v, chunk, phi)
+    if out is None:
+        out = torch.empty((B, H, T, d_v), dtype=q.dtype, device=q.device)
+    if return_state and S_T is None:
+        S_T = torch.empty((B, H, d_v, d_k), dtype=torch.float32, device=q.device)
+    if return_state and variant == LA_NORMALIZED and z_T is None:
+        z_T = torch.empty((B, H, d_k), dtype=torch.float32, device=q.device)
+    ws_bytes = int(lib.la_chunk_fwd_workspace(ctypes.byref(desc)))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    check(lib.la_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                           _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_T), _ptr(z_T), _ptr(ws),
+                           ws_bytes, _stream(stream)))
+    return out, S_T, z_T
+
+
+def la_decode_step(q, k, v, S, *, variant, gate=None, beta=None, z=None, phi=None,
+                   out=None, stream=None):
+    """One recurrent step, updating S (and z) in place (C: ``la_decode_step``).
+
+    q, k (B,H,d_k), v (B,H,d_v) in float32 or bfloat16; S (B,H,d_v,d_k)
+    float32; gate / beta / z as include/la.h describes.  Returns out (B,H,d_v).
+    """
+    lib = load()
+    if q.dtype not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    B, H, d_k = q.shape
+    d_v = v.shape[-1]
+    desc = make_desc(variant, _DTYPES[q.dtype], B, H, 1, d_k, d_v, 0, phi)
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=q.device)
+    check(lib.la_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                             _ptr(beta), _ptr(S), _ptr(z), _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,226 @@
+// la_api.cpp -- the C entry points of include/la.h.
+//
+// Every argument is checked on the host before any HIP call; a failing check
+// returns LA_EINVAL / LA_EUNSUPPORTED, records a message for la_last_error()
+// and launches nothing.  Valid calls are forwarded to the kernel launchers
+// on the caller's stream without host synchronization or allocation.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "la_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+la_status fail(la_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool supported_head_size(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Range {
+    const char *name;
+    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
+};
+
+Range range(const char *name, const void *p, size_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, p ? lo + bytes : lo};
+}
+
+bool overlaps(const Range &a, const Range &b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool misaligned(const void *p, uintptr_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+// Checks shared by both entry points.  n_tok = tokens per head that the call reads.
+la_status check_desc(const la_desc *d, bool chunked) {
+    if (!d) return fail(LA_EINVAL, "desc is NULL");
+    if (d->variant < LA_NORMALIZED || d->variant > LA_GATED_DELTA)
+        return fail(LA_EINVAL, "variant %d is not a la_variant", d->variant);
+    if (d->dtype != LA_F32 && d->dtype != LA_BF16) return fail(LA_EINVAL, "dtype %d is not a la_dtype", d->dtype);
+    if (d->phi != LA_PHI_IDENTITY && d->phi != LA_PHI_ELU1) return fail(LA_EINVAL, "phi %d is not a la_phi", d->phi);
+    if (d->variant == LA_NORMALIZED && d->phi != LA_PHI_ELU1)
+        return fail(LA_EINVAL, "LA_NORMALIZED needs LA_PHI_ELU1 (the normalizer needs positive features)");
+    if (d->variant == LA_GATED_DELTA && d->phi != LA_PHI_IDENTITY)
+        return fail(LA_EINVAL, "LA_GATED_DELTA needs LA_PHI_IDENTITY (keys are unit vectors)");
+    if (d->B < 0 || d->H < 0) return fail(LA_EINVAL, "B=%d, H=%d must be >= 0", d->B, d->H);
+    if (chunked && d->T < 0) return fail(LA_EINVAL, "T=%d must be >= 0", d->T);
+    if (d->d_k <= 0 || d->d_v <= 0) return fail(LA_EINVAL, "d_k=%d, d_v=%d must be > 0", d->d_k, d->d_v);
+    if (!supported_head_size(d->d_k) || !supported_head_size(d->d_v))
+        return fail(LA_EUNSUPPORTED, "head sizes d_k=%d, d_v=%d: supported are 16, 32, 64, 128", d->d_k, d->d_v);
+    if (chunked) {
+        if (d->chunk < 0) return fail(LA_EINVAL, "chunk=%d must be >= 0", d->chunk);
+        if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
+            return fail(LA_EUNSUPPORTED, "chunk=%d: supported are 0 (= 64), 16, 32, 64", d->chunk);
+    }
+    // element counts must stay far from 64-bit overflow
+    const double elems = static_cast<double>(d->B) * d->H * (chunked ? (d->T > 0 ? d->T : 1) : 1) *
+                         (d->d_k > d->d_v ? d->d_k : d->d_v);
+    if (elems > 4.0e18) return fail(LA_EINVAL, "problem too large");
+    return LA_OK;
+}
+
+la_status check_role(const la_desc *d, const float *gate, const float *beta, const float *z_in,
+                     const float *z_out, bool need_data) {
+    if (d->variant == LA_NORMALIZED) {
+        if (gate) return fail(LA_EINVAL, "gate must be NULL for LA_NORMALIZED");
+        if (beta) return fail(LA_EINVAL, "beta must be NULL for LA_NORMALIZED");
+    } else {
+        if (z_in || z_out) return fail(LA_EINVAL, "z must be NULL unless the variant is LA_NORMALIZED");
+        if (need_data && !gate) return fail(LA_EINVAL, "gate is required for this variant");
+        if (d->variant == LA_GATED && beta) return fail(LA_EINVAL, "beta must be NULL for LA_GATED");
+        if (d->variant == LA_GATED_DELTA && need_data && !beta)
+            return fail(LA_EINVAL, "beta is required for LA_GATED_DELTA");
+    }
+    return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+const char *la_status_str(la_status s) {
+    switch (s) {
+        case LA_OK: return "LA_OK: success";
+        case LA_EINVAL: return "LA_EINVAL: invalid argument";
+        case LA_EUNSUPPORTED: return "LA_EUNSUPPORTED: no kernel for this configuration";
+        case LA_EHIP: return "LA_EHIP: HIP runtime error";
+    }
+    return "unknown la_status";
+}
+
+const char *la_last_error(void) { return g_last_error; }
+
+size_t la_chunk_fwd_workspace(const la_desc *d) {
+    if (check_desc(d, true) != LA_OK) return 0;
+    la::ChunkArgs a = {};
+    a.variant = d->variant; a.dtype = d->dtype; a.phi = d->phi;
+    a.B = d->B; a.H = d->H; a.T = d->T; a.d_k = d->d_k; a.d_v = d->d_v;
+    a.chunk = d->chunk ? d->chunk : 64;
+    return la::chunk_workspace_bytes(a);
+}
+
+la_status la_chunk_fwd(const la_desc *d, const void *q, const void *k, const void *v,
+                       const float *gate, const float *beta, const float *S0, const float *z0,
+                       void *out, float *S_T, float *z_T, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+    g_last_error[0] = '\0';
+    la_status st = check_desc(d, true);
+    if (st != LA_OK) return st;
+    const size_t heads = static_cast<size_t>(d->B) * d->H;
+    const size_t tok = heads * static_cast<size_t>(d->T);
+    const bool need_data = tok > 0;
+    st = check_role(d, gate, beta, z0, z_T, need_data);
+    if (st != LA_OK) return st;
+    if (need_data && (!q || !k || !v || !out)) return fail(LA_EINVAL, "q, k, v and out are required when B*H*T > 0");
+
+    const size_t esz = d->dtype == LA_BF16 ? 2 : 4;
+    const void *ptrs[] = {q, k, v, gate, beta, S0, z0, out, S_T, z_T, workspace};
+    const char *names[] = {"q", "k", "v", "gate", "beta", "S0", "z0", "out", "S_T", "z_T", "workspace"};
+    for (int i = 0; i < 11; ++i) {
+        // per-token gate / beta of the gated delta rule are read with scalar loads
+        uintptr_t al = (i == 3 && d->variant == LA_GATED_DELTA) || i == 4 ? 4 : 16;
+        if (misaligned(ptrs[i], al)) return fail(LA_EINVAL, "%s is not %d-byte aligned", names[i], (int)al);
+    }
+
+    la::ChunkArgs a = {};
+    a.variant = d->variant; a.dtype = d->dtype; a.phi = d->phi;
+    a.B = d->B; a.H = d->H; a.T = d->T; a.d_k = d->d_k; a.d_v = d->d_v;
+    a.chunk = d->chunk ? d->chunk : 64;
+    const size_t need_ws = la::chunk_workspace_bytes(a);
+    if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+        return fail(LA_EINVAL, "workspace of %zu bytes required, %zu given", need_ws, workspace ? workspace_bytes : 0);
+
+    const size_t dk = d->d_k, dv = d->d_v;
+    const Range r_q = range("q", q, tok * dk * esz), r_k = range("k", k, tok * dk * esz);
+    const Range r_v = range("v", v, tok * dv * esz);
+    const Range r_g = range("gate", gate, d->variant == LA_GATED ? tok * dk * 4 : tok * 4);
+    const Range r_b = range("beta", beta, tok * 4);
+    const Range r_s0 = range("S0", S0, heads * dv * dk * 4), r_z0 = range("z0", z0, heads * dk * 4);
+    const Range r_o = range("out", out, tok * dv * esz);
+    const Range r_st = range("S_T", S_T, heads * dv * dk * 4), r_zt = range("z_T", z_T, heads * dk * 4);
+    const Range r_ws = range("workspace", workspace, need_ws);
+    const Range inputs[] = {r_q, r_k, r_v, r_g, r_b, r_s0, r_z0};
+    const Range outputs[] = {r_o, r_st, r_zt, r_ws};
+    for (const Range &o : outputs) {
+        for (const Range &i : inputs) {
+            if (!overlaps(o, i)) continue;
+            // the final state may replace the initial one exactly (in-place carry)
+            if ((o.name == r_st.name && i.name == r_s0.name && o.lo == i.lo) ||
+                (o.name == r_zt.name && i.name == r_z0.name && o.lo == i.lo))
+                continue;
+            return fail(LA_EINVAL, "%s overlaps %s", o.name, i.name);
+        }
+        for (const Range &o2 : outputs)
+            if (&o2 != &o && overlaps(o, o2)) return fail(LA_EINVAL, "%s overlaps %s", o.name, o2.name);
+    }
+    if (heads == 0) return LA_OK;
+
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.S0 = S0; a.z0 = z0;
+    a.out = out; a.S_T = S_T; a.z_T = z_T; a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = la::launch_chunk(a);
+    if (e != hipSuccess) return fail(LA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return LA_OK;
+}
+
+la_status la_decode_step(const la_desc *d, const void *q, const void *k, const void *v,
+                         const float *gate, const float *beta, float *S, float *z, void *out,
+                         void *stream) {
+    g_last_error[0] = '\0';
+    la_status st = check_desc(d, false);
+    if (st != LA_OK) return st;
+    const size_t heads = static_cast<size_t>(d->B) * d->H;
+    const bool need_data = heads > 0;
+    st = check_role(d, gate, beta, z, z, need_data);
+    if (st != LA_OK) return st;
+    if (need_data && (!q || !k || !v || !out || !S)) return fail(LA_EINVAL, "q, k, v, S and out are required");
+    if (need_data && d->variant == LA_NORMALIZED && !z) return fail(LA_EINVAL, "z is required for LA_NORMALIZED");
+
+    const size_t esz = d->dtype == LA_BF16 ? 2 : 4;
+    const void *ptrs[] = {q, k, v, gate, beta, S, z, out};
+    const char *names[] = {"q", "k", "v", "gate", "beta", "S", "z", "out"};
+    for (int i = 0; i < 8; ++i) {
+        uintptr_t al = (i == 3 && d->variant == LA_GATED_DELTA) || i == 4 ? 4 : 16;
+        if (i == 7) al = esz;  // one output element per state row
+        if (misaligned(ptrs[i], al)) return fail(LA_EINVAL, "%s is not %d-byte aligned", names[i], (int)al);
+    }
+    const size_t dk = d->d_k, dv = d->d_v;
+    const Range r_q = range("q", q, heads * dk * esz), r_k = range("k", k, heads * dk * esz);
+    const Range r_v = range("v", v, heads * dv * esz);
+    const Range r_g = range("gate", gate, d->variant == LA_GATED ? heads * dk * 4 : heads * 4);
+    const Range r_b = range("beta", beta, heads * 4);
+    const Range r_s = range("S", S, heads * dv * dk * 4), r_z = range("z", z, heads * dk * 4);
+    const Range r_o = range("out", out, heads * dv * esz);
+    const Range inputs[] = {r_q, r_k, r_v, r_g, r_b};
+    const Range outputs[] = {r_s, r_z, r_o};
+    for (const Range &o : outputs) {
+        for (const Range &i : inputs)
+            if (overlaps(o, i)) return fail(LA_EINVAL, "%s overlaps %s", o.name, i.name);
+        for (const Range &o2 : outputs)
+            if (&o2 != &o && overlaps(o, o2)) return fail(LA_EINVAL, "%s overlaps %s", o.name, o2.name);
+    }
+    if (heads == 0) return LA_OK;
+
+    la::DecodeArgs a = {};
+    a.variant = d->variant; a.dtype = d->dtype; a.phi = d->phi;
+    a.B = d->B; a.H = d->H; a.d_k = d->d_k; a.d_v = d->d_v;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.S = S; a.z = z; a.out = out;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = la::launch_decode(a);
+    if (e != hipSuccess) return fail(LA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return LA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,192 @@
+// la_decode.hip -- one-token recurrent step for the three variants (gfx950).
+//
+// The step is bandwidth-bound: every head's d_v x d_k float32 state is read
+// once and written once, with O(d_k d_v) arithmetic (page "Beyond -- Linear
+// attention and recurrent memory", section "The big idea": per-token state
+// work independent of history length).  The kernel streams the state through
+// registers: a state row of d_k floats is split over G = d_k/8 lanes (eight
+// consecutive floats, two 16-byte loads per lane), every row of a workgroup
+// is loaded before any arithmetic so that all of a lane's loads are in
+// flight together, and the two row dot products a step needs are reduced
+// across the G lanes with lane shuffles.  No LDS, and no barrier except the
+// one the normalized variant needs before it overwrites the shared z.
+//
+// Per-row arithmetic (row i of the d_v x d_k state, all in float32):
+//   gated delta rule (page "Linear Attention", decay first, then predict):
+//     p = S_i.k, r = S_i.q, u = beta (v_i - g p),
+//     S_i <- g S_i + u k,  o_i = g r + u (k.q)      (= S_new,i . q)
+//   gated linear attention (page "Ch. 11 Linear attention and Hyena", 11.3):
+//     r = S_i.(gamma o phi(q)),  S_i <- S_i o gamma + v_i phi(k),
+//     o_i = r + v_i (phi(k).phi(q))                 (= S_new,i . phi(q))
+//   normalized (page "Beyond -- Linear attention and recurrent memory"):
+//     r = S_i.phi(q),  S_i <- S_i + v_i phi(k),  z <- z + phi(k),
+//     o_i = (r + v_i (phi(k).phi(q))) / (z_old.phi(q) + phi(k).phi(q))
+#include "la_internal.hpp"
+
+namespace la {
+
+template <int VAR, class DT, int DK, int DV, int PHI>
+__global__ __launch_bounds__(256) void decode_kernel(
+    const typename DT::storage *__restrict__ q, const typename DT::storage *__restrict__ k,
+    const typename DT::storage *__restrict__ v, const float *__restrict__ gate,
+    const float *__restrict__ beta, float *__restrict__ S, float *__restrict__ z,
+    typename DT::storage *__restrict__ out, int64_t n_heads) {
+    constexpr int G = DK / 8;                                // lanes per state row
+    constexpr int GROUPS = 256 / G;                          // row groups per workgroup
+    constexpr int HPW = GROUPS >= DV ? GROUPS / DV : 1;      // heads per workgroup
+    constexpr int GPH = GROUPS / HPW;                        // groups per head
+    constexpr int RPG = DV / GPH;                            // rows per group
+    static_assert(DK % 8 == 0 && G <= 64 && RPG >= 1 && RPG * GPH == DV, "decode tiling");
+
+    const int tid = threadIdx.x;
+    const int grp = tid / G;
+    const int c0 = (tid % G) * 8;
+    const int64_t head = static_cast<int64_t>(blockIdx.x) * HPW + grp / GPH;
+    const int row0 = grp % GPH;
+    const bool active = head < n_heads;
+    const int64_t h = active ? head : 0;   // inactive lanes compute on head 0 and store nothing
+
+    float kk[8], qq[8];
+    load8(k + h * DK + c0, kk);
+    load8(q + h * DK + c0, qq);
+    float s[RPG][8];
+    float vv[RPG];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        load8(S + (h * DV + row0 + r * GPH) * DK + c0, s[r]);
+        vv[r] = load1(v + h * DV + row0 + r * GPH);
+    }
+
+    if constexpr (VAR == LA_GATED_DELTA) {
+        const float g = gate[h];
+        const float b = beta[h];
+        float kq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) kq += kk[c] * qq[c];
+        kq = group_sum<G>(kq);
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) {
+            float p = 0.f, rq = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) { p += s[r][c] * kk[c]; rq += s[r][c] * qq[c]; }
+            p = group_sum<G>(p);
+            rq = group_sum<G>(rq);
+            const float u = b * (vv[r] - g * p);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s[r][c] = g * s[r][c] + u * kk[c];
+            vv[r] = g * rq + u * kq;   // output
+        }
+    } else {
+        float fk[8], fq[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { fk[c] = apply_phi<PHI>(kk[c]); fq[c] = apply_phi<PHI>(qq[c]); }
+        float kq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) kq += fk[c] * fq[c];
+        kq = group_sum<G>(kq);
+        if constexpr (VAR == LA_GATED) {
+            float gm[8], rq_w[8];
+            load8(gate + h * DK + c0, gm);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) rq_w[c] = gm[c] * fq[c];
+#pragma unroll
+            for (int r = 0; r < RPG; ++r) {
+                float rq = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) rq += s[r][c] * rq_w[c];
+                rq = group_sum<G>(rq);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) s[r][c] = s[r][c] * gm[c] + vv[r] * fk[c];
+                vv[r] = rq + vv[r] * kq;
+            }
+        } else {
+            float zz[8];
+            load8(z + h * DK + c0, zz);
+            float zq = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) zq += zz[c] * fq[c];
+            zq = group_sum<G>(zq);
+            const float inv_den = 1.f / (zq + kq);
+#pragma unroll
+            for (int r = 0; r < RPG; ++r) {
+                float rq = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) rq += s[r][c] * fq[c];
+                rq = group_sum<G>(rq);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) s[r][c] = s[r][c] + vv[r] * fk[c];
+                vv[r] = (rq + vv[r] * kq) * inv_den;
+            }
+            // every group of the head has read z; only then may row 0's group overwrite it
+            __syncthreads();
+            if (active && row0 == 0) {
+                float4 *zp = reinterpret_cast<float4 *>(z + h * DK + c0);
+                zp[0] = make_float4(zz[0] + fk[0], zz[1] + fk[1], zz[2] + fk[2], zz[3] + fk[3]);
+                zp[1] = make_float4(zz[4] + fk[4], zz[5] + fk[5], zz[6] + fk[6], zz[7] + fk[7]);
+            }
+        }
+    }
+
+    if (!active) return;
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) {
+        float4 *sp = reinterpret_cast<float4 *>(S + (h * DV + row0 + r * GPH) * DK + c0);
+        sp[0] = make_float4(s[r][0], s[r][1], s[r][2], s[r][3]);
+        sp[1] = make_float4(s[r][4], s[r][5], s[r][6], s[r][7]);
+        if (c0 == 0) store1(out + h * DV + row0 + r * GPH, vv[r]);
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <int VAR, class DT, int DK, int DV, int PHI>
+static hipError_t launch_decode_t(const DecodeArgs &a) {
+    constexpr int G = DK / 8;
+    constexpr int GROUPS = 256 / G;
+    constexpr int HPW = GROUPS >= DV ? GROUPS / DV : 1;
+    const int64_t n_heads = static_cast<int64_t>(a.B) * a.H;
+    const int64_t blocks = (n_heads + HPW - 1) / HPW;
+    typedef typename DT::storage T;
+    hipLaunchKernelGGL((decode_kernel<VAR, DT, DK, DV, PHI>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(256), 0, a.stream, static_cast<const T *>(a.q),
+                       static_cast<const T *>(a.k), static_cast<const T *>(a.v), a.gate, a.beta,
+                       a.S, a.z, static_cast<T *>(a.out), n_heads);
+    return hipGetLastError();
+}
+
+template <int VAR, class DT, int DK, int PHI>
+static hipError_t decode_dv(const DecodeArgs &a) {
+    switch (a.d_v) {
+        case 16: return launch_decode_t<VAR, DT, DK, 16, PHI>(a);
+        case 32: return launch_decode_t<VAR, DT, DK, 32, PHI>(a);
+        case 64: return launch_decode_t<VAR, DT, DK, 64, PHI>(a);
+        case 128: return launch_decode_t<VAR, DT, DK, 128, PHI>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int VAR, class DT, int PHI>
+static hipError_t decode_dk(const DecodeArgs &a) {
+    switch (a.d_k) {
+        case 16: return decode_dv<VAR, DT, 16, PHI>(a);
+        case 32: return decode_dv<VAR, DT, 32, PHI>(a);
+        case 64: return decode_dv<VAR, DT, 64, PHI>(a);
+        case 128: return decode_dv<VAR, DT, 128, PHI>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class DT>
+static hipError_t decode_variant(const DecodeArgs &a) {
+    if (a.variant == LA_NORMALIZED) return decode_dk<LA_NORMALIZED, DT, LA_PHI_ELU1>(a);
+    if (a.variant == LA_GATED_DELTA) return decode_dk<LA_GATED_DELTA, DT, LA_PHI_IDENTITY>(a);
+    if (a.phi == LA_PHI_ELU1) return decode_dk<LA_GATED, DT, LA_PHI_ELU1>(a);
+    return decode_dk<LA_GATED, DT, LA_PHI_IDENTITY>(a);
+}
+
+hipError_t launch_decode(const DecodeArgs &a) {
+    if (a.dtype == LA_BF16) return decode_variant<BF16>(a);
+    return decode_variant<F32>(a);
+}
+
+}  // namespace la

@@ -1,0 +1,39 @@
+// la_internal.hpp -- argument bundles passed from the validated C entry points
+// to the kernel launchers.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "la.h"
+#include "la_common.hpp"
+
+namespace la {
+
+struct DecodeArgs {
+    int variant, dtype, phi;
+    int B, H, d_k, d_v;
+    const void *q, *k, *v;
+    const float *gate, *beta;
+    float *S, *z;
+    void *out;
+    hipStream_t stream;
+};
+
+struct ChunkArgs {
+    int variant, dtype, phi;
+    int B, H, T, d_k, d_v, chunk;
+    const void *q, *k, *v;
+    const float *gate, *beta;
+    const float *S0, *z0;
+    void *out;
+    float *S_T, *z_T;
+    void *workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_chunk(const ChunkArgs &a);
+size_t chunk_workspace_bytes(const ChunkArgs &a);
+
+}  // namespace la

@@ -1,0 +1,179 @@
+/*
+ * la.h -- C ABI of the causal linear-attention library for AMD MI355X (gfx950).
+ *
+ * The operator replaces softmax attention with a fixed-size matrix state that
+ * is updated once per token.  Three variants are provided:
+ *
+ *   LA_NORMALIZED   normalized kernel linear attention with phi(x) = elu(x)+1:
+ *                   S_t = S_{t-1} + v_t phi(k_t)^T,  z_t = z_{t-1} + phi(k_t),
+ *                   o_t = S_t phi(q_t) / (z_t . phi(q_t)).
+ *                   Page "Beyond -- Linear attention and recurrent memory",
+ *                   section "The big idea"; page "Linear Attention",
+ *                   normalized kernel formulation.
+ *   LA_GATED        gated linear attention with a per-step, per-key-channel
+ *                   decay gamma_t in (0,1]^{d_k} and no normalizer:
+ *                   S_t = S_{t-1} diag(gamma_t) + v_t phi(k_t)^T,
+ *                   o_t = S_t phi(q_t).
+ *                   Page "Ch. 11 Linear attention and Hyena", section 11.3
+ *                   (GLA gate, cumulative log-gate rescaling) and the solution
+ *                   to Exercise 11.5.
+ *   LA_GATED_DELTA  gated delta rule with unit-norm keys, scalar gate g_t and
+ *                   write strength beta_t:
+ *                   S_t = g_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *                   o_t = S_t q_t.
+ *                   Page "Module 18 Beyond attention", section 18.2; page
+ *                   "Linear Attention", gated-delta-rule formulation.
+ *
+ * Every token is "update first, then read": a token attends to itself
+ * (page "Beyond -- Linear attention and recurrent memory", section
+ * "Pitfalls to expect").
+ *
+ * CONVENTIONS (all entry points)
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or retains memory, and keeps no global
+ *     state.  Calls are thread-safe.
+ *   - Tensors are dense, row-major (C order), 16-byte aligned.
+ *   - Per-token tensors are (B, H, T, d).  The state S of every variant is
+ *     (B, H, d_v, d_k) float32 (row = value channel, column = key channel);
+ *     the normalizer z is (B, H, d_k) float32.
+ *   - q, k, v and out have the element type `dtype` (LA_F32 or LA_BF16);
+ *     gates, beta and the state are always float32.  Arithmetic is float32;
+ *     matrix products of bf16 inputs run on bf16 matrix cores with float32
+ *     accumulation.
+ *   - Arguments are validated synchronously on the host BEFORE any HIP call;
+ *     a failing call launches nothing and returns LA_EINVAL or
+ *     LA_EUNSUPPORTED; la_last_error() then describes the failed check.
+ *   - Execution is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No host synchronization happens inside a call.  A launch
+ *     failure returns LA_EHIP.
+ *   - Documented preconditions that are NOT checked (values live on the
+ *     device): gate entries in (0, 1]; beta in [0, 1]; keys of
+ *     LA_GATED_DELTA of unit length; z0 >= 0 for LA_NORMALIZED; for
+ *     LA_GATED the product of one channel's gates over any 16 consecutive
+ *     tokens of a chunk is at least 1e-30 (the chunked forward factors the
+ *     decay through per-16-token reference points; past that range float32
+ *     cannot hold the factors).
+ */
+#ifndef LA_H
+#define LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_ABI_VERSION 1
+
+typedef enum {
+    LA_OK = 0,
+    LA_EINVAL = 1,        /* bad argument: null pointer, bad size, bad combination, misalignment, aliasing */
+    LA_EUNSUPPORTED = 2,  /* valid request this build has no kernel for (head size, chunk size) */
+    LA_EHIP = 3           /* the HIP runtime reported an error at launch */
+} la_status;
+
+typedef enum { LA_NORMALIZED = 0, LA_GATED = 1, LA_GATED_DELTA = 2 } la_variant;
+typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+typedef enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1 } la_phi;
+
+/*
+ * Problem descriptor.
+ *   variant  la_variant.
+ *   dtype    la_dtype of q, k, v, out.
+ *   phi      feature map on q and k.  LA_NORMALIZED requires LA_PHI_ELU1 (the
+ *            normalizer needs positive features); LA_GATED accepts either;
+ *            LA_GATED_DELTA requires LA_PHI_IDENTITY.
+ *   B, H     batch size and heads, >= 0.
+ *   T        tokens per sequence, >= 0 (ignored by la_decode_step).
+ *   d_k      key/query head size; d_v value head size.  Supported:
+ *            d_k in {16, 32, 64, 128}, d_v in {16, 32, 64, 128}.
+ *   chunk    chunk length of la_chunk_fwd: 0 (= 64), 16, 32 or 64.  The
+ *            result does not depend on it beyond floating-point rounding.
+ */
+typedef struct {
+    int32_t variant;
+    int32_t dtype;
+    int32_t phi;
+    int32_t B, H, T;
+    int32_t d_k, d_v;
+    int32_t chunk;
+} la_desc;
+
+/*
+ * Bytes of device workspace la_chunk_fwd needs for `desc` (0 when none).
+ * Returns 0 for an invalid descriptor as well; la_chunk_fwd reports it.
+ */
+size_t la_chunk_fwd_workspace(const la_desc *desc);
+
+/*
+ * Chunkwise-parallel forward over whole sequences.
+ *
+ * The sequence is cut into chunks of `chunk` tokens (the last may be
+ * ragged).  Inside a chunk, tokens interact through masked score matrices on
+ * the matrix cores; across chunks only the fixed-size state is carried.
+ * This is the parallel/recurrent equivalence of page "Ch. 11 Linear
+ * attention and Hyena", sections 11.2-11.3, applied per chunk; the gated
+ * delta rule folds its in-chunk dependencies into one unit-lower-triangular
+ * solve per chunk.
+ *
+ *   q     (B,H,T,d_k) dtype.            k (B,H,T,d_k) dtype.
+ *   v     (B,H,T,d_v) dtype.
+ *   gate  LA_GATED: gamma (B,H,T,d_k) f32; LA_GATED_DELTA: g (B,H,T) f32;
+ *         LA_NORMALIZED: must be NULL.
+ *   beta  LA_GATED_DELTA: (B,H,T) f32; otherwise must be NULL.
+ *   S0    initial state (B,H,d_v,d_k) f32, or NULL for zeros.
+ *   z0    LA_NORMALIZED: initial normalizer (B,H,d_k) f32 or NULL for
+ *         zeros; otherwise must be NULL.
+ *   out   (B,H,T,d_v) dtype, written.  Must not overlap any other argument.
+ *   S_T   final state (B,H,d_v,d_k) f32, written, or NULL.  May be the same
+ *         pointer as S0 (in-place carry); must not partially overlap it.
+ *   z_T   LA_NORMALIZED: final normalizer (B,H,d_k) f32 or NULL; may equal
+ *         z0.  Otherwise must be NULL.
+ *   workspace, workspace_bytes
+ *         caller-owned device scratch of at least la_chunk_fwd_workspace()
+ *         bytes (may be NULL when that is 0).
+ *   stream  hipStream_t to run on.
+ */
+la_status la_chunk_fwd(const la_desc *desc,
+                       const void *q, const void *k, const void *v,
+                       const float *gate, const float *beta,
+                       const float *S0, const float *z0,
+                       void *out, float *S_T, float *z_T,
+                       void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * One recurrent decode step for every (b, h): reads one token, updates the
+ * state in place, writes one output.  The per-token arithmetic is the
+ * recurrence of the variant (see the top of this file), with the state
+ * streamed through registers once.  desc->T and desc->chunk are ignored.
+ *
+ *   q, k  (B,H,d_k) dtype.   v (B,H,d_v) dtype.
+ *   gate  LA_GATED: gamma (B,H,d_k) f32; LA_GATED_DELTA: g (B,H) f32;
+ *         LA_NORMALIZED: must be NULL.
+ *   beta  LA_GATED_DELTA: (B,H) f32; otherwise must be NULL.
+ *   S     (B,H,d_v,d_k) f32, read and overwritten with the new state.
+ *   z     LA_NORMALIZED: (B,H,d_k) f32, read and overwritten; otherwise NULL.
+ *   out   (B,H,d_v) dtype, written; must not overlap any other argument.
+ */
+la_status la_decode_step(const la_desc *desc,
+                         const void *q, const void *k, const void *v,
+                         const float *gate, const float *beta,
+                         float *S, float *z, void *out,
+                         void *stream);
+
+/* Static description of a status code. */
+const char *la_status_str(la_status status);
+
+/* Description of the last failed check on the calling thread ("" if none). */
+const char *la_last_error(void);
+
+/* LA_ABI_VERSION of the loaded library. */
+int la_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LA_H */

@@ -1,0 +1,164 @@
+"""The C ABI on the host: exported symbols and synchronous argument checks.
+
+Every call here fails validation, which happens before any HIP call, so these
+tests run without a GPU.  Pointers are fake device addresses that validation
+only compares and never dereferences.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_causal_amd as la
+from gated_delta_rule_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from gated_delta_rule_causal_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings(lib):
+    assert la.la_abi_version() == _lib.LA_ABI_VERSION
+    for s in (la.LA_OK, la.LA_EINVAL, la.LA_EUNSUPPORTED, la.LA_EHIP):
+        assert la.la_status_str(s).startswith("LA_")
+    assert "unknown" in la.la_status_str(99)
+
+
+BASE = 1 << 32          # fake, 256-byte aligned device addresses
+STEP = 1 << 28
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(BASE + i * STEP + off)
+
+
+def call_chunk(lib, desc, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), gate=None, beta=None, S0=None, z0=None,
+                out=fake(3), S_T=fake(4), z_T=None, ws=None, ws_bytes=0)
+    if desc is not None and desc.variant == la.LA_GATED:
+        args["gate"] = fake(5)
+    if desc is not None and desc.variant == la.LA_GATED_DELTA:
+        args["gate"], args["beta"] = fake(5), fake(6)
+    args.update(kw)
+    d = ctypes.byref(desc) if desc is not None else None
+    return lib.la_chunk_fwd(d, args["q"], args["k"], args["v"], args["gate"], args["beta"],
+                            args["S0"], args["z0"], args["out"], args["S_T"], args["z_T"],
+                            args["ws"], args["ws_bytes"], None)
+
+
+def call_decode(lib, desc, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), gate=None, beta=None, S=fake(4), z=None,
+                out=fake(3))
+    if desc.variant == la.LA_NORMALIZED:
+        args["z"] = fake(7)
+    if desc.variant == la.LA_GATED:
+        args["gate"] = fake(5)
+    if desc.variant == la.LA_GATED_DELTA:
+        args["gate"], args["beta"] = fake(5), fake(6)
+    args.update(kw)
+    return lib.la_decode_step(ctypes.byref(desc), args["q"], args["k"], args["v"], args["gate"],
+                              args["beta"], args["S"], args["z"], args["out"], None)
+
+
+def D(variant=la.LA_GATED_DELTA, **kw):
+    p = dict(dtype=la.LA_BF16, B=2, H=3, T=100, d_k=64, d_v=64, chunk=0, phi=None)
+    p.update(kw)
+    return la.make_desc(variant, p["dtype"], p["B"], p["H"], p["T"], p["d_k"], p["d_v"],
+                        p["chunk"], p["phi"])
+
+
+CHUNK_CASES = [
+    ("null_desc", None, {}, la.LA_EINVAL, "desc"),
+    ("bad_variant", D(variant=7), {}, la.LA_EINVAL, "variant"),
+    ("bad_dtype", D(dtype=5), {}, la.LA_EINVAL, "dtype"),
+    ("bad_phi", D(phi=3), {}, la.LA_EINVAL, "phi"),
+    ("normalized_needs_elu1", D(la.LA_NORMALIZED, phi=la.LA_PHI_IDENTITY), {}, la.LA_EINVAL, "LA_PHI_ELU1"),
+    ("delta_needs_identity", D(phi=la.LA_PHI_ELU1), {}, la.LA_EINVAL, "LA_PHI_IDENTITY"),
+    ("negative_B", D(B=-1), {}, la.LA_EINVAL, "B="),
+    ("negative_T", D(T=-5), {}, la.LA_EINVAL, "T="),
+    ("zero_dk", D(d_k=0), {}, la.LA_EINVAL, "d_k"),
+    ("unsupported_dk", D(d_k=48), {}, la.LA_EUNSUPPORTED, "head sizes"),
+    ("unsupported_dv", D(d_v=256), {}, la.LA_EUNSUPPORTED, "head sizes"),
+    ("unsupported_chunk", D(chunk=128), {}, la.LA_EUNSUPPORTED, "chunk"),
+    ("negative_chunk", D(chunk=-16), {}, la.LA_EINVAL, "chunk"),
+    ("missing_q", D(), {"q": None}, la.LA_EINVAL, "required"),
+    ("missing_out", D(), {"out": None}, la.LA_EINVAL, "required"),
+    ("missing_gate", D(), {"gate": None}, la.LA_EINVAL, "gate"),
+    ("missing_beta", D(), {"beta": None}, la.LA_EINVAL, "beta"),
+    ("gate_on_normalized", D(la.LA_NORMALIZED), {"gate": fake(5)}, la.LA_EINVAL, "gate"),
+    ("beta_on_gated", D(la.LA_GATED), {"beta": fake(6)}, la.LA_EINVAL, "beta"),
+    ("z0_on_delta", D(), {"z0": fake(7)}, la.LA_EINVAL, "z"),
+    ("z_T_on_gated", D(la.LA_GATED), {"z_T": fake(7)}, la.LA_EINVAL, "z"),
+    ("misaligned_q", D(), {"q": fake(0, 8)}, la.LA_EINVAL, "aligned"),
+    ("misaligned_S0", D(), {"S0": fake(8, 4)}, la.LA_EINVAL, "aligned"),
+    ("misaligned_beta", D(), {"beta": fake(6, 2)}, la.LA_EINVAL, "aligned"),
+    ("out_overlaps_q", D(), {"out": fake(0, 256)}, la.LA_EINVAL, "overlaps"),
+    ("out_overlaps_v", D(), {"out": fake(2)}, la.LA_EINVAL, "overlaps"),
+    ("state_partially_overlaps_S0", D(), {"S0": fake(8), "S_T": fake(8, 1024)}, la.LA_EINVAL, "overlaps"),
+    ("state_overlaps_out", D(), {"S_T": fake(3, 512)}, la.LA_EINVAL, "overlaps"),
+]
+
+
+@pytest.mark.parametrize("name,desc,kw,status,msg", CHUNK_CASES, ids=[c[0] for c in CHUNK_CASES])
+def test_chunk_fwd_rejects(lib, name, desc, kw, status, msg):
+    assert call_chunk(lib, desc, **kw) == status
+    assert msg in la.la_last_error()
+
+
+DECODE_CASES = [
+    ("normalized_needs_z", D(la.LA_NORMALIZED), {"z": None}, la.LA_EINVAL, "z is required"),
+    ("missing_state", D(), {"S": None}, la.LA_EINVAL, "required"),
+    ("state_overlaps_k", D(), {"S": fake(1, 64)}, la.LA_EINVAL, "overlaps"),
+    ("out_overlaps_state", D(), {"out": fake(4, 128)}, la.LA_EINVAL, "overlaps"),
+    ("z_on_gated", D(la.LA_GATED), {"z": fake(7)}, la.LA_EINVAL, "z"),
+    ("unsupported_dk", D(d_k=8), {}, la.LA_EUNSUPPORTED, "head sizes"),
+]
+
+
+@pytest.mark.parametrize("name,desc,kw,status,msg", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_step_rejects(lib, name, desc, kw, status, msg):
+    assert call_decode(lib, desc, **kw) == status
+    assert msg in la.la_last_error()
+
+
+def test_workspace_query_of_invalid_desc_is_zero(lib):
+    assert la.la_chunk_fwd_workspace(D(d_k=48)) == 0
+
+
+def test_empty_problem_is_a_no_op(lib):
+    # B*H == 0: valid and nothing to launch, so no HIP call happens
+    assert call_chunk(lib, D(B=0), q=None, k=None, v=None, out=None, S_T=None,
+                      gate=None, beta=None) == la.LA_OK
+    assert call_decode(lib, D(H=0), q=None, k=None, v=None, out=None, S=None,
+                       gate=None, beta=None) == la.LA_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 16)
+    with pytest.raises(ValueError):
+        la.la_chunk_fwd(x, x, x, variant=la.LA_NORMALIZED)

@@ -181,6 +181,16 @@ def decode_state(w: Workload, seed: int | None = None, *, B=None, H=None) -> Hos
     return _store(_normal(rng, (B, H, w.d_v, w.d_k), w.S0_std), "f32")
 
 
+def decode_normalizer(w: Workload, seed: int | None = None, *, B=None, H=None) -> HostTensor:
+    """A positive initial normalizer z0 (B,H,d_k) f32 for the normalized variant:
+    |N(0, 1)| * d_k + 1, the scale of a sum of d_k-ish positive features."""
+    seed = w.seed if seed is None else seed
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    rng = np.random.default_rng([seed, (1 << 30) + 1])
+    return _store(np.abs(_normal(rng, (B, H, w.d_k))) * w.d_k + 1.0, "f32")
+
+
 def decode_step_inputs(w: Workload, step: int, seed: int | None = None, *,
                        B=None, H=None) -> dict:
     """Inputs of decode step ``step``: q, k, v (B,H,d) and gate/beta per variant."""
