@@ -1,0 +1,50 @@
+// la_chunk_common.hpp -- pieces shared by the chunked-forward kernels.
+#pragma once
+
+#include "la_internal.hpp"
+#include "la_mfma.hpp"
+
+namespace la {
+
+// Kernel arguments of the chunked forward (device pointers, raw element types).
+struct ChunkParams {
+    const void *q, *k, *v;
+    const float *gate, *beta;
+    const float *S0, *z0;
+    void *out;
+    float *S_T, *z_T;
+    int T, d_v, n_vblk;
+};
+
+// Copy rows [0, n) of a D-wide row-major global tile (row stride `lds`
+// elements) into LDS rows of stride `ldd`, and zero rows [n, R).  16-byte
+// vector copies; every row start must be 16-byte aligned on both sides.
+template <int R, int D, class E>
+__device__ __forceinline__ void stage_rows(E *dst, int ldd, const E *src, size_t lds, int n, int tid, int nthr) {
+    constexpr int VE = 16 / sizeof(E);        // elements per 16-byte vector
+    constexpr int VPR = D / VE;               // vectors per row
+    static_assert(D % VE == 0, "row width");
+    for (int e = tid; e < R * VPR; e += nthr) {
+        const int r = e / VPR, c = (e % VPR) * VE;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (r < n) x = *reinterpret_cast<const uint4 *>(src + r * lds + c);
+        *reinterpret_cast<uint4 *>(dst + r * ldd + c) = x;
+    }
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return bf16_to_f32(x); }
+__device__ __forceinline__ void from_f32(float &d, float x) { d = x; }
+__device__ __forceinline__ void from_f32(bf16_t &d, float x) { d = f32_to_bf16(x); }
+
+}  // namespace la

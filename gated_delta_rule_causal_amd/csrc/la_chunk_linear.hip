@@ -1,5 +1,407 @@
-// la_chunk_linear.hip -- chunked forward of normalized and gated linear attention.
-#include "la_internal.hpp"
+// la_chunk_linear.hip -- chunked forward of normalized and gated linear
+// attention (gfx950).
+//
+// Normalized (page "Beyond -- Linear attention and recurrent memory",
+// section "The big idea"; page "Ch. 11 Linear attention and Hyena", 11.2):
+// with phi = elu+1 and a chunk of C tokens entering with (S0, z0),
+//   P   = M o (phiQ phiK^T)                       (M: j <= t, a token sees itself)
+//   O   = (phiQ S0^T + P V) / (phiQ z0 + P 1)
+//   S_C = S0 + V^T phiK,   z_C = z0 + phiK^T 1.
+// The denominator uses the same rounded P as the numerator.
+//
+// Gated (page "Ch. 11 Linear attention and Hyena", 11.3 and the solution to
+// Exercise 11.5): per-channel gates gamma_t, decay between tokens j <= t of
+// channel c is prod_{i=j+1}^t gamma_ic.  The chunk applies the page's
+// cumulative-gate rescaling locally, with a reference point per 16-token
+// block so that no factor exceeds the float32 range:
+//   * key block J < query block I: reference e_J = last token of J,
+//       q~_t = phi(q_t) prod_{e_J < i <= t} gamma_i   (<= 1 per channel)
+//       k~_j = phi(k_j) prod_{j < i <= e_J} gamma_i   (<= 1)
+//     formed as Qhat_t * rho_IJ with Qhat_t = phi(q_t) prod_{16I <= i <= t}
+//     gamma_i and rho_IJ = product of the whole blocks strictly between.
+//   * diagonal block I: reference r_I = 16I - 1,
+//       Qhat_t (<= 1) and kd_j = phi(k_j) / prod_{16I <= i <= j} gamma_i.
+//     kd is bounded only when a channel's gates over 16 tokens do not
+//     multiply below ~1e-30 (documented precondition).
+//   * inter-chunk: O += (Qhat_t * E_I) S0^T, E_I = prod_{i < 16I} gamma_i;
+//     S_C = S0 diag(prod_all gamma) + V^T (phi(K) o prod_{j < i < C} gamma_i).
+// All gate factors are running products of the gates themselves, so no
+// exponential or logarithm is evaluated.
+//
+// Work decomposition as in the delta-rule kernel: one workgroup per (b, h,
+// block of DVB value channels); wave w keeps the transposed state slice of
+// its 16 value channels in matrix-core accumulators across the sequence.
+#include "la_chunk_common.hpp"
+
 namespace la {
-hipError_t launch_chunk_linear(const ChunkArgs &) { return hipErrorNotSupported; }
+
+// Scaled variants of the LDS x LDS / LDS x register tile products: the A
+// operand's contraction index k is multiplied by scale[k] (float32, in LDS)
+// before it enters the matrix cores.
+template <class Op>
+__device__ __forceinline__ typename Group<Op>::type scaled_group(const Op *a, const float *s) {
+    float x[4];
+    Group<Op>::unpack(ld_group(a), x);
+    const float4 f = *reinterpret_cast<const float4 *>(s);
+    return Group<Op>::make(x[0] * f.x, x[1] * f.y, x[2] * f.z, x[3] * f.w);
+}
+
+template <int K, class Op>
+__device__ __forceinline__ void tile_mma_ll_scaled(f32x4 &acc, const Op *a, int lda, const float *scale, const Op *b,
+                                                   int ldb, int lane) {
+    const int ko = 4 * (lane >> 4);
+    const Op *ar = a + (lane & 15) * lda + ko;
+    const Op *br = b + (lane & 15) * ldb + ko;
+    const float *sr = scale + ko;
+#pragma unroll
+    for (int k = 0; k + 32 <= K; k += 32)
+        mma32(acc, scaled_group(ar + k, sr + k), scaled_group(ar + k + 16, sr + k + 16), ld_group(br + k),
+              ld_group(br + k + 16));
+    if constexpr (K % 32 == 16) mma16(acc, scaled_group(ar + K - 16, sr + K - 16), ld_group(br + K - 16));
+}
+
+template <int NK, class Op, class G>
+__device__ __forceinline__ void tile_mma_lr_scaled(f32x4 &acc, const Op *a, int lda, const float *scale, const G *bg,
+                                                   int lane) {
+    const int ko = 4 * (lane >> 4);
+    const Op *ar = a + (lane & 15) * lda + ko;
+    const float *sr = scale + ko;
+#pragma unroll
+    for (int s = 0; s + 2 <= NK; s += 2)
+        mma32(acc, scaled_group(ar + 16 * s, sr + 16 * s), scaled_group(ar + 16 * s + 16, sr + 16 * s + 16), bg[s],
+              bg[s + 1]);
+    if constexpr (NK % 2 == 1) mma16(acc, scaled_group(ar + 16 * (NK - 1), sr + 16 * (NK - 1)), bg[NK - 1]);
+}
+
+// pair index of an off-diagonal key block J <= I - 2 (blocks strictly between exist)
+__host__ __device__ constexpr int rho_index(int I, int J) { return (I - 2) * (I - 1) / 2 + J; }
+
+template <bool GATED, class DT, int DK, int DVB, int C>
+struct LinearLds {
+    typedef typename OpOf<DT>::type Op;
+    static constexpr int NB = C / 16;
+    static constexpr int NRHO = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 0;
+    static constexpr int PAD = 16 / sizeof(Op);
+    static constexpr int LDK = DK + PAD;
+    static constexpr int LDC = C + PAD;
+    static constexpr int LDG = DK + 4;
+    static constexpr int P_BYTES = C * LDC * (int)sizeof(Op);
+    static constexpr int G_BYTES = GATED ? C * LDG * 4 : 0;
+    static constexpr int PG_BYTES = P_BYTES > G_BYTES ? P_BYTES : G_BYTES;
+    static constexpr int F_FLOATS = GATED ? (NB + 1 + NRHO) * DK : DK + C;
+    static constexpr int BYTES = (GATED ? 3 : 2) * C * LDK * (int)sizeof(Op) + DK * LDC * (int)sizeof(Op) +
+                                 DVB * LDC * (int)sizeof(Op) + PG_BYTES + F_FLOATS * 4;
+};
+
+template <bool GATED, int PHI, class DT, int DK, int DVB, int C>
+__global__ void __launch_bounds__(DVB * 4) linear_chunk_kernel(const ChunkParams p) {
+    typedef typename DT::storage IO;
+    typedef typename OpOf<DT>::type Op;
+    typedef Group<Op> Gp;
+    typedef typename Gp::type G4;
+    typedef LinearLds<GATED, DT, DK, DVB, C> L;
+    constexpr int W = DVB / 16;
+    constexpr int NTHR = W * 64;
+    constexpr int NB = C / 16;
+    constexpr int NCB = DK / 16;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG;
+    constexpr int VE = 16 / sizeof(IO);                   // elements per 16-byte vector
+    static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0, "tiling");
+    static_assert(L::BYTES <= 160 * 1024, "LDS budget");
+
+    __shared__ __align__(16) Op sQ[C * LDK];                 // phi(Q) | Qhat
+    __shared__ __align__(16) Op sK[C * LDK];                 // phi(K) | k~ (off-diagonal reference)
+    __shared__ __align__(16) Op sKd[GATED ? C * LDK : 8];    // kd (diagonal reference)
+    __shared__ __align__(16) Op sKt[DK * LDC];               // key operand of the state update, [c][t]
+    __shared__ __align__(16) Op sVt[DVB * LDC];              // this block's values, [v][t]
+    __shared__ __align__(16) unsigned char sPG[L::PG_BYTES]; // gates (f32), then P
+    __shared__ __align__(16) float sF[L::F_FLOATS];
+    Op *sP = reinterpret_cast<Op *>(sPG);
+    float *sG = reinterpret_cast<float *>(sPG);
+    float *sE = sF;                       // gated: prod of the chunk's gates before block I, [NB][DK]
+    float *sD = sF + NB * DK;             // gated: prod of all the chunk's gates, [DK]
+    float *sRho = sF + (NB + 1) * DK;     // gated: prod of the blocks strictly between J and I, [NRHO][DK]
+    float *sZ = sF;                       // normalized: running z, [DK]
+    float *sDen = sF + DK;                // normalized: denominators, [C]
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int bh = blockIdx.x / p.n_vblk, vb = blockIdx.x % p.n_vblk;
+    const int vloc = 16 * wave + lr;
+    const int vch = vb * DVB + vloc;
+    const size_t tok0 = static_cast<size_t>(bh) * p.T;
+    const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
+    const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
+    const IO *vh = static_cast<const IO *>(p.v) + tok0 * p.d_v + vb * DVB;
+    IO *oh = static_cast<IO *>(p.out) + tok0 * p.d_v;
+    const float *gh = GATED ? p.gate + tok0 * DK : nullptr;
+
+    f32x4 st[NCB];
+    const size_t srow = (static_cast<size_t>(bh) * p.d_v + vch) * DK;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        if (p.S0) {
+            const float4 s = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
+            st[cb] = f32x4{s.x, s.y, s.z, s.w};
+        } else {
+            st[cb] = zero4();
+        }
+    }
+    if constexpr (!GATED) {
+        for (int c = tid; c < DK; c += NTHR) sZ[c] = p.z0 ? p.z0[static_cast<size_t>(bh) * DK + c] : 0.f;
+    }
+
+    for (int c0 = 0; c0 < p.T; c0 += C) {
+        const int n = min(C, p.T - c0);
+
+        // ---- stage: values transposed; queries/keys (normalized: phi applied,
+        // keys also transposed); gates
+        for (int e = tid; e < C * (DVB / VE); e += NTHR) {
+            const int t = e / (DVB / VE), v = (e % (DVB / VE)) * VE;
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.f;
+            if (t < n) {
+                if constexpr (VE == 8) {
+                    load8(reinterpret_cast<const bf16_t *>(vh + static_cast<size_t>(c0 + t) * p.d_v + v), x);
+                } else {
+                    const float4 f = *reinterpret_cast<const float4 *>(vh + static_cast<size_t>(c0 + t) * p.d_v + v);
+                    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < VE; ++i) from_f32(sVt[(v + i) * LDC + t], x[i]);
+        }
+        if constexpr (!GATED) {
+            for (int e = tid; e < C * (DK / VE); e += NTHR) {
+                const int t = e / (DK / VE), c = (e % (DK / VE)) * VE;
+                float xq[8], xk[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { xq[i] = 0.f; xk[i] = 0.f; }   // padded tokens carry no feature
+                if (t < n) {
+                    if constexpr (VE == 8) {
+                        load8(reinterpret_cast<const bf16_t *>(qh + static_cast<size_t>(c0 + t) * DK + c), xq);
+                        load8(reinterpret_cast<const bf16_t *>(kh + static_cast<size_t>(c0 + t) * DK + c), xk);
+                    } else {
+                        const float4 a = *reinterpret_cast<const float4 *>(qh + static_cast<size_t>(c0 + t) * DK + c);
+                        const float4 b = *reinterpret_cast<const float4 *>(kh + static_cast<size_t>(c0 + t) * DK + c);
+                        xq[0] = a.x; xq[1] = a.y; xq[2] = a.z; xq[3] = a.w;
+                        xk[0] = b.x; xk[1] = b.y; xk[2] = b.z; xk[3] = b.w;
+                    }
+#pragma unroll
+                    for (int i = 0; i < VE; ++i) { xq[i] = apply_phi<PHI>(xq[i]); xk[i] = apply_phi<PHI>(xk[i]); }
+                }
+#pragma unroll
+                for (int i = 0; i < VE; ++i) {
+                    from_f32(sQ[t * LDK + c + i], xq[i]);
+                    from_f32(sK[t * LDK + c + i], xk[i]);
+                    from_f32(sKt[(c + i) * LDC + t], xk[i]);
+                }
+            }
+        } else {
+            stage_rows<C, DK>(sQ, LDK, qh + static_cast<size_t>(c0) * DK, DK, n, tid, NTHR);
+            stage_rows<C, DK>(sK, LDK, kh + static_cast<size_t>(c0) * DK, DK, n, tid, NTHR);
+            for (int e = tid; e < C * (DK / 4); e += NTHR) {
+                const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
+                float4 g = make_float4(1.f, 1.f, 1.f, 1.f);   // padded tokens: no decay
+                if (t < n) g = *reinterpret_cast<const float4 *>(gh + static_cast<size_t>(c0 + t) * DK + c);
+                *reinterpret_cast<float4 *>(sG + t * LDG + c) = g;
+            }
+        }
+        __syncthreads();
+
+        if constexpr (GATED) {
+            // ---- per-channel running products of the gates (one thread per key channel)
+            for (int c = tid; c < DK; c += NTHR) {
+                float bt[NB];
+                float before = 1.f;
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    float run = 1.f;
+                    for (int t = 16 * I; t < 16 * I + 16; ++t) {
+                        const bool on = t < n;
+                        run *= sG[t * LDG + c];
+                        const float fq = on ? apply_phi<PHI>(to_f32(sQ[t * LDK + c])) : 0.f;
+                        const float fk = on ? apply_phi<PHI>(to_f32(sK[t * LDK + c])) : 0.f;
+                        from_f32(sQ[t * LDK + c], fq * run);
+                        from_f32(sKd[t * LDK + c], fk / run);
+                    }
+                    bt[I] = run;
+                    sE[I * DK + c] = before;
+                    before *= run;
+                }
+                sD[c] = before;
+#pragma unroll
+                for (int I = 2; I < NB; ++I) {
+                    float r = 1.f;
+#pragma unroll
+                    for (int J = I - 2; J >= 0; --J) {
+                        r *= bt[J + 1];
+                        sRho[rho_index(I, J) * DK + c] = r;
+                    }
+                }
+                // reverse sweeps: whole chunk (state-update operand) and within blocks (k~)
+                float tail = 1.f, blk = 1.f;
+                for (int t = C - 1; t >= 0; --t) {
+                    const float fk = t < n ? apply_phi<PHI>(to_f32(sK[t * LDK + c])) : 0.f;
+                    if ((t & 15) == 15) blk = 1.f;
+                    from_f32(sKt[c * LDC + t], fk * tail);
+                    from_f32(sK[t * LDK + c], fk * blk);
+                    const float g = sG[t * LDG + c];
+                    tail *= g;
+                    blk *= g;
+                }
+            }
+            __syncthreads();   // the gate tile is dead from here on; its space holds P
+        }
+
+        // ---- intra-chunk scores P (16x16 tiles, block-lower-triangular)
+        for (int tt = wave; tt < NB * NB; tt += W) {
+            const int I = tt / NB, J = tt % NB;
+            const int row = 16 * I + 4 * lg, col = 16 * J + lr;
+            if (J > I) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sP[(row + i) * LDC + col] = Op(0);
+                continue;
+            }
+            f32x4 acc = zero4();
+            if constexpr (GATED) {
+                if (J == I)
+                    tile_mma_ll<DK>(acc, sQ + 16 * I * LDK, LDK, sKd + 16 * J * LDK, LDK, lane);
+                else if (J == I - 1)
+                    tile_mma_ll<DK>(acc, sQ + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, lane);
+                else
+                    tile_mma_ll_scaled<DK>(acc, sQ + 16 * I * LDK, LDK, sRho + rho_index(I, J) * DK,
+                                           sK + 16 * J * LDK, LDK, lane);
+            } else {
+                tile_mma_ll<DK>(acc, sQ + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, lane);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) from_f32(sP[(row + i) * LDC + col], col <= row + i ? acc[i] : 0.f);
+        }
+        __syncthreads();
+
+        if constexpr (!GATED) {
+            // ---- denominators phi(q_t).z0 + sum_j P_tj (the rounded P of the numerator)
+            for (int t = tid; t < C; t += NTHR) {
+                float d = 0.f;
+                for (int c = 0; c < DK; ++c) d += to_f32(sQ[t * LDK + c]) * sZ[c];
+                for (int j = 0; j <= t; ++j) d += to_f32(sP[t * LDC + j]);
+                sDen[t] = d;
+            }
+            __syncthreads();
+            // z_C = z0 + phiK^T 1 (after every denominator has read z0)
+            for (int c = tid; c < DK; c += NTHR) {
+                float s = 0.f;
+                for (int t = 0; t < C; ++t) s += to_f32(sKt[c * LDC + t]);
+                sZ[c] += s;
+            }
+        }
+
+        // ---- state-dependent part: this wave's 16 value channels
+        G4 sb[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            f32x4 o = zero4();
+            if constexpr (GATED) {
+                if (I == 0) tile_mma_lr<NCB>(o, sQ, LDK, sb, lane);
+                else tile_mma_lr_scaled<NCB>(o, sQ + 16 * I * LDK, LDK, sE + I * DK, sb, lane);
+            } else {
+                tile_mma_lr<NCB>(o, sQ + 16 * I * LDK, LDK, sb, lane);
+            }
+            tile_mma_ll<C>(o, sP + 16 * I * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * I + 4 * lg + i;
+                float val = o[i];
+                if constexpr (!GATED) val = val / sDen[t];
+                if (t < n) store1(oh + static_cast<size_t>(c0 + t) * p.d_v + vch, val);
+            }
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            if constexpr (GATED) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) st[cb][i] *= sD[16 * cb + 4 * lg + i];
+            }
+            tile_mma_ll<C>(st[cb], sKt + 16 * cb * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
+        }
+        __syncthreads();
+    }
+
+    if (p.S_T) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            *reinterpret_cast<float4 *>(p.S_T + srow + 16 * cb + 4 * lg) =
+                make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
+    }
+    if constexpr (!GATED) {
+        if (p.z_T && vb == 0)
+            for (int c = tid; c < DK; c += NTHR) p.z_T[static_cast<size_t>(bh) * DK + c] = sZ[c];
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+template <bool GATED, int PHI, class DT, int DK, int DVB, int C>
+static hipError_t launch_linear_t(const ChunkArgs &a) {
+    ChunkParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.beta = nullptr; p.S0 = a.S0; p.z0 = a.z0;
+    p.out = a.out; p.S_T = a.S_T; p.z_T = a.z_T;
+    p.T = a.T; p.d_v = a.d_v; p.n_vblk = a.d_v / DVB;
+    const int64_t blocks = static_cast<int64_t>(a.B) * a.H * p.n_vblk;
+    hipLaunchKernelGGL((linear_chunk_kernel<GATED, PHI, DT, DK, DVB, C>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(DVB * 4), 0, a.stream, p);
+    return hipGetLastError();
+}
+
+// Largest chunk <= the requested one whose LDS tiles fit (the result does not
+// depend on the chunk length).
+template <bool GATED, class DT, int DK, int DVB, int C>
+constexpr int fit_chunk() {
+    if constexpr (C > 16 && LinearLds<GATED, DT, DK, DVB, C>::BYTES > 160 * 1024) return fit_chunk<GATED, DT, DK, DVB, C / 2>();
+    else return C;
+}
+
+template <bool GATED, int PHI, class DT, int DK, int DVB>
+static hipError_t linear_chunk(const ChunkArgs &a) {
+    switch (a.chunk) {
+        case 16: return launch_linear_t<GATED, PHI, DT, DK, DVB, 16>(a);
+        case 32: return launch_linear_t<GATED, PHI, DT, DK, DVB, fit_chunk<GATED, DT, DK, DVB, 32>()>(a);
+        case 64: return launch_linear_t<GATED, PHI, DT, DK, DVB, fit_chunk<GATED, DT, DK, DVB, 64>()>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <bool GATED, int PHI, class DT, int DK>
+static hipError_t linear_dvb(const ChunkArgs &a) {
+    if (a.d_v >= 32) return linear_chunk<GATED, PHI, DT, DK, 32>(a);
+    return linear_chunk<GATED, PHI, DT, DK, 16>(a);
+}
+
+template <bool GATED, int PHI, class DT>
+static hipError_t linear_dk(const ChunkArgs &a) {
+    switch (a.d_k) {
+        case 16: return linear_dvb<GATED, PHI, DT, 16>(a);
+        case 32: return linear_dvb<GATED, PHI, DT, 32>(a);
+        case 64: return linear_dvb<GATED, PHI, DT, 64>(a);
+        case 128: return linear_dvb<GATED, PHI, DT, 128>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class DT>
+static hipError_t linear_variant(const ChunkArgs &a) {
+    if (a.variant == LA_NORMALIZED) return linear_dk<false, LA_PHI_ELU1, DT>(a);
+    if (a.phi == LA_PHI_ELU1) return linear_dk<true, LA_PHI_ELU1, DT>(a);
+    return linear_dk<true, LA_PHI_IDENTITY, DT>(a);
+}
+
+hipError_t launch_chunk_linear(const ChunkArgs &a) {
+    if (a.dtype == LA_BF16) return linear_variant<BF16>(a);
+    return linear_variant<F32>(a);
+}
+
 }  // namespace la
