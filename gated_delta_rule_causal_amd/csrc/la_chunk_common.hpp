@@ -13,7 +13,7 @@ struct ChunkParams {
     const float *S0, *z0;
     void *out;
     float *S_T, *z_T;
-    int T, d_v, n_vblk;
+    int T, d_v, n_vblk, n_heads;
 };
 
 // Copy rows [0, n) of a D-wide row-major global tile (row stride `lds`
@@ -29,6 +29,55 @@ __device__ __forceinline__ void stage_rows(E *dst, int ldd, const E *src, size_t
         uint4 x = make_uint4(0u, 0u, 0u, 0u);
         if (r < n) x = *reinterpret_cast<const uint4 *>(src + r * lds + c);
         *reinterpret_cast<uint4 *>(dst + r * ldd + c) = x;
+    }
+}
+
+// Register staging of an R x D row-major tile: load() issues every 16-byte
+// global read of the tile at once (rows >= n read as zero), store() writes
+// the registers to LDS.  Issued one chunk ahead, the reads complete while
+// the current chunk computes; the workgroup barriers only wait for LDS.
+template <int R, int D, int NTHR, class E>
+struct TilePrefetch {
+    static constexpr int VE = 16 / sizeof(E);
+    static constexpr int VPR = D / VE;
+    static constexpr int TOTAL = R * VPR;
+    static constexpr int PER = (TOTAL + NTHR - 1) / NTHR;
+    static_assert(D % VE == 0, "row width");
+    uint4 r[PER];
+
+    __device__ __forceinline__ void load(const E *src, size_t lds, int n, int tid) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + i * NTHR;
+            const int row = e / VPR, col = (e % VPR) * VE;
+            r[i] = make_uint4(0u, 0u, 0u, 0u);
+            if ((TOTAL % NTHR == 0 || e < TOTAL) && row < n)
+                r[i] = *reinterpret_cast<const uint4 *>(src + row * lds + col);
+        }
+    }
+    __device__ __forceinline__ void store(E *dst, int ldd, int tid) const {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int e = tid + i * NTHR;
+            if (TOTAL % NTHR == 0 || e < TOTAL)
+                *reinterpret_cast<uint4 *>(dst + (e / VPR) * ldd + (e % VPR) * VE) = r[i];
+        }
+    }
+};
+
+// Workgroup -> (head, value block).  The dispatcher deals workgroups to the
+// 8 XCDs round robin (workgroup i runs on XCD i % 8); when the head count is
+// a multiple of 8 the value blocks of one head are given ids that differ by
+// multiples of 8, so they run on one XCD and share its L2 for the re-read
+// queries and keys.
+__device__ __forceinline__ void block_to_head(int bid, int n_heads, int n_vblk, int &bh, int &vb) {
+    if ((n_heads & 7) == 0) {
+        const int xcd = bid & 7, r = bid >> 3;
+        vb = r % n_vblk;
+        bh = (r / n_vblk) * 8 + xcd;
+    } else {
+        bh = bid / n_vblk;
+        vb = bid % n_vblk;
     }
 }
 

@@ -88,25 +88,25 @@ struct LinearLds {
     static constexpr int P_BYTES = C * LDC * (int)sizeof(Op);
     static constexpr int G_BYTES = GATED ? C * LDG * 4 : 0;
     static constexpr int PG_BYTES = P_BYTES > G_BYTES ? P_BYTES : G_BYTES;
-    static constexpr int F_FLOATS = GATED ? (NB + 1 + NRHO) * DK : DK + C;
+    static constexpr int F_FLOATS = GATED ? (2 * NB + 1 + NRHO) * DK : DK + C;
     static constexpr int BYTES = (GATED ? 3 : 2) * C * LDK * (int)sizeof(Op) + DK * LDC * (int)sizeof(Op) +
                                  DVB * LDC * (int)sizeof(Op) + PG_BYTES + F_FLOATS * 4;
 };
 
-template <bool GATED, int PHI, class DT, int DK, int DVB, int C>
-__global__ void __launch_bounds__(DVB * 4) linear_chunk_kernel(const ChunkParams p) {
+template <bool GATED, int PHI, class DT, int DK, int DVB, int C, int NW>
+__global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams p) {
     typedef typename DT::storage IO;
     typedef typename OpOf<DT>::type Op;
     typedef Group<Op> Gp;
     typedef typename Gp::type G4;
     typedef LinearLds<GATED, DT, DK, DVB, C> L;
-    constexpr int W = DVB / 16;
-    constexpr int NTHR = W * 64;
+    constexpr int WS = DVB / 16;                          // state waves
+    constexpr int NTHR = NW * 64;
     constexpr int NB = C / 16;
     constexpr int NCB = DK / 16;
     constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG;
     constexpr int VE = 16 / sizeof(IO);                   // elements per 16-byte vector
-    static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0, "tiling");
+    static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && WS <= NW, "tiling");
     static_assert(L::BYTES <= 160 * 1024, "LDS budget");
 
     __shared__ __align__(16) Op sQ[C * LDK];                 // phi(Q) | Qhat
@@ -121,12 +121,14 @@ __global__ void __launch_bounds__(DVB * 4) linear_chunk_kernel(const ChunkParams
     float *sE = sF;                       // gated: prod of the chunk's gates before block I, [NB][DK]
     float *sD = sF + NB * DK;             // gated: prod of all the chunk's gates, [DK]
     float *sRho = sF + (NB + 1) * DK;     // gated: prod of the blocks strictly between J and I, [NRHO][DK]
+    float *sBT = sF + (NB + 1 + L::NRHO) * DK;  // gated: prod of the gates of block I, [NB][DK]
     float *sZ = sF;                       // normalized: running z, [DK]
     float *sDen = sF + DK;                // normalized: denominators, [C]
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
-    const int bh = blockIdx.x / p.n_vblk, vb = blockIdx.x % p.n_vblk;
+    int bh, vb;
+    block_to_head(blockIdx.x, p.n_heads, p.n_vblk, bh, vb);
     const int vloc = 16 * wave + lr;
     const int vch = vb * DVB + vloc;
     const size_t tok0 = static_cast<size_t>(bh) * p.T;
@@ -137,126 +139,168 @@ __global__ void __launch_bounds__(DVB * 4) linear_chunk_kernel(const ChunkParams
     const float *gh = GATED ? p.gate + tok0 * DK : nullptr;
 
     f32x4 st[NCB];
-    const size_t srow = (static_cast<size_t>(bh) * p.d_v + vch) * DK;
+    const size_t srow = (static_cast<size_t>(bh) * p.d_v + (wave < WS ? vch : 0)) * DK;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        if (p.S0) {
+        st[cb] = zero4();
+        if (p.S0 && wave < WS) {
             const float4 s = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
             st[cb] = f32x4{s.x, s.y, s.z, s.w};
-        } else {
-            st[cb] = zero4();
         }
     }
     if constexpr (!GATED) {
         for (int c = tid; c < DK; c += NTHR) sZ[c] = p.z0 ? p.z0[static_cast<size_t>(bh) * DK + c] : 0.f;
     }
 
+    // chunk inputs staged one chunk ahead in registers
+    TilePrefetch<C, DK, NTHR, IO> pq, pk;
+    TilePrefetch<C, DVB, NTHR, IO> pv;
+    TilePrefetch<C, GATED ? DK : 4, NTHR, float> pgt;
+    auto prefetch = [&](int c0) {
+        const int n = min(C, p.T - c0);
+        pq.load(qh + static_cast<size_t>(c0) * DK, DK, n, tid);
+        pk.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
+        pv.load(vh + static_cast<size_t>(c0) * p.d_v, p.d_v, n, tid);
+        if constexpr (GATED) pgt.load(gh + static_cast<size_t>(c0) * DK, DK, n, tid);
+    };
+    if (p.T > 0) prefetch(0);
+
     for (int c0 = 0; c0 < p.T; c0 += C) {
         const int n = min(C, p.T - c0);
 
-        // ---- stage: values transposed; queries/keys (normalized: phi applied,
-        // keys also transposed); gates
-        for (int e = tid; e < C * (DVB / VE); e += NTHR) {
-            const int t = e / (DVB / VE), v = (e % (DVB / VE)) * VE;
-            float x[8];
+        // ---- commit the staged chunk.  Values transposed; queries/keys raw
+        // (gated) or with phi applied and keys also transposed (normalized);
+        // gates as float32 with padded tokens set to 1 (no decay).
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = 0.f;
-            if (t < n) {
-                if constexpr (VE == 8) {
-                    load8(reinterpret_cast<const bf16_t *>(vh + static_cast<size_t>(c0 + t) * p.d_v + v), x);
-                } else {
-                    const float4 f = *reinterpret_cast<const float4 *>(vh + static_cast<size_t>(c0 + t) * p.d_v + v);
-                    x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+        for (int i = 0; i < pv.PER; ++i) {
+            const int e = tid + i * NTHR;
+            if (pv.TOTAL % NTHR != 0 && e >= pv.TOTAL) continue;
+            const int t = e / pv.VPR, v = (e % pv.VPR) * VE;
+            const uint4 w = pv.r[i];
+            if constexpr (VE == 8) {
+                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sVt[(v + 2 * j) * LDC + t] = static_cast<bf16_t>(u[j] & 0xffffu);
+                    sVt[(v + 2 * j + 1) * LDC + t] = static_cast<bf16_t>(u[j] >> 16);
                 }
+            } else {
+                sVt[(v + 0) * LDC + t] = __uint_as_float(w.x);
+                sVt[(v + 1) * LDC + t] = __uint_as_float(w.y);
+                sVt[(v + 2) * LDC + t] = __uint_as_float(w.z);
+                sVt[(v + 3) * LDC + t] = __uint_as_float(w.w);
             }
-#pragma unroll
-            for (int i = 0; i < VE; ++i) from_f32(sVt[(v + i) * LDC + t], x[i]);
         }
         if constexpr (!GATED) {
-            for (int e = tid; e < C * (DK / VE); e += NTHR) {
-                const int t = e / (DK / VE), c = (e % (DK / VE)) * VE;
+#pragma unroll
+            for (int i = 0; i < pq.PER; ++i) {
+                const int e = tid + i * NTHR;
+                if (pq.TOTAL % NTHR != 0 && e >= pq.TOTAL) continue;
+                const int t = e / pq.VPR, c = (e % pq.VPR) * VE;
                 float xq[8], xk[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { xq[i] = 0.f; xk[i] = 0.f; }   // padded tokens carry no feature
-                if (t < n) {
-                    if constexpr (VE == 8) {
-                        load8(reinterpret_cast<const bf16_t *>(qh + static_cast<size_t>(c0 + t) * DK + c), xq);
-                        load8(reinterpret_cast<const bf16_t *>(kh + static_cast<size_t>(c0 + t) * DK + c), xk);
-                    } else {
-                        const float4 a = *reinterpret_cast<const float4 *>(qh + static_cast<size_t>(c0 + t) * DK + c);
-                        const float4 b = *reinterpret_cast<const float4 *>(kh + static_cast<size_t>(c0 + t) * DK + c);
-                        xq[0] = a.x; xq[1] = a.y; xq[2] = a.z; xq[3] = a.w;
-                        xk[0] = b.x; xk[1] = b.y; xk[2] = b.z; xk[3] = b.w;
-                    }
-#pragma unroll
-                    for (int i = 0; i < VE; ++i) { xq[i] = apply_phi<PHI>(xq[i]); xk[i] = apply_phi<PHI>(xk[i]); }
+                if constexpr (VE == 8) {
+                    const uint4 a = pq.r[i], b = pk.r[i];
+                    xq[0] = lo_bf16(a.x); xq[1] = hi_bf16(a.x); xq[2] = lo_bf16(a.y); xq[3] = hi_bf16(a.y);
+                    xq[4] = lo_bf16(a.z); xq[5] = hi_bf16(a.z); xq[6] = lo_bf16(a.w); xq[7] = hi_bf16(a.w);
+                    xk[0] = lo_bf16(b.x); xk[1] = hi_bf16(b.x); xk[2] = lo_bf16(b.y); xk[3] = hi_bf16(b.y);
+                    xk[4] = lo_bf16(b.z); xk[5] = hi_bf16(b.z); xk[6] = lo_bf16(b.w); xk[7] = hi_bf16(b.w);
+                } else {
+                    const uint4 a = pq.r[i], b = pk.r[i];
+                    xq[0] = __uint_as_float(a.x); xq[1] = __uint_as_float(a.y);
+                    xq[2] = __uint_as_float(a.z); xq[3] = __uint_as_float(a.w);
+                    xk[0] = __uint_as_float(b.x); xk[1] = __uint_as_float(b.y);
+                    xk[2] = __uint_as_float(b.z); xk[3] = __uint_as_float(b.w);
                 }
+                const bool on = t < n;   // padded tokens carry no feature (phi(0) would be 1)
 #pragma unroll
-                for (int i = 0; i < VE; ++i) {
-                    from_f32(sQ[t * LDK + c + i], xq[i]);
-                    from_f32(sK[t * LDK + c + i], xk[i]);
-                    from_f32(sKt[(c + i) * LDC + t], xk[i]);
+                for (int j = 0; j < VE; ++j) {
+                    const float fq = on ? apply_phi<PHI>(xq[j]) : 0.f;
+                    const float fk = on ? apply_phi<PHI>(xk[j]) : 0.f;
+                    from_f32(sQ[t * LDK + c + j], fq);
+                    from_f32(sK[t * LDK + c + j], fk);
+                    from_f32(sKt[(c + j) * LDC + t], fk);
                 }
             }
         } else {
-            stage_rows<C, DK>(sQ, LDK, qh + static_cast<size_t>(c0) * DK, DK, n, tid, NTHR);
-            stage_rows<C, DK>(sK, LDK, kh + static_cast<size_t>(c0) * DK, DK, n, tid, NTHR);
-            for (int e = tid; e < C * (DK / 4); e += NTHR) {
-                const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
-                float4 g = make_float4(1.f, 1.f, 1.f, 1.f);   // padded tokens: no decay
-                if (t < n) g = *reinterpret_cast<const float4 *>(gh + static_cast<size_t>(c0 + t) * DK + c);
+            pq.store(sQ, LDK, tid);
+            pk.store(sK, LDK, tid);
+#pragma unroll
+            for (int i = 0; i < pgt.PER; ++i) {
+                const int e = tid + i * NTHR;
+                if (pgt.TOTAL % NTHR != 0 && e >= pgt.TOTAL) continue;
+                const int t = e / pgt.VPR, c = (e % pgt.VPR) * 4;
+                float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
+                if (t < n) g = *reinterpret_cast<const float4 *>(&pgt.r[i]);
                 *reinterpret_cast<float4 *>(sG + t * LDG + c) = g;
             }
         }
         __syncthreads();
+        if (c0 + C < p.T) prefetch(c0 + C);
 
         if constexpr (GATED) {
-            // ---- per-channel running products of the gates (one thread per key channel)
-            for (int c = tid; c < DK; c += NTHR) {
+            // ---- gate products, one thread per (key channel, 16-token block)
+            for (int e = tid; e < NB * DK; e += NTHR) {
+                const int c = e % DK, I = e / DK;
+                float run = 1.f;
+#pragma unroll
+                for (int t = 16 * I; t < 16 * I + 16; ++t) run *= sG[t * LDG + c];
+                sBT[I * DK + c] = run;
+            }
+            __syncthreads();
+            for (int e = tid; e < NB * DK; e += NTHR) {
+                const int c = e % DK, I = e / DK;
                 float bt[NB];
-                float before = 1.f;
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    float run = 1.f;
-                    for (int t = 16 * I; t < 16 * I + 16; ++t) {
-                        const bool on = t < n;
-                        run *= sG[t * LDG + c];
-                        const float fq = on ? apply_phi<PHI>(to_f32(sQ[t * LDK + c])) : 0.f;
-                        const float fk = on ? apply_phi<PHI>(to_f32(sK[t * LDK + c])) : 0.f;
-                        from_f32(sQ[t * LDK + c], fq * run);
-                        from_f32(sKd[t * LDK + c], fk / run);
+                for (int J = 0; J < NB; ++J) bt[J] = sBT[J * DK + c];
+                float after = 1.f;   // prod of the gates of the blocks after I
+#pragma unroll
+                for (int J = NB - 1; J > 0; --J)
+                    if (J > I) after *= bt[J];
+                if (I == 0) {
+                    float before = 1.f;
+#pragma unroll
+                    for (int J = 0; J < NB; ++J) {
+                        sE[J * DK + c] = before;
+                        before *= bt[J];
                     }
-                    bt[I] = run;
-                    sE[I * DK + c] = before;
-                    before *= run;
-                }
-                sD[c] = before;
+                    sD[c] = before;
 #pragma unroll
-                for (int I = 2; I < NB; ++I) {
-                    float r = 1.f;
+                    for (int J1 = 2; J1 < NB; ++J1) {
+                        float r = 1.f;
 #pragma unroll
-                    for (int J = I - 2; J >= 0; --J) {
-                        r *= bt[J + 1];
-                        sRho[rho_index(I, J) * DK + c] = r;
+                        for (int J0 = J1 - 2; J0 >= 0; --J0) {
+                            r *= bt[J0 + 1];
+                            sRho[rho_index(J1, J0) * DK + c] = r;
+                        }
                     }
                 }
-                // reverse sweeps: whole chunk (state-update operand) and within blocks (k~)
-                float tail = 1.f, blk = 1.f;
-                for (int t = C - 1; t >= 0; --t) {
+                // forward within the block: Qhat = phi(q) R_t, kd = phi(k) / R_t
+                float run = 1.f;
+#pragma unroll
+                for (int t = 16 * I; t < 16 * I + 16; ++t) {
+                    const bool on = t < n;
+                    run *= sG[t * LDG + c];
+                    const float fq = on ? apply_phi<PHI>(to_f32(sQ[t * LDK + c])) : 0.f;
+                    const float fk = on ? apply_phi<PHI>(to_f32(sK[t * LDK + c])) : 0.f;
+                    from_f32(sQ[t * LDK + c], fq * run);
+                    from_f32(sKd[t * LDK + c], fk / run);
+                }
+                // reverse within the block: k~ = phi(k) prod_{t<i<=e_I} gamma, and the
+                // state-update operand phi(k) prod_{t<i<C} gamma
+                float rev = 1.f;
+#pragma unroll
+                for (int t = 16 * I + 15; t >= 16 * I; --t) {
                     const float fk = t < n ? apply_phi<PHI>(to_f32(sK[t * LDK + c])) : 0.f;
-                    if ((t & 15) == 15) blk = 1.f;
-                    from_f32(sKt[c * LDC + t], fk * tail);
-                    from_f32(sK[t * LDK + c], fk * blk);
-                    const float g = sG[t * LDG + c];
-                    tail *= g;
-                    blk *= g;
+                    from_f32(sK[t * LDK + c], fk * rev);
+                    from_f32(sKt[c * LDC + t], fk * rev * after);
+                    rev *= sG[t * LDG + c];
                 }
             }
             __syncthreads();   // the gate tile is dead from here on; its space holds P
         }
 
         // ---- intra-chunk scores P (16x16 tiles, block-lower-triangular)
-        for (int tt = wave; tt < NB * NB; tt += W) {
+        for (int tt = wave; tt < NB * NB; tt += NW) {
             const int I = tt / NB, J = tt % NB;
             const int row = 16 * I + 4 * lg, col = 16 * J + lr;
             if (J > I) {
@@ -282,56 +326,62 @@ __global__ void __launch_bounds__(DVB * 4) linear_chunk_kernel(const ChunkParams
         __syncthreads();
 
         if constexpr (!GATED) {
-            // ---- denominators phi(q_t).z0 + sum_j P_tj (the rounded P of the numerator)
-            for (int t = tid; t < C; t += NTHR) {
+            // ---- denominators phi(q_t).z0 + sum_j P_tj (the rounded P of the
+            // numerator); 8 lanes per token
+            for (int e = tid; e < 8 * C; e += NTHR) {
+                const int t = e >> 3, part = e & 7;
                 float d = 0.f;
-                for (int c = 0; c < DK; ++c) d += to_f32(sQ[t * LDK + c]) * sZ[c];
-                for (int j = 0; j <= t; ++j) d += to_f32(sP[t * LDC + j]);
-                sDen[t] = d;
+                for (int c = part; c < DK; c += 8) d += to_f32(sQ[t * LDK + c]) * sZ[c];
+                for (int j = part; j <= t; j += 8) d += to_f32(sP[t * LDC + j]);
+                d = group_sum<8>(d);
+                if (part == 0) sDen[t] = d;
             }
             __syncthreads();
             // z_C = z0 + phiK^T 1 (after every denominator has read z0)
             for (int c = tid; c < DK; c += NTHR) {
                 float s = 0.f;
+#pragma unroll 8
                 for (int t = 0; t < C; ++t) s += to_f32(sKt[c * LDC + t]);
                 sZ[c] += s;
             }
         }
 
         // ---- state-dependent part: this wave's 16 value channels
-        G4 sb[NCB];
+        if (wave < WS) {
+            G4 sb[NCB];
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
+            for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
 #pragma unroll
-        for (int I = 0; I < NB; ++I) {
-            f32x4 o = zero4();
-            if constexpr (GATED) {
-                if (I == 0) tile_mma_lr<NCB>(o, sQ, LDK, sb, lane);
-                else tile_mma_lr_scaled<NCB>(o, sQ + 16 * I * LDK, LDK, sE + I * DK, sb, lane);
-            } else {
-                tile_mma_lr<NCB>(o, sQ + 16 * I * LDK, LDK, sb, lane);
+            for (int I = 0; I < NB; ++I) {
+                f32x4 o = zero4();
+                if constexpr (GATED) {
+                    if (I == 0) tile_mma_lr<NCB>(o, sQ, LDK, sb, lane);
+                    else tile_mma_lr_scaled<NCB>(o, sQ + 16 * I * LDK, LDK, sE + I * DK, sb, lane);
+                } else {
+                    tile_mma_lr<NCB>(o, sQ + 16 * I * LDK, LDK, sb, lane);
+                }
+                tile_mma_ll<C>(o, sP + 16 * I * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * I + 4 * lg + i;
+                    float val = o[i];
+                    if constexpr (!GATED) val = val / sDen[t];
+                    if (t < n) store1(oh + static_cast<size_t>(c0 + t) * p.d_v + vch, val);
+                }
             }
-            tile_mma_ll<C>(o, sP + 16 * I * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * I + 4 * lg + i;
-                float val = o[i];
-                if constexpr (!GATED) val = val / sDen[t];
-                if (t < n) store1(oh + static_cast<size_t>(c0 + t) * p.d_v + vch, val);
+            for (int cb = 0; cb < NCB; ++cb) {
+                if constexpr (GATED) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[cb][i] *= sD[16 * cb + 4 * lg + i];
+                }
+                tile_mma_ll<C>(st[cb], sKt + 16 * cb * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
             }
-        }
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            if constexpr (GATED) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st[cb][i] *= sD[16 * cb + 4 * lg + i];
-            }
-            tile_mma_ll<C>(st[cb], sKt + 16 * cb * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
         }
         __syncthreads();
     }
 
-    if (p.S_T) {
+    if (p.S_T && wave < WS) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
             *reinterpret_cast<float4 *>(p.S_T + srow + 16 * cb + 4 * lg) =
@@ -345,15 +395,17 @@ __global__ void __launch_bounds__(DVB * 4) linear_chunk_kernel(const ChunkParams
 
 // ------------------------------------------------------------------ dispatch
 
+constexpr int kLinearWaves = 8;   // waves per workgroup
+
 template <bool GATED, int PHI, class DT, int DK, int DVB, int C>
 static hipError_t launch_linear_t(const ChunkArgs &a) {
     ChunkParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.beta = nullptr; p.S0 = a.S0; p.z0 = a.z0;
     p.out = a.out; p.S_T = a.S_T; p.z_T = a.z_T;
-    p.T = a.T; p.d_v = a.d_v; p.n_vblk = a.d_v / DVB;
-    const int64_t blocks = static_cast<int64_t>(a.B) * a.H * p.n_vblk;
-    hipLaunchKernelGGL((linear_chunk_kernel<GATED, PHI, DT, DK, DVB, C>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(DVB * 4), 0, a.stream, p);
+    p.T = a.T; p.d_v = a.d_v; p.n_vblk = a.d_v / DVB; p.n_heads = a.B * a.H;
+    const int64_t blocks = static_cast<int64_t>(p.n_heads) * p.n_vblk;
+    hipLaunchKernelGGL((linear_chunk_kernel<GATED, PHI, DT, DK, DVB, C, kLinearWaves>),
+                       dim3(static_cast<uint32_t>(blocks)), dim3(kLinearWaves * 64), 0, a.stream, p);
     return hipGetLastError();
 }
 

@@ -20,17 +20,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
+// float -> bfloat16, round to nearest even: gfx950's v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))  // NaN stays NaN
-        return static_cast<bf16_t>((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<bf16_t>(u >> 16);
+    return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
-// two floats -> packed pair of bf16 (low half = a)
+// two floats -> packed pair of bf16 (low half = a), one conversion instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    const bf16x2_t h = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
