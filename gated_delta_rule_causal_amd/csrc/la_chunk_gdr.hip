@@ -30,13 +30,34 @@
 
 namespace la {
 
-// LDS bytes of one workgroup of gdr_chunk_kernel<DT, DK, DVB, C>.
+// LDS bytes of one workgroup of gdr_chunk_kernel<DT, DK, DVB, C>: two sets of
+// chunk tiles (Q, K, V, P, T, gate values) plus the float32 solve tile and the
+// output staging tile.
 template <class DT, int DK, int DVB, int C>
 constexpr int gdr_lds_bytes() {
     typedef typename OpOf<DT>::type Op;
     constexpr int PAD = 16 / sizeof(Op);
-    return (2 * C * (DK + PAD) + 2 * C * (C + PAD) + 2 * C * (DVB + PAD) + DK * (C + PAD)) * (int)sizeof(Op) +
-           C * (C + 4) * 4 + 4 * C * 4 + 4;
+    return 2 * (2 * C * (DK + PAD) + 2 * C * (C + PAD) + C * (DVB + PAD)) * (int)sizeof(Op) +
+           C * (DVB + PAD) * (int)sizeof(Op) + C * (C + 4) * 4 + 2 * (4 * C + 1) * 4;
+}
+
+// A-operand group of K^T for key channel c = c0 + lane%16 and tokens
+// t0 + 4*(lane/16) .. +3, read from the natural-layout K tile (rows = tokens).
+// bf16: one transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
+// group, lane a supplies row t0 + 4*(lane/16) + a/4, columns c0 + 4*(a%4)..+3,
+// and lane j receives column c0 + j of the group's four rows.
+__device__ __forceinline__ uint2 kt_group(const bf16_t *sK, int ldk, int t0, int c0, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int a = lane & 15, g = lane >> 4;
+    const bf16_t *src = sK + (t0 + 4 * g + (a >> 2)) * ldk + c0 + 4 * (a & 3);
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)((__attribute__((address_space(3))) bf16_t *)src));
+    return __builtin_bit_cast(uint2, r);
+}
+// float32: four scalar reads of the column
+__device__ __forceinline__ float4 kt_group(const float *sK, int ldk, int t0, int c0, int lane) {
+    const float *src = sK + (t0 + 4 * (lane >> 4)) * ldk + c0 + (lane & 15);
+    return make_float4(src[0], src[ldk], src[2 * ldk], src[3 * ldk]);
 }
 
 template <class DT, int DK, int DVB, int C, int NW>
@@ -46,6 +67,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     typedef Group<Op> Gp;
     typedef typename Gp::type G4;
     constexpr int WS = DVB / 16;         // state waves; wave w < WS owns value channels [16w, 16w + 16)
+    constexpr int NHW = NW - WS;         // helper waves: the state-independent work of the next chunk
     constexpr int NTHR = NW * 64;
     constexpr int NB = C / 16;           // 16-token blocks per chunk
     constexpr int NCB = DK / 16;         // 16-channel key blocks
@@ -54,28 +76,30 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     constexpr int LDC = C + PAD;
     constexpr int LDV = DVB + PAD;
     constexpr int LDA = C + 4;
-    constexpr int LDO = DVB + PAD;
     constexpr int VE = 16 / sizeof(Op);
-    static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && WS <= NW, "tiling");
+    constexpr int NLOW = NB * (NB + 1) / 2;
+    static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && NHW >= 1, "tiling");
     static_assert(gdr_lds_bytes<DT, DK, DVB, C>() <= 160 * 1024, "LDS budget");
 
-    __shared__ __align__(16) Op sQ[C * LDK];
-    __shared__ __align__(16) Op sK[C * LDK];
-    __shared__ __align__(16) Op sP[C * LDC];     // M o Gamma o Q K^T
-    __shared__ __align__(16) Op sT[C * LDC];     // (I + A)^{-1}
-    __shared__ __align__(16) Op sV[C * LDV];     // this block's value channels
-    __shared__ __align__(16) Op sO[C * LDO];     // output tile of the block, staged for 16-byte stores
-    __shared__ __align__(16) Op sKt[DK * LDC];   // K^T diag(e^{b_C - b}), operand of the state update
-    __shared__ __align__(16) float sA[C * LDA];  // A, then T, in float32 during the solve
-    __shared__ float sB[C], sEB[C], sBeta[C], sEBC[C];
-    __shared__ float sDecay;
+    __shared__ __align__(16) Op sQ[2][C * LDK];
+    __shared__ __align__(16) Op sK[2][C * LDK];
+    __shared__ __align__(16) Op sV[2][C * LDV];    // this block's value channels
+    __shared__ __align__(16) Op sP[2][C * LDC];    // M o Gamma o Q K^T
+    __shared__ __align__(16) Op sT[2][C * LDC];    // (I + A)^{-1}
+    __shared__ __align__(16) Op sO[C * LDV];       // output tile, staged for 16-byte stores
+    __shared__ __align__(16) float sA[C * LDA];    // A, then the blocks of T, in float32 during the solve
+    __shared__ __align__(16) float sB[2][C], sEB[2][C], sBeta[2][C], sEBC[2][C];
+    __shared__ float sDecay[2];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
+    const bool state_wave = wave < WS;
+    const int hw = wave - WS;                      // helper index (valid when !state_wave)
+    const int htid = tid - WS * 64;                // helper thread index
     int bh, vb;
     block_to_head(blockIdx.x, p.n_heads, p.n_vblk, bh, vb);
     const int vloc = 16 * wave + lr;               // value channel within the block (state waves)
-    const int vch = vb * DVB + vloc;               // value channel of this lane's column
+    const int vch = vb * DVB + vloc;
     const size_t tok0 = static_cast<size_t>(bh) * p.T;
     const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
     const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
@@ -83,229 +107,328 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     IO *oh = static_cast<IO *>(p.out) + tok0 * p.d_v;
     const float *gh = p.gate + tok0;
     const float *bth = p.beta + tok0;
+    const int nchunks = (p.T + C - 1) / C;
 
     // state slice S^T[c][v] for c in key block cb, v = this lane's column (state waves)
     f32x4 st[NCB];
-    const size_t srow = (static_cast<size_t>(bh) * p.d_v + (wave < WS ? vch : 0)) * DK;
+    const size_t srow = (static_cast<size_t>(bh) * p.d_v + (state_wave ? vch : 0)) * DK;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         st[cb] = zero4();
-        if (p.S0 && wave < WS) {
-            const float4 s = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
-            st[cb] = f32x4{s.x, s.y, s.z, s.w};
+        if (p.S0 && state_wave) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
+            st[cb] = f32x4{s4.x, s4.y, s4.z, s4.w};
         }
     }
 
-    // chunk inputs staged one chunk ahead in registers
+    // ---------------------------------------------------------------- stages
     TilePrefetch<C, DK, NTHR, IO> pq, pk;
     TilePrefetch<C, DVB, NTHR, IO> pv;
-    float pg = 1.f, pb = 0.f;   // wave 0, lane t: gate and beta of token t (padding: g = 1, beta = 0)
-    auto prefetch = [&](int c0) {
-        const int n = min(C, p.T - c0);
+    // the gate scan runs on the last wave, which has no block column of the
+    // off-diagonal inverse to work on
+    constexpr int SCAN_WAVE = NW - 1;
+    static_assert(NHW >= NB + 1 || NB == 1, "a helper wave must be free for the gate scan");
+    float pg = 1.f, pb = 0.f;   // SCAN_WAVE, lane t: gate and beta of token t (padding: g = 1, beta = 0)
+    auto prefetch = [&](int c) {
+        const int c0 = c * C, n = min(C, p.T - c0);
         pq.load(qh + static_cast<size_t>(c0) * DK, DK, n, tid);
         pk.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
         pv.load(vh + static_cast<size_t>(c0) * p.d_v, p.d_v, n, tid);
-        if (wave == 0) {
+        if (wave == SCAN_WAVE) {
             pg = lane < n ? gh[c0 + lane] : 1.f;
             pb = lane < n ? bth[c0 + lane] : 0.f;
         }
     };
-    if (p.T > 0) prefetch(0);
-
-    for (int c0 = 0; c0 < p.T; c0 += C) {
-        const int n = min(C, p.T - c0);
-
-        // ---- commit the staged chunk; gate scan on wave 0
-        pq.store(sQ, LDK, tid);
-        pk.store(sK, LDK, tid);
-        pv.store(sV, LDV, tid);
-        if (wave == 0) {
+    // registers -> buffer `buf`
+    auto commit = [&](int buf) {
+        pq.store(sQ[buf], LDK, tid);
+        pk.store(sK[buf], LDK, tid);
+        pv.store(sV[buf], LDV, tid);
+    };
+    // SCAN_WAVE: cumulative log-gates of the staged chunk into buffer `buf`
+    auto scan = [&](int buf) {
+        if (wave == SCAN_WAVE) {
             const float b = wave_inclusive_sum(__logf(pg), lane);
             const float bC = __shfl(b, C - 1, 64);
             if (lane < C) {
-                sB[lane] = b;
-                sEB[lane] = __expf(b);
-                sEBC[lane] = __expf(bC - b);
-                sBeta[lane] = pb;
+                sB[buf][lane] = b;
+                sEB[buf][lane] = __expf(b);
+                sEBC[buf][lane] = __expf(bC - b);
+                sBeta[buf][lane] = pb;
             }
-            if (lane == 0) sDecay = __expf(bC);
+            if (lane == 0) sDecay[buf] = __expf(bC);
         }
-        __syncthreads();
-        if (c0 + C < p.T) prefetch(c0 + C);
-
-        // ---- scores: P = M o Gamma o Q K^T and A = strict(beta Gamma o K K^T), the
-        // NB(NB+1)/2 lower 16x16 tiles; one wave computes the Q and K tiles of a
-        // (I, J) pair from the same K fragments.  Upper tiles are zero.
-        constexpr int NLOW = NB * (NB + 1) / 2;
-        for (int tt = wave; tt < NLOW; tt += NW) {
+    };
+    // scores of buffer `buf`: P and A (lower tiles; upper tiles of P and T zero);
+    // work split over waves [w0, w0 + nw)
+    auto scores = [&](int buf, int w0, int nw) {
+        const Op *Q = sQ[buf], *K = sK[buf];
+        const float *bb = sB[buf], *beta = sBeta[buf];
+        Op *P = sP[buf], *Tt = sT[buf];
+        for (int tt = wave - w0; tt < NLOW; tt += nw) {
             int I = 0;
             while ((I + 1) * (I + 2) / 2 <= tt) ++I;
             const int J = tt - I * (I + 1) / 2;
             const int row = 16 * I + 4 * lg, col = 16 * J + lr;
             f32x4 aq = zero4(), ak = zero4();
-            {
-                const Op *qr = sQ + (16 * I + lr) * LDK + 4 * lg;
-                const Op *kr = sK + (16 * I + lr) * LDK + 4 * lg;
-                const Op *br = sK + (16 * J + lr) * LDK + 4 * lg;
+            const Op *qr = Q + (16 * I + lr) * LDK + 4 * lg;
+            const Op *kr = K + (16 * I + lr) * LDK + 4 * lg;
+            const Op *br = K + (16 * J + lr) * LDK + 4 * lg;
 #pragma unroll
-                for (int k = 0; k + 32 <= DK; k += 32) {
-                    const auto b0 = ld_group(br + k), b1 = ld_group(br + k + 16);
-                    mma32(aq, ld_group(qr + k), ld_group(qr + k + 16), b0, b1);
-                    mma32(ak, ld_group(kr + k), ld_group(kr + k + 16), b0, b1);
-                }
-                if constexpr (DK % 32 == 16) {
-                    const auto b0 = ld_group(br + DK - 16);
-                    mma16(aq, ld_group(qr + DK - 16), b0);
-                    mma16(ak, ld_group(kr + DK - 16), b0);
-                }
+            for (int k = 0; k + 32 <= DK; k += 32) {
+                const auto b0 = ld_group(br + k), b1 = ld_group(br + k + 16);
+                mma32(aq, ld_group(qr + k), ld_group(qr + k + 16), b0, b1);
+                mma32(ak, ld_group(kr + k), ld_group(kr + k + 16), b0, b1);
             }
-            const float bj = sB[col];
+            if constexpr (DK % 32 == 16) {
+                const auto b0 = ld_group(br + DK - 16);
+                mma16(aq, ld_group(qr + DK - 16), b0);
+                mma16(ak, ld_group(kr + DK - 16), b0);
+            }
+            const float bj = bb[col];
+            const float4 bt4 = *reinterpret_cast<const float4 *>(bb + row);
+            const float4 be4 = *reinterpret_cast<const float4 *>(beta + row);
+            const float btv[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
+            const float bev[4] = {be4.x, be4.y, be4.z, be4.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = row + i;
-                const float gam = __expf(fminf(sB[t] - bj, 0.f));
-                sA[t * LDA + col] = col < t ? sBeta[t] * gam * ak[i] : 0.f;
-                from_f32(sP[t * LDC + col], col <= t ? gam * aq[i] : 0.f);
+                const float gam = __expf(fminf(btv[i] - bj, 0.f));
+                const float a = bev[i] * gam * ak[i];
+                const float pv = gam * aq[i];
+                sA[t * LDA + col] = col < t ? a : 0.f;
+                from_f32(P[t * LDC + col], col <= t ? pv : 0.f);
             }
         }
-        // zero tiles above the block diagonal of P and T
-        for (int e = tid; e < NB * NB * 16 * 2; e += NTHR) {
+        for (int e = tid - w0 * 64; e < NB * NB * 16 * 2; e += nw * 64) {
             const int tile = e / 32, r16 = (e % 32) / 2, half = e & 1;
             const int I = tile / NB, J = tile % NB;
             if (J <= I) continue;
-            Op *pr = sP + (16 * I + r16) * LDC + 16 * J + 8 * half;
-            Op *trow = sT + (16 * I + r16) * LDC + 16 * J + 8 * half;
+            Op *pr = P + (16 * I + r16) * LDC + 16 * J + 8 * half;
+            Op *trow = Tt + (16 * I + r16) * LDC + 16 * J + 8 * half;
 #pragma unroll
             for (int z = 0; z < 8; ++z) { pr[z] = Op(0); trow[z] = Op(0); }
         }
-        // K^T diag(e^{b_C - b}) for the state update: a lane takes two tokens of
-        // eight key channels and writes token pairs as one 32-bit word per channel
-        for (int e = tid; e < (C / 2) * (DK / 8); e += NTHR) {
-            const int tp = e % (C / 2), cg = e / (C / 2);
-            const int t0 = 2 * tp;
-            const float s0 = sEBC[t0], s1 = sEBC[t0 + 1];
-            float x0[8], x1[8];
-            if constexpr (VE == 8) {
-                load8(reinterpret_cast<const bf16_t *>(sK + t0 * LDK + 8 * cg), x0);
-                load8(reinterpret_cast<const bf16_t *>(sK + (t0 + 1) * LDK + 8 * cg), x1);
+    };
+    // diagonal 16x16 blocks of T = (I + A)^{-1} by forward substitution, one lane
+    // per column of each block (one wave), written over A's diagonal blocks
+    auto diag_inverse = [&]() {
+        if (lane >= 16 * NB) return;
+        const int blk = lane >> 4, nn = lane & 15;
+        float *Ab = sA + 16 * blk * LDA + 16 * blk;
+        float x[16];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<uint32_t *>(sKt + (8 * cg + i) * LDC + t0) = pack_bf16x2(x0[i] * s0, x1[i] * s1);
-            } else {
-                load8(reinterpret_cast<const float *>(sK + t0 * LDK + 8 * cg), x0);
-                load8(reinterpret_cast<const float *>(sK + (t0 + 1) * LDK + 8 * cg), x1);
+        for (int m = 0; m < 16; ++m) x[m] = m == nn ? 1.f : 0.f;
+        float4 row[4], nxt[4];
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<float2 *>(sKt + (8 * cg + i) * LDC + t0) = make_float2(x0[i] * s0, x1[i] * s1);
+        for (int q4 = 0; q4 < 4; ++q4) row[q4] = *reinterpret_cast<const float4 *>(Ab + 1 * LDA + 4 * q4);
+#pragma unroll
+        for (int t = 1; t < 16; ++t) {
+            if (t + 1 < 16) {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *reinterpret_cast<const float4 *>(Ab + (t + 1) * LDA + 4 * q4);
             }
-        }
-        __syncthreads();
-
-        // ---- T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (wave 0,
-        // one lane per column of each block), written over A's diagonal blocks
-        if (wave == 0 && lane < 16 * NB) {
-            const int blk = lane >> 4, nn = lane & 15;
-            float *Ab = sA + 16 * blk * LDA + 16 * blk;
-            float x[16];
+            float a[16];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) x[m] = m == nn ? 1.f : 0.f;
-#pragma unroll
-            for (int t = 1; t < 16; ++t) {
-                float s4[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: shorter dependency chains
-#pragma unroll
-                for (int m = 0; m < t; ++m) s4[m & 3] += Ab[t * LDA + m] * x[m];
-                if (t > nn) x[t] = -((s4[0] + s4[1]) + (s4[2] + s4[3]));
+            for (int q4 = 0; q4 < 4; ++q4) {
+                a[4 * q4] = row[q4].x; a[4 * q4 + 1] = row[q4].y; a[4 * q4 + 2] = row[q4].z; a[4 * q4 + 3] = row[q4].w;
             }
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: shorter dependency chains
 #pragma unroll
-            for (int t = 0; t < 16; ++t) Ab[t * LDA + nn] = x[t];
+            for (int m = 0; m < t; ++m) s4[m & 3] += a[m] * x[m];
+            if (t > nn) x[t] = -((s4[0] + s4[1]) + (s4[2] + s4[3]));
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) row[q4] = nxt[q4];
         }
-        __syncthreads();
-
-        // off-diagonal blocks, one block column per wave: T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj
+#pragma unroll
+        for (int t = 0; t < 16; ++t) Ab[t * LDA + nn] = x[t];
+    };
+    // off-diagonal blocks of T into buffer `buf`, one block column per helper wave:
+    // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj (matrix cores in the operand type)
+    auto offdiag = [&](int buf, int w0, int nw) {
+        Op *Tt = sT[buf];
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            if (j % NW != wave) continue;
-            float4 tb[NB];  // T_mj as B-operand groups (result layout), m >= j
+            if (j % nw != wave - w0) continue;
+            G4 tb[NB];
             {
                 f32x4 d;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) d[i] = sA[(16 * j + 4 * lg + i) * LDA + 16 * j + lr];
-                tb[j] = Group<float>::make(d);
+                tb[j] = Gp::make(d);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) from_f32(sT[(16 * j + 4 * lg + i) * LDC + 16 * j + lr], d[i]);
+                for (int i = 0; i < 4; ++i) from_f32(Tt[(16 * j + 4 * lg + i) * LDC + 16 * j + lr], d[i]);
             }
 #pragma unroll
             for (int i = j + 1; i < NB; ++i) {
+                const float *ar = sA + (16 * i + lr) * LDA + 4 * lg;
+                auto agroup = [&](int m) {
+                    const float4 f = *reinterpret_cast<const float4 *>(ar + 16 * m);
+                    return Gp::make(f.x, f.y, f.z, f.w);
+                };
                 f32x4 acc = zero4();
+                int m = j;
 #pragma unroll
-                for (int m = j; m < i; ++m) mma16(acc, ld_group(sA + (16 * i + lr) * LDA + 16 * m + 4 * lg), tb[m]);
+                for (; m + 1 < i; m += 2) mma32(acc, agroup(m), agroup(m + 1), tb[m], tb[m + 1]);
+                if (m < i) mma16(acc, agroup(m), tb[m]);
                 f32x4 tij = zero4();
-                mma16(tij, ld_group(sA + (16 * i + lr) * LDA + 16 * i + 4 * lg), Group<float>::make(acc));
+                mma16(tij, agroup(i), Gp::make(acc));
 #pragma unroll
                 for (int r = 0; r < 4; ++r) tij[r] = -tij[r];
-                tb[i] = Group<float>::make(tij);
+                tb[i] = Gp::make(tij);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) from_f32(sT[(16 * i + 4 * lg + r) * LDC + 16 * j + lr], tij[r]);
+                for (int r = 0; r < 4; ++r) from_f32(Tt[(16 * i + 4 * lg + r) * LDC + 16 * j + lr], tij[r]);
             }
         }
-        __syncthreads();
+    };
 
-        // ---- state-dependent part: this wave's 16 value channels, from registers
-        if (wave < WS) {
+    // output rows of chunk c (staged in sO), 16 bytes per lane, by the helpers
+    auto copy_out = [&](int c) {
+        const int c0 = c * C, n = min(C, p.T - c0);
+        for (int e = htid; e < n * (DVB / VE); e += NHW * 64) {
+            const int t = e / (DVB / VE), v = (e % (DVB / VE)) * VE;
+            *reinterpret_cast<uint4 *>(oh + static_cast<size_t>(c0 + t) * p.d_v + vb * DVB + v) =
+                *reinterpret_cast<const uint4 *>(sO + t * LDV + v);
+        }
+    };
+
+    // ---------------------------------------------------------------- prologue
+    if (nchunks > 0) {
+        prefetch(0);
+        commit(0);
+        scan(0);
+        __syncthreads();
+        if (nchunks > 1) prefetch(1);
+        scores(0, 0, NW);
+        __syncthreads();
+        if (wave == 0) diag_inverse();
+        __syncthreads();
+        offdiag(0, 0, NW);
+        __syncthreads();
+        if (nchunks > 1) {
+            commit(1);
+            scan(1);
+            __syncthreads();
+            if (nchunks > 2) prefetch(2);
+        }
+    }
+
+    // ---------------------------------------------------------------- chunk loop
+    for (int c = 0; c < nchunks; ++c) {
+        const int cur = c & 1, nxt = cur ^ 1;
+        const bool has_next = c + 1 < nchunks;
+
+        // step 1: state waves K S0^T, Q S0^T and the solve's right-hand side of chunk c;
+        // helpers: scores of chunk c+1
+        G4 yb[NB];
+        f32x4 qs[NB];
+        if (state_wave) {
             G4 sb[NCB];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
-            G4 yb[NB];
-            f32x4 qs[NB];
+            f32x4 ks[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) { ks[I] = zero4(); qs[I] = zero4(); }
+            const int ko = 4 * lg;
+#pragma unroll
+            for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    const Op *kr = sK[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
+                    const Op *qr = sQ[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
+                    mma32(ks[I], ld_group(kr), ld_group(kr + 16), sb[s2], sb[s2 + 1]);
+                    mma32(qs[I], ld_group(qr), ld_group(qr + 16), sb[s2], sb[s2 + 1]);
+                }
+            }
+            if constexpr (NCB % 2 == 1) {
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    mma16(ks[I], ld_group(sK[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
+                    mma16(qs[I], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
+                }
+            }
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
-                f32x4 ks = zero4();
-                tile_mma_lr<NCB>(ks, sK + 16 * I * LDK, LDK, sb, lane);
-                qs[I] = zero4();
-                tile_mma_lr<NCB>(qs[I], sQ + 16 * I * LDK, LDK, sb, lane);
+                const float4 be = *reinterpret_cast<const float4 *>(&sBeta[cur][16 * I + 4 * lg]);
+                const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
+                const Op *vr = sV[cur] + (16 * I + 4 * lg) * LDV + vloc;
                 f32x4 y;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * I + 4 * lg + i;
-                    y[i] = sBeta[t] * (to_f32(sV[t * LDV + vloc]) - sEB[t] * ks[i]);
-                }
+                y[0] = be.x * (to_f32(vr[0]) - eb.x * ks[I][0]);
+                y[1] = be.y * (to_f32(vr[LDV]) - eb.y * ks[I][1]);
+                y[2] = be.z * (to_f32(vr[2 * LDV]) - eb.z * ks[I][2]);
+                y[3] = be.w * (to_f32(vr[3 * LDV]) - eb.w * ks[I][3]);
                 yb[I] = Gp::make(y);
             }
+        } else {
+            // the previous chunk's outputs leave now, so that these stores have
+            // drained before the helpers next wait on their memory counter
+            if (c > 0) copy_out(c - 1);
+            if (has_next) scores(nxt, WS, NHW);
+        }
+        __syncthreads();
+
+        // step 2: state waves U = T Y and the outputs of chunk c; first helper: the
+        // diagonal blocks of chunk c+1's inverse
+        G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
+        float decay = 1.f;
+        if (state_wave) {
+            decay = sDecay[cur];
             G4 ub[NB];
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
                 f32x4 u = zero4();
-                tile_mma_lr_n<NB>(u, sT + 16 * I * LDC, LDC, yb, I + 1, lane);
+                tile_mma_lr_n<NB>(u, sT[cur] + 16 * I * LDC, LDC, yb, I + 1, lane);
                 ub[I] = Gp::make(u);
+                const float4 ec = *reinterpret_cast<const float4 *>(&sEBC[cur][16 * I + 4 * lg]);
+                usb[I] = Gp::make(u[0] * ec.x, u[1] * ec.y, u[2] * ec.z, u[3] * ec.w);
             }
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
                 f32x4 o = zero4();
-                tile_mma_lr_n<NB>(o, sP + 16 * I * LDC, LDC, ub, I + 1, lane);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * I + 4 * lg + i;
-                    from_f32(sO[t * LDO + vloc], o[i] + sEB[t] * qs[I][i]);
-                }
+                tile_mma_lr_n<NB>(o, sP[cur] + 16 * I * LDC, LDC, ub, I + 1, lane);
+                const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
+                Op *orow = sO + (16 * I + 4 * lg) * LDV + vloc;
+                from_f32(orow[0], o[0] + eb.x * qs[I][0]);
+                from_f32(orow[LDV], o[1] + eb.y * qs[I][1]);
+                from_f32(orow[2 * LDV], o[2] + eb.z * qs[I][2]);
+                from_f32(orow[3 * LDV], o[3] + eb.w * qs[I][3]);
             }
-            const float decay = sDecay;
+        } else if (has_next && hw == 0) {
+            diag_inverse();
+        }
+        __syncthreads();
+
+        // step 3: state waves S <- e^{b_C} S + K^T (U e^{b_C - b}); helpers: the
+        // off-diagonal inverse of chunk c+1 and the output rows of chunk c
+        if (state_wave) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) st[cb][i] *= decay;
-                tile_mma_lr<NB>(st[cb], sKt + 16 * cb * LDC, LDC, ub, lane);
+#pragma unroll
+                for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
+                    mma32(st[cb], kt_group(sK[cur], LDK, 16 * s2, 16 * cb, lane),
+                          kt_group(sK[cur], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
+                if constexpr (NB % 2 == 1) mma16(st[cb], kt_group(sK[cur], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
             }
+        } else {
+            if (has_next) offdiag(nxt, WS, NHW);
+            // chunk c+2's gate values (held by SCAN_WAVE) -> gate buffer cur, whose
+            // chunk-c values the state waves no longer read
+            if (c + 2 < nchunks) scan(cur);
         }
         __syncthreads();
-        // the block's output rows, 16 bytes per lane
-        for (int e = tid; e < n * (DVB / VE); e += NTHR) {
-            const int t = e / (DVB / VE), v = (e % (DVB / VE)) * VE;
-            *reinterpret_cast<uint4 *>(oh + static_cast<size_t>(c0 + t) * p.d_v + vb * DVB + v) =
-                *reinterpret_cast<const uint4 *>(sO + t * LDO + v);
+
+        // step 4: chunk c+2's tiles into the buffers chunk c has released
+        if (c + 2 < nchunks) {
+            commit(cur);
+            __syncthreads();
+            if (c + 3 < nchunks) prefetch(c + 3);
         }
     }
 
-    if (p.S_T && wave < WS) {
+    if (nchunks > 0 && !state_wave) copy_out(nchunks - 1);
+    if (p.S_T && state_wave) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
             *reinterpret_cast<float4 *>(p.S_T + srow + 16 * cb + 4 * lg) =
