@@ -23,6 +23,7 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
 // float -> bfloat16, round to nearest even: gfx950's v_cvt_pk_bf16_f32.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));

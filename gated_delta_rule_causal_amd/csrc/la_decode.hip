@@ -8,8 +8,10 @@
 // consecutive floats, two 16-byte loads per lane), every row of a workgroup
 // is loaded before any arithmetic so that all of a lane's loads are in
 // flight together, and the two row dot products a step needs are reduced
-// across the G lanes with lane shuffles.  No LDS, and no barrier except the
-// one the normalized variant needs before it overwrites the shared z.
+// across the G lanes with lane shuffles.  Workgroups of 1024 lanes keep at
+// most two rows per lane (few registers, many waves in flight); the new state
+// is written with non-temporal stores.  No LDS, and no barrier except the one
+// the normalized variant needs before it overwrites the shared z.
 //
 // Per-row arithmetic (row i of the d_v x d_k state, all in float32):
 //   gated delta rule (page "Linear Attention", decay first, then predict):
@@ -25,14 +27,16 @@
 
 namespace la {
 
+constexpr int kDecodeThreads = 1024;
+
 template <int VAR, class DT, int DK, int DV, int PHI>
-__global__ __launch_bounds__(256) void decode_kernel(
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const typename DT::storage *__restrict__ q, const typename DT::storage *__restrict__ k,
     const typename DT::storage *__restrict__ v, const float *__restrict__ gate,
     const float *__restrict__ beta, float *__restrict__ S, float *__restrict__ z,
     typename DT::storage *__restrict__ out, int64_t n_heads) {
     constexpr int G = DK / 8;                                // lanes per state row
-    constexpr int GROUPS = 256 / G;                          // row groups per workgroup
+    constexpr int GROUPS = kDecodeThreads / G;               // row groups per workgroup
     constexpr int HPW = GROUPS >= DV ? GROUPS / DV : 1;      // heads per workgroup
     constexpr int GPH = GROUPS / HPW;                        // groups per head
     constexpr int RPG = DV / GPH;                            // rows per group
@@ -130,9 +134,9 @@ __global__ __launch_bounds__(256) void decode_kernel(
     if (!active) return;
 #pragma unroll
     for (int r = 0; r < RPG; ++r) {
-        float4 *sp = reinterpret_cast<float4 *>(S + (h * DV + row0 + r * GPH) * DK + c0);
-        sp[0] = make_float4(s[r][0], s[r][1], s[r][2], s[r][3]);
-        sp[1] = make_float4(s[r][4], s[r][5], s[r][6], s[r][7]);
+        f32x4_t *sp = reinterpret_cast<f32x4_t *>(S + (h * DV + row0 + r * GPH) * DK + c0);
+        __builtin_nontemporal_store(f32x4_t{s[r][0], s[r][1], s[r][2], s[r][3]}, sp);
+        __builtin_nontemporal_store(f32x4_t{s[r][4], s[r][5], s[r][6], s[r][7]}, sp + 1);
         if (c0 == 0) store1(out + h * DV + row0 + r * GPH, vv[r]);
     }
 }
@@ -142,13 +146,13 @@ __global__ __launch_bounds__(256) void decode_kernel(
 template <int VAR, class DT, int DK, int DV, int PHI>
 static hipError_t launch_decode_t(const DecodeArgs &a) {
     constexpr int G = DK / 8;
-    constexpr int GROUPS = 256 / G;
+    constexpr int GROUPS = kDecodeThreads / G;
     constexpr int HPW = GROUPS >= DV ? GROUPS / DV : 1;
     const int64_t n_heads = static_cast<int64_t>(a.B) * a.H;
     const int64_t blocks = (n_heads + HPW - 1) / HPW;
     typedef typename DT::storage T;
     hipLaunchKernelGGL((decode_kernel<VAR, DT, DK, DV, PHI>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(256), 0, a.stream, static_cast<const T *>(a.q),
+                       dim3(kDecodeThreads), 0, a.stream, static_cast<const T *>(a.q),
                        static_cast<const T *>(a.k), static_cast<const T *>(a.v), a.gate, a.beta,
                        a.S, a.z, static_cast<T *>(a.out), n_heads);
     return hipGetLastError();
