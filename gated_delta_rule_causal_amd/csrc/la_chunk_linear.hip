@@ -427,9 +427,15 @@ static hipError_t linear_chunk(const ChunkArgs &a) {
     return hipErrorInvalidValue;
 }
 
+// Value-block width: the widest block (fewest duplicated state-independent
+// passes per head) that still gives about one workgroup per compute unit.
+constexpr int kComputeUnits = 256;
+
 template <bool GATED, int PHI, class DT, int DK>
 static hipError_t linear_dvb(const ChunkArgs &a) {
-    if (a.d_v >= 32) return linear_chunk<GATED, PHI, DT, DK, 32>(a);
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    if (a.d_v >= 64 && heads * (a.d_v / 64) >= kComputeUnits) return linear_chunk<GATED, PHI, DT, DK, 64>(a);
+    if (a.d_v >= 32 && heads * (a.d_v / 32) >= kComputeUnits) return linear_chunk<GATED, PHI, DT, DK, 32>(a);
     return linear_chunk<GATED, PHI, DT, DK, 16>(a);
 }
 
