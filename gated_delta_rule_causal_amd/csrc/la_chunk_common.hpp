@@ -55,12 +55,15 @@ struct TilePrefetch {
                 r[i] = *reinterpret_cast<const uint4 *>(src + row * lds + col);
         }
     }
+    // SW != 0: on rows with bit 3 set, element column c goes to c ^ SW
+    template <int SW = 0>
     __device__ __forceinline__ void store(E *dst, int ldd, int tid) const {
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = tid + i * NTHR;
+            const int row = e / VPR, col = (e % VPR) * VE;
             if (TOTAL % NTHR == 0 || e < TOTAL)
-                *reinterpret_cast<uint4 *>(dst + (e / VPR) * ldd + (e % VPR) * VE) = r[i];
+                *reinterpret_cast<uint4 *>(dst + row * ldd + (col ^ (SW * ((row >> 3) & 1)))) = r[i];
         }
     }
 };

@@ -33,11 +33,36 @@ namespace la {
 // LDS bytes of one workgroup of gdr_chunk_kernel<DT, DK, DVB, C>: two sets of
 // chunk tiles (Q, K, V, P, T, gate values) plus the float32 solve tile and the
 // output staging tile.
+// Layout of the Q and K tiles in LDS.  Two access patterns read them: row
+// reads (16 rows x 16 bytes per half wave, the matrix-core A/B operands) and,
+// for bfloat16 K, transposing reads (8 consecutive rows x 32 bytes per half
+// wave).  bfloat16 rows are 288 bytes apart (32 bytes of padding) and the
+// 16-byte column chunks of every row with bit 3 set are swapped in pairs
+// (element column c is stored at c ^ 8): both patterns then touch each of the
+// 64 four-byte banks once.  float32 tiles keep 16 bytes of padding and no swap.
+template <class Op>
+constexpr int gdr_kpad() { return sizeof(Op) == 2 ? 16 : 16 / (int)sizeof(Op); }
+template <class Op>
+constexpr int gdr_kswap() { return sizeof(Op) == 2 ? 8 : 0; }
+__device__ __forceinline__ int swap_col(int row, int col, int sw) { return col ^ (sw * ((row >> 3) & 1)); }
+
+// acc += X[0:16, 0:K] Y[0:16, 0:K]^T for two tiles in the Q/K layout above,
+// each starting at a row that is a multiple of 16.
+template <int K, int SW, class Op>
+__device__ __forceinline__ void tile_mma_qk(f32x4 &acc, const Op *x, const Op *y, int ld, int lane) {
+    const int off = (lane & 15) * ld + swap_col(lane & 15, 4 * (lane >> 4), SW);
+    const Op *xr = x + off, *yr = y + off;
+#pragma unroll
+    for (int k = 0; k + 32 <= K; k += 32)
+        mma32(acc, ld_group(xr + k), ld_group(xr + k + 16), ld_group(yr + k), ld_group(yr + k + 16));
+    if constexpr (K % 32 == 16) mma16(acc, ld_group(xr + K - 16), ld_group(yr + K - 16));
+}
+
 template <class DT, int DK, int DVB, int C>
 constexpr int gdr_lds_bytes() {
     typedef typename OpOf<DT>::type Op;
     constexpr int PAD = 16 / sizeof(Op);
-    return 2 * (2 * C * (DK + PAD) + 2 * C * (C + PAD) + C * (DVB + PAD)) * (int)sizeof(Op) +
+    return 2 * (2 * C * (DK + gdr_kpad<Op>()) + 2 * C * (C + PAD) + C * (DVB + PAD)) * (int)sizeof(Op) +
            C * (DVB + PAD) * (int)sizeof(Op) + C * (C + 4) * 4 + 2 * (4 * C + 1) * 4;
 }
 
@@ -46,10 +71,12 @@ constexpr int gdr_lds_bytes() {
 // bf16: one transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
 // group, lane a supplies row t0 + 4*(lane/16) + a/4, columns c0 + 4*(a%4)..+3,
 // and lane j receives column c0 + j of the group's four rows.
+// Rows are in the Q/K layout above (t0 and c0 multiples of 16).
 __device__ __forceinline__ uint2 kt_group(const bf16_t *sK, int ldk, int t0, int c0, int lane) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     const int a = lane & 15, g = lane >> 4;
-    const bf16_t *src = sK + (t0 + 4 * g + (a >> 2)) * ldk + c0 + 4 * (a & 3);
+    const int row = t0 + 4 * g + (a >> 2);
+    const bf16_t *src = sK + row * ldk + c0 + swap_col(row, 4 * (a & 3), gdr_kswap<bf16_t>());
     const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) v4i16 *)((__attribute__((address_space(3))) bf16_t *)src));
     return __builtin_bit_cast(uint2, r);
@@ -72,7 +99,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     constexpr int NB = C / 16;           // 16-token blocks per chunk
     constexpr int NCB = DK / 16;         // 16-channel key blocks
     constexpr int PAD = 16 / sizeof(Op);
-    constexpr int LDK = DK + PAD;        // row strides (elements) of the LDS tiles
+    constexpr int LDK = DK + gdr_kpad<Op>();   // row strides (elements) of the LDS tiles
+    constexpr int KSW = gdr_kswap<Op>();
     constexpr int LDC = C + PAD;
     constexpr int LDV = DVB + PAD;
     constexpr int LDA = C + 4;
@@ -91,7 +119,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     __shared__ __align__(16) float sB[2][C], sEB[2][C], sBeta[2][C], sEBC[2][C];
     __shared__ float sDecay[2];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform: role branches compile to scalar branches
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const bool state_wave = wave < WS;
     const int hw = wave - WS;                      // helper index (valid when !state_wave)
@@ -120,6 +149,11 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             st[cb] = f32x4{s4.x, s4.y, s4.z, s4.w};
         }
     }
+    // Wait for the entering state here, before any tile load is issued: the
+    // compiler cannot tell that a wave keeps its role, so a state register still
+    // pending at the loop entry would cost a full wait on the global-memory
+    // counter (including the tile prefetch in flight) inside every chunk.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // ---------------------------------------------------------------- stages
     TilePrefetch<C, DK, NTHR, IO> pq, pk;
@@ -141,8 +175,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     };
     // registers -> buffer `buf`
     auto commit = [&](int buf) {
-        pq.store(sQ[buf], LDK, tid);
-        pk.store(sK[buf], LDK, tid);
+        pq.template store<KSW>(sQ[buf], LDK, tid);
+        pk.template store<KSW>(sK[buf], LDK, tid);
         pv.store(sV[buf], LDV, tid);
     };
     // SCAN_WAVE: cumulative log-gates of the staged chunk into buffer `buf`
@@ -159,55 +193,37 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             if (lane == 0) sDecay[buf] = __expf(bC);
         }
     };
-    // scores of buffer `buf`: P and A (lower tiles; upper tiles of P and T zero);
-    // work split over waves [w0, w0 + nw)
-    auto scores = [&](int buf, int w0, int nw) {
-        const Op *Q = sQ[buf], *K = sK[buf];
+    // lower score tiles of buffer `buf`, work split over waves [w0, w0 + nw):
+    // isK: A = diag(beta) (Gamma o K K^T), strictly lower, in float32 for the
+    // inverse; else P = M o Gamma o Q K^T in the operand type.  Tiles above the
+    // block diagonal are never read (the products below stop at the diagonal).
+    auto score_tiles = [&](int buf, bool isK, int w0, int nw) {
+        const Op *X = isK ? sK[buf] : sQ[buf], *K = sK[buf];
         const float *bb = sB[buf], *beta = sBeta[buf];
-        Op *P = sP[buf], *Tt = sT[buf];
+        Op *P = sP[buf];
         for (int tt = wave - w0; tt < NLOW; tt += nw) {
             int I = 0;
             while ((I + 1) * (I + 2) / 2 <= tt) ++I;
             const int J = tt - I * (I + 1) / 2;
-            const int row = 16 * I + 4 * lg, col = 16 * J + lr;
-            f32x4 aq = zero4(), ak = zero4();
-            const Op *qr = Q + (16 * I + lr) * LDK + 4 * lg;
-            const Op *kr = K + (16 * I + lr) * LDK + 4 * lg;
-            const Op *br = K + (16 * J + lr) * LDK + 4 * lg;
-#pragma unroll
-            for (int k = 0; k + 32 <= DK; k += 32) {
-                const auto b0 = ld_group(br + k), b1 = ld_group(br + k + 16);
-                mma32(aq, ld_group(qr + k), ld_group(qr + k + 16), b0, b1);
-                mma32(ak, ld_group(kr + k), ld_group(kr + k + 16), b0, b1);
+            // the product is taken transposed (K_J X_I^T), so that each lane holds
+            // four consecutive columns s of one row t and writes them at once
+            const int t = 16 * I + lr, s0 = 16 * J + 4 * lg;
+            f32x4 acc = zero4();
+            tile_mma_qk<DK, KSW>(acc, K + 16 * J * LDK, X + 16 * I * LDK, LDK, lane);
+            const float bt = bb[t];
+            const float4 bs = *reinterpret_cast<const float4 *>(bb + s0);
+            const float g0 = __expf(fminf(bt - bs.x, 0.f)), g1 = __expf(fminf(bt - bs.y, 0.f));
+            const float g2 = __expf(fminf(bt - bs.z, 0.f)), g3 = __expf(fminf(bt - bs.w, 0.f));
+            if (isK) {
+                const float be = beta[t];
+                *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
+                    make_float4(s0 < t ? be * g0 * acc[0] : 0.f, s0 + 1 < t ? be * g1 * acc[1] : 0.f,
+                                s0 + 2 < t ? be * g2 * acc[2] : 0.f, s0 + 3 < t ? be * g3 * acc[3] : 0.f);
+            } else {
+                st_group(P + t * LDC + s0,
+                         Gp::make(s0 <= t ? g0 * acc[0] : 0.f, s0 + 1 <= t ? g1 * acc[1] : 0.f,
+                                  s0 + 2 <= t ? g2 * acc[2] : 0.f, s0 + 3 <= t ? g3 * acc[3] : 0.f));
             }
-            if constexpr (DK % 32 == 16) {
-                const auto b0 = ld_group(br + DK - 16);
-                mma16(aq, ld_group(qr + DK - 16), b0);
-                mma16(ak, ld_group(kr + DK - 16), b0);
-            }
-            const float bj = bb[col];
-            const float4 bt4 = *reinterpret_cast<const float4 *>(bb + row);
-            const float4 be4 = *reinterpret_cast<const float4 *>(beta + row);
-            const float btv[4] = {bt4.x, bt4.y, bt4.z, bt4.w};
-            const float bev[4] = {be4.x, be4.y, be4.z, be4.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = row + i;
-                const float gam = __expf(fminf(btv[i] - bj, 0.f));
-                const float a = bev[i] * gam * ak[i];
-                const float pv = gam * aq[i];
-                sA[t * LDA + col] = col < t ? a : 0.f;
-                from_f32(P[t * LDC + col], col <= t ? pv : 0.f);
-            }
-        }
-        for (int e = tid - w0 * 64; e < NB * NB * 16 * 2; e += nw * 64) {
-            const int tile = e / 32, r16 = (e % 32) / 2, half = e & 1;
-            const int I = tile / NB, J = tile % NB;
-            if (J <= I) continue;
-            Op *pr = P + (16 * I + r16) * LDC + 16 * J + 8 * half;
-            Op *trow = Tt + (16 * I + r16) * LDC + 16 * J + 8 * half;
-#pragma unroll
-            for (int z = 0; z < 8; ++z) { pr[z] = Op(0); trow[z] = Op(0); }
         }
     };
     // diagonal 16x16 blocks of T = (I + A)^{-1} by forward substitution, one lane
@@ -299,7 +315,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         scan(0);
         __syncthreads();
         if (nchunks > 1) prefetch(1);
-        scores(0, 0, NW);
+        if (wave < NW / 2) score_tiles(0, true, 0, NW / 2);
+        else score_tiles(0, false, NW / 2, NW - NW / 2);
         __syncthreads();
         if (wave == 0) diag_inverse();
         __syncthreads();
@@ -319,9 +336,9 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         const bool has_next = c + 1 < nchunks;
 
         // step 1: state waves K S0^T, Q S0^T and the solve's right-hand side of chunk c;
-        // helpers: scores of chunk c+1
+        // helpers: the K K^T tiles of chunk c+1
         G4 yb[NB];
-        f32x4 qs[NB];
+        f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
         if (state_wave) {
             G4 sb[NCB];
 #pragma unroll
@@ -329,7 +346,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             f32x4 ks[NB];
 #pragma unroll
             for (int I = 0; I < NB; ++I) { ks[I] = zero4(); qs[I] = zero4(); }
-            const int ko = 4 * lg;
+            const int ko = swap_col(lr, 4 * lg, KSW);   // rows 16 I + lr
 #pragma unroll
             for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
 #pragma unroll
@@ -337,14 +354,14 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     const Op *kr = sK[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
                     const Op *qr = sQ[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
                     mma32(ks[I], ld_group(kr), ld_group(kr + 16), sb[s2], sb[s2 + 1]);
-                    mma32(qs[I], ld_group(qr), ld_group(qr + 16), sb[s2], sb[s2 + 1]);
+                    mma32(qs[I], sb[s2], sb[s2 + 1], ld_group(qr), ld_group(qr + 16));
                 }
             }
             if constexpr (NCB % 2 == 1) {
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
                     mma16(ks[I], ld_group(sK[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
-                    mma16(qs[I], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
+                    mma16(qs[I], sb[NCB - 1], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)));
                 }
             }
 #pragma unroll
@@ -363,12 +380,12 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             // the previous chunk's outputs leave now, so that these stores have
             // drained before the helpers next wait on their memory counter
             if (c > 0) copy_out(c - 1);
-            if (has_next) scores(nxt, WS, NHW);
+            if (has_next) score_tiles(nxt, true, WS, NHW);
         }
         __syncthreads();
 
         // step 2: state waves U = T Y and the outputs of chunk c; first helper: the
-        // diagonal blocks of chunk c+1's inverse
+        // diagonal blocks of chunk c+1's inverse; other helpers: its Q K^T tiles
         G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
         float decay = 1.f;
         if (state_wave) {
@@ -384,17 +401,17 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             }
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
+                // O^T = U^T P^T: lane holds values 16*wave + 4*lg..+3 of token 16 I + lr
                 f32x4 o = zero4();
-                tile_mma_lr_n<NB>(o, sP[cur] + 16 * I * LDC, LDC, ub, I + 1, lane);
-                const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
-                Op *orow = sO + (16 * I + 4 * lg) * LDV + vloc;
-                from_f32(orow[0], o[0] + eb.x * qs[I][0]);
-                from_f32(orow[LDV], o[1] + eb.y * qs[I][1]);
-                from_f32(orow[2 * LDV], o[2] + eb.z * qs[I][2]);
-                from_f32(orow[3 * LDV], o[3] + eb.w * qs[I][3]);
+                tile_mma_rl_n<NB>(o, ub, sP[cur] + 16 * I * LDC, LDC, I + 1, lane);
+                const float eb = sEB[cur][16 * I + lr];
+                st_group(sO + (16 * I + lr) * LDV + 16 * wave + 4 * lg,
+                         Gp::make(o[0] + eb * qs[I][0], o[1] + eb * qs[I][1], o[2] + eb * qs[I][2],
+                                  o[3] + eb * qs[I][3]));
             }
-        } else if (has_next && hw == 0) {
-            diag_inverse();
+        } else if (has_next) {
+            if (hw == 0) diag_inverse();
+            else score_tiles(nxt, false, WS + 1, NHW - 1);
         }
         __syncthreads();
 

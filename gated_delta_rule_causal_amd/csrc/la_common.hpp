@@ -63,6 +63,10 @@ __device__ __forceinline__ float load1(const bf16_t *p) { return bf16_to_f32(*p)
 __device__ __forceinline__ void store1(float *p, float x) { *p = x; }
 __device__ __forceinline__ void store1(bf16_t *p, float x) { *p = f32_to_bf16(x); }
 
+// s_waitcnt immediate (gfx9 encoding) that waits for every outstanding vector
+// memory load and leaves the LDS and export counters free.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ------------------------------------------------------------- feature map
 
 // elu(x) + 1: x + 1 above zero, exp(x) at or below zero (always > 0).

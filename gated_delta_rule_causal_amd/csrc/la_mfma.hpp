@@ -128,4 +128,20 @@ __device__ __forceinline__ void tile_mma_lr_n(f32x4 &acc, const Op *a, int lda, 
     }
 }
 
+// acc += Areg * B over the first `nk` (<= NKMAX) k-blocks, with the A operand
+// in registers as groups (result-layout tiles of A^T, one per k-block) and B
+// supplied transposed from LDS: row n of `b` (rows ldb apart) holds column n
+// of B with k contiguous.  The result is the transpose of what tile_mma_lr_n
+// gives for the swapped product, so each lane ends up with four consecutive
+// columns of one row of that product.
+template <int NKMAX, class Op, class G>
+__device__ __forceinline__ void tile_mma_rl_n(f32x4 &acc, const G *ag, const Op *b, int ldb, int nk, int lane) {
+    const Op *br = b + (lane & 15) * ldb + 4 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < NKMAX; s += 2) {
+        if (s + 2 <= nk) mma32(acc, ag[s], ag[s + 1], ld_group(br + 16 * s), ld_group(br + 16 * s + 16));
+        else if (s + 1 == nk) mma16(acc, ag[s], ld_group(br + 16 * s));
+    }
+}
+
 }  // namespace la
