@@ -106,6 +106,9 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     constexpr int LDA = C + 4;
     constexpr int VE = 16 / sizeof(Op);
     constexpr int NLOW = NB * (NB + 1) / 2;
+    constexpr bool S32 = sizeof(Op) == 2 && C % 32 == 0;   // scores in 32x32 jobs
+    constexpr int NJ32 = (C / 32) * (C / 32 + 1) / 2;
+    static_assert(!S32 || NJ32 <= NHW, "one helper wave per score job");
     static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && NHW >= 1, "tiling");
     static_assert(gdr_lds_bytes<DT, DK, DVB, C>() <= 160 * 1024, "LDS budget");
 
@@ -226,6 +229,53 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             }
         }
     };
+    // bfloat16 chunks of 32 or 64 tokens: the scores in 32x32 jobs.  Job
+    // (I, J), I >= J over 32-token blocks, forms K_J Q_I^T and K_J K_I^T in one
+    // pass over the key channels (K_J is the shared A operand and, on the
+    // diagonal, also the B operand of K K^T); each lane then holds sixteen
+    // columns s of one row t, written four at a time.
+    auto score_job32 = [&](int buf, int job) {
+        if constexpr (S32) {
+            int I = 0;
+            while ((I + 1) * (I + 2) / 2 <= job) ++I;
+            const int J = job - I * (I + 1) / 2;
+            const int r = lane & 31, h = lane >> 5;
+            const int off = r * LDK + swap_col(r, 8 * h, KSW);
+            const Op *aJ = sK[buf] + 32 * J * LDK + off;
+            const Op *bQ = sQ[buf] + 32 * I * LDK + off, *bK = sK[buf] + 32 * I * LDK + off;
+            f32x16 ap = {}, ak = {};
+            if (I == J) {
+#pragma unroll
+                for (int kk = 0; kk < DK / 16; ++kk) {
+                    const uint4 a = *reinterpret_cast<const uint4 *>(aJ + 16 * kk);
+                    mma32x32(ap, a, *reinterpret_cast<const uint4 *>(bQ + 16 * kk));
+                    mma32x32(ak, a, a);
+                }
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < DK / 16; ++kk) {
+                    const uint4 a = *reinterpret_cast<const uint4 *>(aJ + 16 * kk);
+                    mma32x32(ap, a, *reinterpret_cast<const uint4 *>(bQ + 16 * kk));
+                    mma32x32(ak, a, *reinterpret_cast<const uint4 *>(bK + 16 * kk));
+                }
+            }
+            const int t = 32 * I + r;
+            const float bt = sB[buf][t], be = sBeta[buf][t];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s0 = 32 * J + 8 * q + 4 * h;
+                const float4 bs = *reinterpret_cast<const float4 *>(sB[buf] + s0);
+                const float g0 = __expf(fminf(bt - bs.x, 0.f)), g1 = __expf(fminf(bt - bs.y, 0.f));
+                const float g2 = __expf(fminf(bt - bs.z, 0.f)), g3 = __expf(fminf(bt - bs.w, 0.f));
+                st_group(sP[buf] + t * LDC + s0,
+                         Gp::make(s0 <= t ? g0 * ap[4 * q] : 0.f, s0 + 1 <= t ? g1 * ap[4 * q + 1] : 0.f,
+                                  s0 + 2 <= t ? g2 * ap[4 * q + 2] : 0.f, s0 + 3 <= t ? g3 * ap[4 * q + 3] : 0.f));
+                *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
+                    make_float4(s0 < t ? be * g0 * ak[4 * q] : 0.f, s0 + 1 < t ? be * g1 * ak[4 * q + 1] : 0.f,
+                                s0 + 2 < t ? be * g2 * ak[4 * q + 2] : 0.f, s0 + 3 < t ? be * g3 * ak[4 * q + 3] : 0.f);
+            }
+        }
+    };
     // diagonal 16x16 blocks of T = (I + A)^{-1} by forward substitution, one lane
     // per column of each block (one wave), written over A's diagonal blocks
     auto diag_inverse = [&]() {
@@ -315,8 +365,12 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         scan(0);
         __syncthreads();
         if (nchunks > 1) prefetch(1);
-        if (wave < NW / 2) score_tiles(0, true, 0, NW / 2);
-        else score_tiles(0, false, NW / 2, NW - NW / 2);
+        if constexpr (S32) {
+            if (wave < NJ32) score_job32(0, wave);
+        } else {
+            if (wave < NW / 2) score_tiles(0, true, 0, NW / 2);
+            else score_tiles(0, false, NW / 2, NW - NW / 2);
+        }
         __syncthreads();
         if (wave == 0) diag_inverse();
         __syncthreads();
@@ -336,7 +390,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         const bool has_next = c + 1 < nchunks;
 
         // step 1: state waves K S0^T, Q S0^T and the solve's right-hand side of chunk c;
-        // helpers: the K K^T tiles of chunk c+1
+        // helpers: the scores of chunk c+1 (only its K K^T tiles for 16x16 tiles)
         G4 yb[NB];
         f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
         if (state_wave) {
@@ -380,12 +434,17 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             // the previous chunk's outputs leave now, so that these stores have
             // drained before the helpers next wait on their memory counter
             if (c > 0) copy_out(c - 1);
-            if (has_next) score_tiles(nxt, true, WS, NHW);
+            if constexpr (S32) {
+                if (has_next && hw < NJ32) score_job32(nxt, hw);
+            } else {
+                if (has_next) score_tiles(nxt, true, WS, NHW);
+            }
         }
         __syncthreads();
 
         // step 2: state waves U = T Y and the outputs of chunk c; first helper: the
-        // diagonal blocks of chunk c+1's inverse; other helpers: its Q K^T tiles
+        // diagonal blocks of chunk c+1's inverse; with 16x16 tiles, other helpers:
+        // its Q K^T tiles
         G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
         float decay = 1.f;
         if (state_wave) {
@@ -411,7 +470,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             }
         } else if (has_next) {
             if (hw == 0) diag_inverse();
-            else score_tiles(nxt, false, WS + 1, NHW - 1);
+            else if constexpr (!S32) score_tiles(nxt, false, WS + 1, NHW - 1);
         }
         __syncthreads();
 

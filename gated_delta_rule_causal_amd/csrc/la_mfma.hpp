@@ -59,6 +59,17 @@ template <> struct Group<bf16_t> {
 
 // ---- matrix-core steps
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 32x32 tile step in the natural operand layouts: lane l supplies
+// A[l%32][8*(l/32) .. +7] and B[8*(l/32) .. +7][l%32] (eight consecutive k,
+// one 16-byte register quad each); acc[r] is C[8*(r/4) + 4*(l/32) + r%4][l%32].
+// Its accumulators are never mixed with the 16x16 steps.
+__device__ __forceinline__ void mma32x32(f32x16 &acc, const uint4 &a, const uint4 &b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  acc, 0, 0, 0);
+}
+
 // acc += A(16 x 16) B(16 x 16), one group per lane.
 __device__ __forceinline__ void mma16(f32x4 &acc, const float4 &a, const float4 &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc, 0, 0, 0);
