@@ -30,9 +30,9 @@
 
 namespace la {
 
-// LDS bytes of one workgroup of gdr_chunk_kernel<DT, DK, DVB, C>: two sets of
-// chunk tiles (Q, K, V, P, T, gate values) plus the float32 solve tile and the
-// output staging tile.
+// LDS bytes of one workgroup of gdr_chunk_kernel<DT, DK, DVB, C>: Q, V, P and
+// the gate values of two chunks, K of three, one inverse T, the float32 solve
+// tile and the output staging tile.
 // Layout of the Q and K tiles in LDS.  Two access patterns read them: row
 // reads (16 rows x 16 bytes per half wave, the matrix-core A/B operands) and,
 // for bfloat16 K, transposing reads (8 consecutive rows x 32 bytes per half
@@ -62,8 +62,8 @@ template <class DT, int DK, int DVB, int C>
 constexpr int gdr_lds_bytes() {
     typedef typename OpOf<DT>::type Op;
     constexpr int PAD = 16 / sizeof(Op);
-    return 2 * (2 * C * (DK + gdr_kpad<Op>()) + 2 * C * (C + PAD) + C * (DVB + PAD)) * (int)sizeof(Op) +
-           C * (DVB + PAD) * (int)sizeof(Op) + C * (C + 4) * 4 + 2 * (4 * C + 1) * 4;
+    return (5 * C * (DK + gdr_kpad<Op>()) + 3 * C * (C + PAD) + 3 * C * (DVB + PAD)) * (int)sizeof(Op) +
+           C * (C + 4) * 4 + 2 * (4 * C + 1) * 4;
 }
 
 // A-operand group of K^T for key channel c = c0 + lane%16 and tokens
@@ -113,10 +113,10 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     static_assert(gdr_lds_bytes<DT, DK, DVB, C>() <= 160 * 1024, "LDS budget");
 
     __shared__ __align__(16) Op sQ[2][C * LDK];
-    __shared__ __align__(16) Op sK[2][C * LDK];
+    __shared__ __align__(16) Op sK[3][C * LDK];    // chunk c in buffer c % 3
     __shared__ __align__(16) Op sV[2][C * LDV];    // this block's value channels
     __shared__ __align__(16) Op sP[2][C * LDC];    // M o Gamma o Q K^T
-    __shared__ __align__(16) Op sT[2][C * LDC];    // (I + A)^{-1}
+    __shared__ __align__(16) Op sT[C * LDC];       // (I + A)^{-1}: chunk c+1's replaces chunk c's in step 3
     __shared__ __align__(16) Op sO[C * LDV];       // output tile, staged for 16-byte stores
     __shared__ __align__(16) float sA[C * LDA];    // A, then the blocks of T, in float32 during the solve
     __shared__ __align__(16) float sB[2][C], sEB[2][C], sBeta[2][C], sEBC[2][C];
@@ -177,9 +177,9 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         }
     };
     // registers -> buffer `buf`
-    auto commit = [&](int buf) {
+    auto commit = [&](int buf, int kbuf) {
         pq.template store<KSW>(sQ[buf], LDK, tid);
-        pk.template store<KSW>(sK[buf], LDK, tid);
+        pk.template store<KSW>(sK[kbuf], LDK, tid);
         pv.store(sV[buf], LDV, tid);
     };
     // SCAN_WAVE: cumulative log-gates of the staged chunk into buffer `buf`
@@ -200,8 +200,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // isK: A = diag(beta) (Gamma o K K^T), strictly lower, in float32 for the
     // inverse; else P = M o Gamma o Q K^T in the operand type.  Tiles above the
     // block diagonal are never read (the products below stop at the diagonal).
-    auto score_tiles = [&](int buf, bool isK, int w0, int nw) {
-        const Op *X = isK ? sK[buf] : sQ[buf], *K = sK[buf];
+    auto score_tiles = [&](int buf, int kbuf, bool isK, int w0, int nw) {
+        const Op *X = isK ? sK[kbuf] : sQ[buf], *K = sK[kbuf];
         const float *bb = sB[buf], *beta = sBeta[buf];
         Op *P = sP[buf];
         for (int tt = wave - w0; tt < NLOW; tt += nw) {
@@ -234,15 +234,15 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // pass over the key channels (K_J is the shared A operand and, on the
     // diagonal, also the B operand of K K^T); each lane then holds sixteen
     // columns s of one row t, written four at a time.
-    auto score_job32 = [&](int buf, int job) {
+    auto score_job32 = [&](int buf, int kbuf, int job) {
         if constexpr (S32) {
             int I = 0;
             while ((I + 1) * (I + 2) / 2 <= job) ++I;
             const int J = job - I * (I + 1) / 2;
             const int r = lane & 31, h = lane >> 5;
             const int off = r * LDK + swap_col(r, 8 * h, KSW);
-            const Op *aJ = sK[buf] + 32 * J * LDK + off;
-            const Op *bQ = sQ[buf] + 32 * I * LDK + off, *bK = sK[buf] + 32 * I * LDK + off;
+            const Op *aJ = sK[kbuf] + 32 * J * LDK + off;
+            const Op *bQ = sQ[buf] + 32 * I * LDK + off, *bK = sK[kbuf] + 32 * I * LDK + off;
             f32x16 ap = {}, ak = {};
             if (I == J) {
 #pragma unroll
@@ -276,43 +276,35 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             }
         }
     };
-    // diagonal 16x16 blocks of T = (I + A)^{-1} by forward substitution, one lane
-    // per column of each block (one wave), written over A's diagonal blocks
-    auto diag_inverse = [&]() {
-        if (lane >= 16 * NB) return;
-        const int blk = lane >> 4, nn = lane & 15;
+    // diagonal 16x16 block `blk` of T = (I + A)^{-1} by forward substitution,
+    // written over A's block.  One wave per block: lane 4n + p owns rows
+    // 4p..4p+3 of column n, so each step's row-times-column product is four
+    // multiply-adds and a sum over the lane quad (two DPP adds).
+    auto diag_block = [&](int blk) {
+        const int n = lane >> 2, pp = lane & 3;
         float *Ab = sA + 16 * blk * LDA + 16 * blk;
-        float x[16];
+        float x[4];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) x[m] = m == nn ? 1.f : 0.f;
-        float4 row[4], nxt[4];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) row[q4] = *reinterpret_cast<const float4 *>(Ab + 1 * LDA + 4 * q4);
+        for (int i = 0; i < 4; ++i) x[i] = 4 * pp + i == n ? 1.f : 0.f;
+        float4 row = *reinterpret_cast<const float4 *>(Ab + 1 * LDA + 4 * pp), nxt4;
 #pragma unroll
         for (int t = 1; t < 16; ++t) {
-            if (t + 1 < 16) {
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) nxt[q4] = *reinterpret_cast<const float4 *>(Ab + (t + 1) * LDA + 4 * q4);
-            }
-            float a[16];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                a[4 * q4] = row[q4].x; a[4 * q4 + 1] = row[q4].y; a[4 * q4 + 2] = row[q4].z; a[4 * q4 + 3] = row[q4].w;
-            }
-            float s4[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: shorter dependency chains
-#pragma unroll
-            for (int m = 0; m < t; ++m) s4[m & 3] += a[m] * x[m];
-            if (t > nn) x[t] = -((s4[0] + s4[1]) + (s4[2] + s4[3]));
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) row[q4] = nxt[q4];
+            if (t + 1 < 16) nxt4 = *reinterpret_cast<const float4 *>(Ab + (t + 1) * LDA + 4 * pp);
+            // A's diagonal and upper part are zero, so the not yet computed
+            // entries (zero) and x[n] = 1 above row t add nothing
+            float part = (row.x * x[0] + row.y * x[1]) + (row.z * x[2] + row.w * x[3]);
+            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0xB1, 0xF, 0xF, true));  // lanes ^1
+            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x4E, 0xF, 0xF, true));  // lanes ^2
+            if (pp == (t >> 2) && t > n) x[t & 3] = -part;
+            row = nxt4;
         }
 #pragma unroll
-        for (int t = 0; t < 16; ++t) Ab[t * LDA + nn] = x[t];
+        for (int i = 0; i < 4; ++i) Ab[(4 * pp + i) * LDA + n] = x[i];
     };
     // off-diagonal blocks of T into buffer `buf`, one block column per helper wave:
     // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj (matrix cores in the operand type)
-    auto offdiag = [&](int buf, int w0, int nw) {
-        Op *Tt = sT[buf];
+    auto offdiag = [&](int w0, int nw) {
+        Op *Tt = sT;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
             if (j % nw != wave - w0) continue;
@@ -361,23 +353,23 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // ---------------------------------------------------------------- prologue
     if (nchunks > 0) {
         prefetch(0);
-        commit(0);
+        commit(0, 0);
         scan(0);
         __syncthreads();
         if (nchunks > 1) prefetch(1);
         if constexpr (S32) {
-            if (wave < NJ32) score_job32(0, wave);
+            if (wave < NJ32) score_job32(0, 0, wave);
         } else {
-            if (wave < NW / 2) score_tiles(0, true, 0, NW / 2);
-            else score_tiles(0, false, NW / 2, NW - NW / 2);
+            if (wave < NW / 2) score_tiles(0, 0, true, 0, NW / 2);
+            else score_tiles(0, 0, false, NW / 2, NW - NW / 2);
         }
         __syncthreads();
-        if (wave == 0) diag_inverse();
+        if (wave < NB) diag_block(wave);
         __syncthreads();
-        offdiag(0, 0, NW);
+        offdiag(0, NW);
         __syncthreads();
         if (nchunks > 1) {
-            commit(1);
+            commit(1, 1);
             scan(1);
             __syncthreads();
             if (nchunks > 2) prefetch(2);
@@ -387,6 +379,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // ---------------------------------------------------------------- chunk loop
     for (int c = 0; c < nchunks; ++c) {
         const int cur = c & 1, nxt = cur ^ 1;
+        const int kc = c % 3, kn = kc == 2 ? 0 : kc + 1, knn = kn == 2 ? 0 : kn + 1;   // K buffers of c, c+1, c+2
         const bool has_next = c + 1 < nchunks;
 
         // step 1: state waves K S0^T, Q S0^T and the solve's right-hand side of chunk c;
@@ -405,7 +398,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
-                    const Op *kr = sK[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
+                    const Op *kr = sK[kc] + (16 * I + lr) * LDK + ko + 16 * s2;
                     const Op *qr = sQ[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
                     mma32(ks[I], ld_group(kr), ld_group(kr + 16), sb[s2], sb[s2 + 1]);
                     mma32(qs[I], sb[s2], sb[s2 + 1], ld_group(qr), ld_group(qr + 16));
@@ -414,7 +407,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             if constexpr (NCB % 2 == 1) {
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
-                    mma16(ks[I], ld_group(sK[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
+                    mma16(ks[I], ld_group(sK[kc] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
                     mma16(qs[I], sb[NCB - 1], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)));
                 }
             }
@@ -435,16 +428,16 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             // drained before the helpers next wait on their memory counter
             if (c > 0) copy_out(c - 1);
             if constexpr (S32) {
-                if (has_next && hw < NJ32) score_job32(nxt, hw);
+                if (has_next && hw < NJ32) score_job32(nxt, kn, hw);
             } else {
-                if (has_next) score_tiles(nxt, true, WS, NHW);
+                if (has_next) score_tiles(nxt, kn, true, WS, NHW);
             }
         }
         __syncthreads();
 
-        // step 2: state waves U = T Y and the outputs of chunk c; first helper: the
-        // diagonal blocks of chunk c+1's inverse; with 16x16 tiles, other helpers:
-        // its Q K^T tiles
+        // step 2: state waves U = T Y and the outputs of chunk c; one helper per
+        // diagonal block of chunk c+1's inverse; with 16x16 tiles, the other
+        // helpers: its Q K^T tiles
         G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
         float decay = 1.f;
         if (state_wave) {
@@ -453,7 +446,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
                 f32x4 u = zero4();
-                tile_mma_lr_n<NB>(u, sT[cur] + 16 * I * LDC, LDC, yb, I + 1, lane);
+                tile_mma_lr_n<NB>(u, sT + 16 * I * LDC, LDC, yb, I + 1, lane);
                 ub[I] = Gp::make(u);
                 const float4 ec = *reinterpret_cast<const float4 *>(&sEBC[cur][16 * I + 4 * lg]);
                 usb[I] = Gp::make(u[0] * ec.x, u[1] * ec.y, u[2] * ec.z, u[3] * ec.w);
@@ -469,13 +462,13 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                                   o[3] + eb * qs[I][3]));
             }
         } else if (has_next) {
-            if (hw == 0) diag_inverse();
-            else if constexpr (!S32) score_tiles(nxt, false, WS + 1, NHW - 1);
+            if (hw < NB) diag_block(hw);
+            else if constexpr (!S32) score_tiles(nxt, kn, false, WS + NB, NHW - NB);
         }
         __syncthreads();
 
         // step 3: state waves S <- e^{b_C} S + K^T (U e^{b_C - b}); helpers: the
-        // off-diagonal inverse of chunk c+1 and the output rows of chunk c
+        // off-diagonal inverse of chunk c+1 (over chunk c's T, read in step 2)
         if (state_wave) {
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
@@ -483,24 +476,23 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 for (int i = 0; i < 4; ++i) st[cb][i] *= decay;
 #pragma unroll
                 for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
-                    mma32(st[cb], kt_group(sK[cur], LDK, 16 * s2, 16 * cb, lane),
-                          kt_group(sK[cur], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
-                if constexpr (NB % 2 == 1) mma16(st[cb], kt_group(sK[cur], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
+                    mma32(st[cb], kt_group(sK[kc], LDK, 16 * s2, 16 * cb, lane),
+                          kt_group(sK[kc], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
+                if constexpr (NB % 2 == 1) mma16(st[cb], kt_group(sK[kc], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
             }
         } else {
-            if (has_next) offdiag(nxt, WS, NHW);
+            if (has_next) offdiag(WS, NHW);
             // chunk c+2's gate values (held by SCAN_WAVE) -> gate buffer cur, whose
             // chunk-c values the state waves no longer read
             if (c + 2 < nchunks) scan(cur);
         }
-        __syncthreads();
-
-        // step 4: chunk c+2's tiles into the buffers chunk c has released
+        // everyone: chunk c+2's tiles into buffers no step reads any more (Q and V
+        // of chunk c, K of chunk c-1), then the loads of chunk c+3
         if (c + 2 < nchunks) {
-            commit(cur);
-            __syncthreads();
+            commit(cur, knn);
             if (c + 3 < nchunks) prefetch(c + 3);
         }
+        __syncthreads();
     }
 
     if (nchunks > 0 && !state_wave) copy_out(nchunks - 1);
