@@ -33,9 +33,12 @@ __device__ __forceinline__ void stage_rows(E *dst, int ldd, const E *src, size_t
 }
 
 // Register staging of an R x D row-major tile: load() issues every 16-byte
-// global read of the tile at once (rows >= n read as zero), store() writes
-// the registers to LDS.  Issued one chunk ahead, the reads complete while
-// the current chunk computes; the workgroup barriers only wait for LDS.
+// global read of the tile at once, store() writes the registers to LDS with
+// rows >= n as zeros.  Issued one chunk ahead, the reads complete while the
+// current chunk computes; the workgroup barriers only wait for LDS.  Rows
+// beyond n read row 0 instead (always valid) and the zeroing happens at
+// store time: no register of a load in flight is written by another
+// instruction, which would make the compiler wait for every outstanding load.
 template <int R, int D, int NTHR, class E>
 struct TilePrefetch {
     static constexpr int VE = 16 / sizeof(E);
@@ -43,16 +46,20 @@ struct TilePrefetch {
     static constexpr int TOTAL = R * VPR;
     static constexpr int PER = (TOTAL + NTHR - 1) / NTHR;
     static_assert(D % VE == 0, "row width");
+    static_assert(PER <= 32, "row-valid mask");
     uint4 r[PER];
+    uint32_t valid;   // bit i: r[i] holds a row < n
 
     __device__ __forceinline__ void load(const E *src, size_t lds, int n, int tid) {
+        valid = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = tid + i * NTHR;
             const int row = e / VPR, col = (e % VPR) * VE;
-            r[i] = make_uint4(0u, 0u, 0u, 0u);
-            if ((TOTAL % NTHR == 0 || e < TOTAL) && row < n)
-                r[i] = *reinterpret_cast<const uint4 *>(src + row * lds + col);
+            if (TOTAL % NTHR == 0 || e < TOTAL) {
+                r[i] = *reinterpret_cast<const uint4 *>(src + (row < n ? row : 0) * lds + col);
+                valid |= (row < n ? 1u : 0u) << i;
+            }
         }
     }
     // SW != 0: on rows with bit 3 set, element column c goes to c ^ SW
@@ -63,7 +70,8 @@ struct TilePrefetch {
             const int e = tid + i * NTHR;
             const int row = e / VPR, col = (e % VPR) * VE;
             if (TOTAL % NTHR == 0 || e < TOTAL)
-                *reinterpret_cast<uint4 *>(dst + row * ldd + (col ^ (SW * ((row >> 3) & 1)))) = r[i];
+                *reinterpret_cast<uint4 *>(dst + row * ldd + (col ^ (SW * ((row >> 3) & 1)))) =
+                    (valid >> i) & 1u ? r[i] : make_uint4(0u, 0u, 0u, 0u);
         }
     }
 };

@@ -30,9 +30,10 @@
 
 namespace la {
 
-// LDS bytes of one workgroup of gdr_chunk_kernel<DT, DK, DVB, C>: Q, V, P and
-// the gate values of two chunks, K of three, one inverse T, the float32 solve
-// tile and the output staging tile.
+// LDS bytes of one workgroup of gdr_chunk_kernel<DT, DK, DVB, C>: Q, P and the
+// gate values of two chunks, K of three, V and the inverse T of one, the
+// float32 solve tile, and either the output staging tile or the published
+// state and U^T.
 // Layout of the Q and K tiles in LDS.  Two access patterns read them: row
 // reads (16 rows x 16 bytes per half wave, the matrix-core A/B operands) and,
 // for bfloat16 K, transposing reads (8 consecutive rows x 32 bytes per half
@@ -58,11 +59,19 @@ __device__ __forceinline__ void tile_mma_qk(f32x4 &acc, const Op *x, const Op *y
     if constexpr (K % 32 == 16) mma16(acc, ld_group(xr + K - 16), ld_group(yr + K - 16));
 }
 
+// With bfloat16, 32- or 64-token chunks and 32-channel value blocks the
+// outputs Q S0^T and P U are formed by helper waves from copies of the state
+// and of U^T that the state waves publish in LDS (instead of an output tile).
+template <class Op, int DVB, int C>
+constexpr bool gdr_helper_outputs() { return sizeof(Op) == 2 && C % 32 == 0 && DVB == 32; }
+
 template <class DT, int DK, int DVB, int C>
 constexpr int gdr_lds_bytes() {
     typedef typename OpOf<DT>::type Op;
     constexpr int PAD = 16 / sizeof(Op);
-    return (5 * C * (DK + gdr_kpad<Op>()) + 3 * C * (C + PAD) + 3 * C * (DVB + PAD)) * (int)sizeof(Op) +
+    constexpr int tail = gdr_helper_outputs<Op, DVB, C>() ? DVB * (DK + gdr_kpad<Op>()) + DVB * (C + PAD)
+                                                          : C * (DVB + PAD);
+    return (5 * C * (DK + gdr_kpad<Op>()) + 3 * C * (C + PAD) + C * (DVB + PAD) + tail) * (int)sizeof(Op) +
            C * (C + 4) * 4 + 2 * (4 * C + 1) * 4;
 }
 
@@ -107,17 +116,24 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     constexpr int VE = 16 / sizeof(Op);
     constexpr int NLOW = NB * (NB + 1) / 2;
     constexpr bool S32 = sizeof(Op) == 2 && C % 32 == 0;   // scores in 32x32 jobs
-    constexpr int NJ32 = (C / 32) * (C / 32 + 1) / 2;
+    constexpr int NJ32 = (C / 32) * (C / 32 + 1);   // score jobs: two per 32-block pair
     static_assert(!S32 || NJ32 <= NHW, "one helper wave per score job");
+    constexpr bool HO = gdr_helper_outputs<Op, DVB, C>();   // outputs on helper waves
+    constexpr int NJO = C / 32;                     // output jobs of 32 tokens (HO)
+    constexpr int OJ0 = NHW - NJO;                  // helper index of the first output job
+    constexpr int LDU = C + PAD;
+    static_assert(!HO || OJ0 >= NB, "output jobs need helpers of their own in step 2");
     static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && NHW >= 1, "tiling");
     static_assert(gdr_lds_bytes<DT, DK, DVB, C>() <= 160 * 1024, "LDS budget");
 
     __shared__ __align__(16) Op sQ[2][C * LDK];
     __shared__ __align__(16) Op sK[3][C * LDK];    // chunk c in buffer c % 3
-    __shared__ __align__(16) Op sV[2][C * LDV];    // this block's value channels
+    __shared__ __align__(16) Op sV[C * LDV];       // this block's value channels of chunk c (read in step 1)
     __shared__ __align__(16) Op sP[2][C * LDC];    // M o Gamma o Q K^T
     __shared__ __align__(16) Op sT[C * LDC];       // (I + A)^{-1}: chunk c+1's replaces chunk c's in step 3
-    __shared__ __align__(16) Op sO[C * LDV];       // output tile, staged for 16-byte stores
+    __shared__ __align__(16) Op sO[HO ? VE : C * LDV];     // output tile, staged for 16-byte stores
+    __shared__ __align__(16) Op sS0[HO ? DVB * LDK : VE];  // entering state, rows = values (Q/K layout)
+    __shared__ __align__(16) Op sUT[HO ? DVB * LDU : VE];  // U^T, rows = values
     __shared__ __align__(16) float sA[C * LDA];    // A, then the blocks of T, in float32 during the solve
     __shared__ __align__(16) float sB[2][C], sEB[2][C], sBeta[2][C], sEBC[2][C];
     __shared__ float sDecay[2];
@@ -159,39 +175,42 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // ---------------------------------------------------------------- stages
+    // All waves stage the tiles, in step 3: register prefetch one chunk ahead,
+    // then LDS (Q, K and the gate values two chunks ahead, V one chunk ahead).
     TilePrefetch<C, DK, NTHR, IO> pq, pk;
     TilePrefetch<C, DVB, NTHR, IO> pv;
     // the gate scan runs on the last wave, which has no block column of the
     // off-diagonal inverse to work on
     constexpr int SCAN_WAVE = NW - 1;
     static_assert(NHW >= NB + 1 || NB == 1, "a helper wave must be free for the gate scan");
-    float pg = 1.f, pb = 0.f;   // SCAN_WAVE, lane t: gate and beta of token t (padding: g = 1, beta = 0)
-    auto prefetch = [&](int c) {
-        const int c0 = c * C, n = min(C, p.T - c0);
+    // SCAN_WAVE, lane t: gate and beta of token t of the staged chunk (lanes past
+    // its end read token 0; the scan treats them as g = 1, beta = 0)
+    float pg = 1.f, pb = 0.f;
+    auto rows = [&](int c) { return min(C, p.T - c * C); };
+    auto load_q = [&](int c) {
+        const int c0 = c * C, n = rows(c);
         pq.load(qh + static_cast<size_t>(c0) * DK, DK, n, tid);
-        pk.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
-        pv.load(vh + static_cast<size_t>(c0) * p.d_v, p.d_v, n, tid);
         if (wave == SCAN_WAVE) {
-            pg = lane < n ? gh[c0 + lane] : 1.f;
-            pb = lane < n ? bth[c0 + lane] : 0.f;
+            pg = gh[c0 + (lane < n ? lane : 0)];
+            pb = bth[c0 + (lane < n ? lane : 0)];
         }
     };
-    // registers -> buffer `buf`
-    auto commit = [&](int buf, int kbuf) {
-        pq.template store<KSW>(sQ[buf], LDK, tid);
-        pk.template store<KSW>(sK[kbuf], LDK, tid);
-        pv.store(sV[buf], LDV, tid);
-    };
-    // SCAN_WAVE: cumulative log-gates of the staged chunk into buffer `buf`
-    auto scan = [&](int buf) {
+    auto load_k = [&](int c) { pk.load(kh + static_cast<size_t>(c * C) * DK, DK, rows(c), tid); };
+    auto load_v = [&](int c) { pv.load(vh + static_cast<size_t>(c * C) * p.d_v, p.d_v, rows(c), tid); };
+    auto store_q = [&](int buf) { pq.template store<KSW>(sQ[buf], LDK, tid); };
+    auto store_k = [&](int kbuf) { pk.template store<KSW>(sK[kbuf], LDK, tid); };
+    auto store_v = [&]() { pv.store(sV, LDV, tid); };
+    // SCAN_WAVE: cumulative log-gates of the staged chunk c into buffer `buf`
+    auto scan = [&](int buf, int c) {
         if (wave == SCAN_WAVE) {
-            const float b = wave_inclusive_sum(__logf(pg), lane);
+            const bool in = lane < min(C, p.T - c * C);
+            const float b = wave_inclusive_sum(in ? __logf(pg) : 0.f, lane);
             const float bC = __shfl(b, C - 1, 64);
             if (lane < C) {
                 sB[buf][lane] = b;
                 sEB[buf][lane] = __expf(b);
                 sEBC[buf][lane] = __expf(bC - b);
-                sBeta[buf][lane] = pb;
+                sBeta[buf][lane] = in ? pb : 0.f;
             }
             if (lane == 0) sDecay[buf] = __expf(bC);
         }
@@ -229,35 +248,33 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             }
         }
     };
-    // bfloat16 chunks of 32 or 64 tokens: the scores in 32x32 jobs.  Job
-    // (I, J), I >= J over 32-token blocks, forms K_J Q_I^T and K_J K_I^T in one
-    // pass over the key channels (K_J is the shared A operand and, on the
-    // diagonal, also the B operand of K K^T); each lane then holds sixteen
-    // columns s of one row t, written four at a time.
+    // bfloat16 chunks of 32 or 64 tokens: the scores in 32x32 jobs.  Job j
+    // covers the 32-token block pair (I, J), I >= J, given by j / 2 and forms
+    // K_J Q_I^T (j even: P) or K_J K_I^T (j odd: A; on the diagonal K_J is
+    // both operands); each lane then holds sixteen columns s of one row t,
+    // written four at a time.
     auto score_job32 = [&](int buf, int kbuf, int job) {
         if constexpr (S32) {
+            const int pair = job >> 1;
+            const bool isK = job & 1;
             int I = 0;
-            while ((I + 1) * (I + 2) / 2 <= job) ++I;
-            const int J = job - I * (I + 1) / 2;
+            while ((I + 1) * (I + 2) / 2 <= pair) ++I;
+            const int J = pair - I * (I + 1) / 2;
             const int r = lane & 31, h = lane >> 5;
             const int off = r * LDK + swap_col(r, 8 * h, KSW);
             const Op *aJ = sK[kbuf] + 32 * J * LDK + off;
-            const Op *bQ = sQ[buf] + 32 * I * LDK + off, *bK = sK[kbuf] + 32 * I * LDK + off;
-            f32x16 ap = {}, ak = {};
-            if (I == J) {
+            const Op *bX = (isK ? sK[kbuf] : sQ[buf]) + 32 * I * LDK + off;
+            f32x16 acc = {};
+            if (isK && I == J) {
 #pragma unroll
                 for (int kk = 0; kk < DK / 16; ++kk) {
                     const uint4 a = *reinterpret_cast<const uint4 *>(aJ + 16 * kk);
-                    mma32x32(ap, a, *reinterpret_cast<const uint4 *>(bQ + 16 * kk));
-                    mma32x32(ak, a, a);
+                    mma32x32(acc, a, a);
                 }
             } else {
 #pragma unroll
-                for (int kk = 0; kk < DK / 16; ++kk) {
-                    const uint4 a = *reinterpret_cast<const uint4 *>(aJ + 16 * kk);
-                    mma32x32(ap, a, *reinterpret_cast<const uint4 *>(bQ + 16 * kk));
-                    mma32x32(ak, a, *reinterpret_cast<const uint4 *>(bK + 16 * kk));
-                }
+                for (int kk = 0; kk < DK / 16; ++kk)
+                    mma32x32(acc, *reinterpret_cast<const uint4 *>(aJ + 16 * kk), *reinterpret_cast<const uint4 *>(bX + 16 * kk));
             }
             const int t = 32 * I + r;
             const float bt = sB[buf][t], be = sBeta[buf][t];
@@ -267,12 +284,14 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 const float4 bs = *reinterpret_cast<const float4 *>(sB[buf] + s0);
                 const float g0 = __expf(fminf(bt - bs.x, 0.f)), g1 = __expf(fminf(bt - bs.y, 0.f));
                 const float g2 = __expf(fminf(bt - bs.z, 0.f)), g3 = __expf(fminf(bt - bs.w, 0.f));
-                st_group(sP[buf] + t * LDC + s0,
-                         Gp::make(s0 <= t ? g0 * ap[4 * q] : 0.f, s0 + 1 <= t ? g1 * ap[4 * q + 1] : 0.f,
-                                  s0 + 2 <= t ? g2 * ap[4 * q + 2] : 0.f, s0 + 3 <= t ? g3 * ap[4 * q + 3] : 0.f));
-                *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
-                    make_float4(s0 < t ? be * g0 * ak[4 * q] : 0.f, s0 + 1 < t ? be * g1 * ak[4 * q + 1] : 0.f,
-                                s0 + 2 < t ? be * g2 * ak[4 * q + 2] : 0.f, s0 + 3 < t ? be * g3 * ak[4 * q + 3] : 0.f);
+                if (isK)
+                    *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
+                        make_float4(s0 < t ? be * g0 * acc[4 * q] : 0.f, s0 + 1 < t ? be * g1 * acc[4 * q + 1] : 0.f,
+                                    s0 + 2 < t ? be * g2 * acc[4 * q + 2] : 0.f, s0 + 3 < t ? be * g3 * acc[4 * q + 3] : 0.f);
+                else
+                    st_group(sP[buf] + t * LDC + s0,
+                             Gp::make(s0 <= t ? g0 * acc[4 * q] : 0.f, s0 + 1 <= t ? g1 * acc[4 * q + 1] : 0.f,
+                                      s0 + 2 <= t ? g2 * acc[4 * q + 2] : 0.f, s0 + 3 <= t ? g3 * acc[4 * q + 3] : 0.f));
             }
         }
     };
@@ -324,11 +343,14 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     const float4 f = *reinterpret_cast<const float4 *>(ar + 16 * m);
                     return Gp::make(f.x, f.y, f.z, f.w);
                 };
+                // every index below is a compile-time constant once the loops are
+                // unrolled, so tb stays in registers
                 f32x4 acc = zero4();
-                int m = j;
 #pragma unroll
-                for (; m + 1 < i; m += 2) mma32(acc, agroup(m), agroup(m + 1), tb[m], tb[m + 1]);
-                if (m < i) mma16(acc, agroup(m), tb[m]);
+                for (int m = j; m < i; m += 2) {
+                    if (m + 1 < i) mma32(acc, agroup(m), agroup(m + 1), tb[m], tb[m + 1]);
+                    else mma16(acc, agroup(m), tb[m]);
+                }
                 f32x4 tij = zero4();
                 mma16(tij, agroup(i), Gp::make(acc));
 #pragma unroll
@@ -350,13 +372,82 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         }
     };
 
+    // HO: the state waves publish the entering state (bfloat16, rows = values)
+    auto publish_s0 = [&]() {
+        if constexpr (HO) {
+            const int v = 16 * wave + lr;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+                st_group(sS0 + v * LDK + swap_col(v, 16 * cb + 4 * lg, KSW), Gp::make(st[cb]));
+        }
+    };
+    // HO, step 2: S0 Q_I^T for the 32 tokens of output job I (lane: token
+    // 32 I + lane%32, values 8q + 4(lane/32) + i in acc[4q + i]) and e^{b_t}
+    auto qs_job = [&](int cur, int I, f32x16 &acc, float &ebt) {
+        if constexpr (HO) {
+            const int r = lane & 31, h = lane >> 5;
+            const int off = r * LDK + swap_col(r, 8 * h, KSW);
+            const Op *a = sS0 + off, *b = sQ[cur] + 32 * I * LDK + off;
+            acc = f32x16{};
+#pragma unroll
+            for (int kk = 0; kk < DK / 16; ++kk)
+                mma32x32(acc, *reinterpret_cast<const uint4 *>(a + 16 * kk), *reinterpret_cast<const uint4 *>(b + 16 * kk));
+            ebt = sEB[cur][32 * I + r];
+        }
+    };
+    // HO, step 3: O^T = U^T P_I^T + S0 Q_I^T diag(e^b) for job I, straight to
+    // global memory (four values of one token per store)
+    auto out_job = [&](int c, int cur, int I, const f32x16 &qs, float ebt) {
+        if constexpr (HO) {
+            const int r = lane & 31, h = lane >> 5;
+            const Op *a = sUT + r * LDU + 8 * h, *b = sP[cur] + (32 * I + r) * LDC + 8 * h;
+            f32x16 acc = {};
+#pragma unroll
+            for (int kk = 0; kk < 2 * NJO; ++kk)
+                if (kk < 2 * (I + 1))
+                    mma32x32(acc, *reinterpret_cast<const uint4 *>(a + 16 * kk), *reinterpret_cast<const uint4 *>(b + 16 * kk));
+            const int t = c * C + 32 * I + r;
+            if (t < p.T) {
+                IO *orow = oh + static_cast<size_t>(t) * p.d_v + vb * DVB + 4 * h;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    st_group(orow + 8 * q, Gp::make(acc[4 * q] + ebt * qs[4 * q], acc[4 * q + 1] + ebt * qs[4 * q + 1],
+                                                    acc[4 * q + 2] + ebt * qs[4 * q + 2], acc[4 * q + 3] + ebt * qs[4 * q + 3]));
+            }
+        }
+    };
+
     // ---------------------------------------------------------------- prologue
+    // staging: everyone; chunk 0's tiles and gates, then chunk 0's scores and
+    // inverse, chunk 1's Q, K and gates; the registers then hold V(1), Q(2), K(2)
+    auto stage = [&](int c) {
+        if (c + 1 < nchunks) store_v();
+        if (c + 2 < nchunks) {
+            store_q(c & 1);
+            store_k((c + 2) % 3);
+            scan(c & 1, c + 2);
+            load_v(c + 2);
+        }
+        if (c + 3 < nchunks) {
+            load_q(c + 3);
+            load_k(c + 3);
+        }
+    };
     if (nchunks > 0) {
-        prefetch(0);
-        commit(0, 0);
-        scan(0);
+        load_q(0);
+        load_k(0);
+        load_v(0);
+        store_q(0);
+        store_k(0);
+        store_v();
+        scan(0, 0);
+        if (state_wave) publish_s0();
         __syncthreads();
-        if (nchunks > 1) prefetch(1);
+        if (nchunks > 1) {
+            load_q(1);
+            load_k(1);
+            load_v(1);
+        }
         if constexpr (S32) {
             if (wave < NJ32) score_job32(0, 0, wave);
         } else {
@@ -369,133 +460,161 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         offdiag(0, NW);
         __syncthreads();
         if (nchunks > 1) {
-            commit(1, 1);
-            scan(1);
+            store_q(1);
+            store_k(1);
+            scan(1, 1);
             __syncthreads();
-            if (nchunks > 2) prefetch(2);
+            if (nchunks > 2) {
+                load_q(2);
+                load_k(2);
+            }
         }
     }
 
     // ---------------------------------------------------------------- chunk loop
-    for (int c = 0; c < nchunks; ++c) {
-        const int cur = c & 1, nxt = cur ^ 1;
-        const int kc = c % 3, kn = kc == 2 ? 0 : kc + 1, knn = kn == 2 ? 0 : kn + 1;   // K buffers of c, c+1, c+2
-        const bool has_next = c + 1 < nchunks;
+    // The two roles run loops of their own with the same three barriers per
+    // chunk, so that each role's registers are allocated for its own work.
+    if (state_wave) {
+        for (int c = 0; c < nchunks; ++c) {
+            const int cur = c & 1, kc = c % 3;
 
-        // step 1: state waves K S0^T, Q S0^T and the solve's right-hand side of chunk c;
-        // helpers: the scores of chunk c+1 (only its K K^T tiles for 16x16 tiles)
-        G4 yb[NB];
-        f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
-        if (state_wave) {
-            G4 sb[NCB];
+            // step 1: K S0^T, Q S0^T and the solve's right-hand side Y of chunk c
+            G4 yb[NB];
+            f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
+            {
+                G4 sb[NCB];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
-            f32x4 ks[NB];
+                for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
+                f32x4 ks[NB];
 #pragma unroll
-            for (int I = 0; I < NB; ++I) { ks[I] = zero4(); qs[I] = zero4(); }
-            const int ko = swap_col(lr, 4 * lg, KSW);   // rows 16 I + lr
+                for (int I = 0; I < NB; ++I) { ks[I] = zero4(); qs[I] = zero4(); }   // qs: unused with HO
+                const int ko = swap_col(lr, 4 * lg, KSW);   // rows 16 I + lr
 #pragma unroll
-            for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
+                for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        const Op *kr = sK[kc] + (16 * I + lr) * LDK + ko + 16 * s2;
+                        const Op *qr = sQ[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
+                        mma32(ks[I], ld_group(kr), ld_group(kr + 16), sb[s2], sb[s2 + 1]);
+                        if constexpr (!HO) mma32(qs[I], sb[s2], sb[s2 + 1], ld_group(qr), ld_group(qr + 16));
+                    }
+                }
+                if constexpr (NCB % 2 == 1) {
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        mma16(ks[I], ld_group(sK[kc] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
+                        if constexpr (!HO) mma16(qs[I], sb[NCB - 1], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)));
+                    }
+                }
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
-                    const Op *kr = sK[kc] + (16 * I + lr) * LDK + ko + 16 * s2;
-                    const Op *qr = sQ[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
-                    mma32(ks[I], ld_group(kr), ld_group(kr + 16), sb[s2], sb[s2 + 1]);
-                    mma32(qs[I], sb[s2], sb[s2 + 1], ld_group(qr), ld_group(qr + 16));
+                    const float4 be = *reinterpret_cast<const float4 *>(&sBeta[cur][16 * I + 4 * lg]);
+                    const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
+                    const Op *vr = sV + (16 * I + 4 * lg) * LDV + vloc;
+                    f32x4 y;
+                    y[0] = be.x * (to_f32(vr[0]) - eb.x * ks[I][0]);
+                    y[1] = be.y * (to_f32(vr[LDV]) - eb.y * ks[I][1]);
+                    y[2] = be.z * (to_f32(vr[2 * LDV]) - eb.z * ks[I][2]);
+                    y[3] = be.w * (to_f32(vr[3 * LDV]) - eb.w * ks[I][3]);
+                    yb[I] = Gp::make(y);
                 }
             }
-            if constexpr (NCB % 2 == 1) {
+            __syncthreads();
+
+            // step 2: U = T Y and (not HO) the outputs of chunk c
+            G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
+            float decay;
+            {
+                decay = sDecay[cur];
+                G4 ub[NB];
 #pragma unroll
                 for (int I = 0; I < NB; ++I) {
-                    mma16(ks[I], ld_group(sK[kc] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
-                    mma16(qs[I], sb[NCB - 1], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)));
+                    f32x4 u = zero4();
+                    tile_mma_lr_n<NB>(u, sT + 16 * I * LDC, LDC, yb, I + 1, lane);
+                    ub[I] = Gp::make(u);
+                    // HO: U^T for the output jobs (rows = values, four tokens per write)
+                    if constexpr (HO) st_group(sUT + vloc * LDU + 16 * I + 4 * lg, ub[I]);
+                    const float4 ec = *reinterpret_cast<const float4 *>(&sEBC[cur][16 * I + 4 * lg]);
+                    usb[I] = Gp::make(u[0] * ec.x, u[1] * ec.y, u[2] * ec.z, u[3] * ec.w);
+                }
+                if constexpr (!HO) {
+#pragma unroll
+                    for (int I = 0; I < NB; ++I) {
+                        // O^T = U^T P^T: lane holds values 16*wave + 4*lg..+3 of token 16 I + lr
+                        f32x4 o = zero4();
+                        tile_mma_rl_n<NB>(o, ub, sP[cur] + 16 * I * LDC, LDC, I + 1, lane);
+                        const float eb = sEB[cur][16 * I + lr];
+                        st_group(sO + (16 * I + lr) * LDV + 16 * wave + 4 * lg,
+                                 Gp::make(o[0] + eb * qs[I][0], o[1] + eb * qs[I][1], o[2] + eb * qs[I][2],
+                                          o[3] + eb * qs[I][3]));
+                    }
                 }
             }
+            __syncthreads();
+
+            // step 3: S <- e^{b_C} S + K^T (U e^{b_C - b})
+            {
 #pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                const float4 be = *reinterpret_cast<const float4 *>(&sBeta[cur][16 * I + 4 * lg]);
-                const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
-                const Op *vr = sV[cur] + (16 * I + 4 * lg) * LDV + vloc;
-                f32x4 y;
-                y[0] = be.x * (to_f32(vr[0]) - eb.x * ks[I][0]);
-                y[1] = be.y * (to_f32(vr[LDV]) - eb.y * ks[I][1]);
-                y[2] = be.z * (to_f32(vr[2 * LDV]) - eb.z * ks[I][2]);
-                y[3] = be.w * (to_f32(vr[3 * LDV]) - eb.w * ks[I][3]);
-                yb[I] = Gp::make(y);
+                for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[cb][i] *= decay;
+#pragma unroll
+                    for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
+                        mma32(st[cb], kt_group(sK[kc], LDK, 16 * s2, 16 * cb, lane),
+                              kt_group(sK[kc], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
+                    if constexpr (NB % 2 == 1) mma16(st[cb], kt_group(sK[kc], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
+                }
+                publish_s0();   // HO: entering state of chunk c+1
             }
-        } else {
-            // the previous chunk's outputs leave now, so that these stores have
-            // drained before the helpers next wait on their memory counter
-            if (c > 0) copy_out(c - 1);
+            stage(c);
+            __syncthreads();
+        }
+    } else {
+        f32x16 oqs = {};   // HO output jobs: S0 Q_I^T of the current chunk and e^{b_t}
+        float oeb = 0.f;
+        for (int c = 0; c < nchunks; ++c) {
+            const int cur = c & 1, nxt = cur ^ 1;
+            const int kn = (c + 1) % 3;   // K buffer of chunk c+1
+            const bool has_next = c + 1 < nchunks;
+
+            // step 1: the scores of chunk c+1 (only its K K^T tiles with 16x16
+            // tiles); without HO the staged outputs of chunk c-1 leave
+            if constexpr (!HO) {
+                if (c > 0) copy_out(c - 1);
+            }
             if constexpr (S32) {
                 if (has_next && hw < NJ32) score_job32(nxt, kn, hw);
             } else {
                 if (has_next) score_tiles(nxt, kn, true, WS, NHW);
             }
-        }
-        __syncthreads();
+            __syncthreads();
 
-        // step 2: state waves U = T Y and the outputs of chunk c; one helper per
-        // diagonal block of chunk c+1's inverse; with 16x16 tiles, the other
-        // helpers: its Q K^T tiles
-        G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
-        float decay = 1.f;
-        if (state_wave) {
-            decay = sDecay[cur];
-            G4 ub[NB];
-#pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                f32x4 u = zero4();
-                tile_mma_lr_n<NB>(u, sT + 16 * I * LDC, LDC, yb, I + 1, lane);
-                ub[I] = Gp::make(u);
-                const float4 ec = *reinterpret_cast<const float4 *>(&sEBC[cur][16 * I + 4 * lg]);
-                usb[I] = Gp::make(u[0] * ec.x, u[1] * ec.y, u[2] * ec.z, u[3] * ec.w);
+            // step 2: one wave per diagonal block of chunk c+1's inverse; with 16x16
+            // tiles, the other helpers: its Q K^T tiles; HO: S0 Q^T of chunk c
+            if (has_next) {
+                if (hw < NB) diag_block(hw);
+                else if constexpr (!S32) score_tiles(nxt, kn, false, WS + NB, NHW - NB);
             }
-#pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                // O^T = U^T P^T: lane holds values 16*wave + 4*lg..+3 of token 16 I + lr
-                f32x4 o = zero4();
-                tile_mma_rl_n<NB>(o, ub, sP[cur] + 16 * I * LDC, LDC, I + 1, lane);
-                const float eb = sEB[cur][16 * I + lr];
-                st_group(sO + (16 * I + lr) * LDV + 16 * wave + 4 * lg,
-                         Gp::make(o[0] + eb * qs[I][0], o[1] + eb * qs[I][1], o[2] + eb * qs[I][2],
-                                  o[3] + eb * qs[I][3]));
-            }
-        } else if (has_next) {
-            if (hw < NB) diag_block(hw);
-            else if constexpr (!S32) score_tiles(nxt, kn, false, WS + NB, NHW - NB);
-        }
-        __syncthreads();
+            if (HO && hw >= OJ0) qs_job(cur, hw - OJ0, oqs, oeb);
+            __syncthreads();
 
-        // step 3: state waves S <- e^{b_C} S + K^T (U e^{b_C - b}); helpers: the
-        // off-diagonal inverse of chunk c+1 (over chunk c's T, read in step 2)
-        if (state_wave) {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) st[cb][i] *= decay;
-#pragma unroll
-                for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
-                    mma32(st[cb], kt_group(sK[kc], LDK, 16 * s2, 16 * cb, lane),
-                          kt_group(sK[kc], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
-                if constexpr (NB % 2 == 1) mma16(st[cb], kt_group(sK[kc], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
-            }
-        } else {
+            // step 3: first the staging (the loads it stores arrived during the
+            // previous chunk; the new loads then fly while the rest computes): V of
+            // chunk c+1 over chunk c's, chunk c+2's gate values -> gate buffer cur
+            // and its Q and K into buffers no step reads any more (Q of chunk c, K
+            // of chunk c-1), then the loads of V(c+2) and Q, K(c+3).  Then the
+            // off-diagonal inverse of chunk c+1 (over chunk c's T, last read in
+            // step 2) and, HO, the outputs of chunk c.
+            stage(c);
             if (has_next) offdiag(WS, NHW);
-            // chunk c+2's gate values (held by SCAN_WAVE) -> gate buffer cur, whose
-            // chunk-c values the state waves no longer read
-            if (c + 2 < nchunks) scan(cur);
+            if (HO && hw >= OJ0) out_job(c, cur, hw - OJ0, oqs, oeb);
+            __syncthreads();
         }
-        // everyone: chunk c+2's tiles into buffers no step reads any more (Q and V
-        // of chunk c, K of chunk c-1), then the loads of chunk c+3
-        if (c + 2 < nchunks) {
-            commit(cur, knn);
-            if (c + 3 < nchunks) prefetch(c + 3);
+        if constexpr (!HO) {
+            if (nchunks > 0) copy_out(nchunks - 1);
         }
-        __syncthreads();
     }
 
-    if (nchunks > 0 && !state_wave) copy_out(nchunks - 1);
     if (p.S_T && state_wave) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
