@@ -583,7 +583,12 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 if (c > 0) copy_out(c - 1);
             }
             if constexpr (S32) {
-                if (has_next && hw < NJ32) score_job32(nxt, kn, hw);
+                if (has_next && hw < NJ32) {
+                    // the score jobs bound step 1: raised issue priority
+                    __builtin_amdgcn_s_setprio(1);
+                    score_job32(nxt, kn, hw);
+                    __builtin_amdgcn_s_setprio(0);
+                }
             } else {
                 if (has_next) score_tiles(nxt, kn, true, WS, NHW);
             }
@@ -606,7 +611,13 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             // off-diagonal inverse of chunk c+1 (over chunk c's T, last read in
             // step 2) and, HO, the outputs of chunk c.
             stage(c);
-            if (has_next) offdiag(WS, NHW);
+            if (has_next) {
+                // the off-diagonal inverse is the longest task of the step: raised
+                // issue priority over the waves it shares a SIMD with
+                __builtin_amdgcn_s_setprio(1);
+                offdiag(WS, NHW);
+                __builtin_amdgcn_s_setprio(0);
+            }
             if (HO && hw >= OJ0) out_job(c, cur, hw - OJ0, oqs, oeb);
             __syncthreads();
         }
