@@ -73,6 +73,21 @@ __device__ __forceinline__ void tile_mma_lr_scaled(f32x4 &acc, const Op *a, int 
     if constexpr (NK % 2 == 1) mma16(acc, scaled_group(ar + 16 * (NK - 1), sr + 16 * (NK - 1)), bg[NK - 1]);
 }
 
+// acc += Areg * B over NK k-blocks, B supplied transposed from LDS (row n of
+// `b` holds column n of B, k contiguous) with its contraction index k
+// multiplied by scale[k]; see tile_mma_rl_n.
+template <int NK, class Op, class G>
+__device__ __forceinline__ void tile_mma_rl_scaled(f32x4 &acc, const G *ag, const Op *b, int ldb, const float *scale,
+                                                   int lane) {
+    const int ko = 4 * (lane >> 4);
+    const Op *br = b + (lane & 15) * ldb + ko;
+    const float *sr = scale + ko;
+#pragma unroll
+    for (int s = 0; s + 2 <= NK; s += 2)
+        mma32(acc, ag[s], ag[s + 1], scaled_group(br + 16 * s, sr + 16 * s), scaled_group(br + 16 * s + 16, sr + 16 * s + 16));
+    if constexpr (NK % 2 == 1) mma16(acc, ag[NK - 1], scaled_group(br + 16 * (NK - 1), sr + 16 * (NK - 1)));
+}
+
 // pair index of an off-diagonal key block J <= I - 2 (blocks strictly between exist)
 __host__ __device__ constexpr int rho_index(int I, int J) { return (I - 2) * (I - 1) / 2 + J; }
 
@@ -125,7 +140,8 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     float *sZ = sF;                       // normalized: running z, [DK]
     float *sDen = sF + DK;                // normalized: denominators, [C]
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform: role branches compile to scalar branches
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     int bh, vb;
     block_to_head(blockIdx.x, p.n_heads, p.n_vblk, bh, vb);
@@ -151,6 +167,9 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     if constexpr (!GATED) {
         for (int c = tid; c < DK; c += NTHR) sZ[c] = p.z0 ? p.z0[static_cast<size_t>(bh) * DK + c] : 0.f;
     }
+    // the entering state is in registers before any tile load is issued, so
+    // the loop never waits on the global-memory counter for it
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // chunk inputs staged one chunk ahead in registers
     TilePrefetch<C, DK, NTHR, IO> pq, pk;
@@ -300,28 +319,29 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
         }
 
         // ---- intra-chunk scores P (16x16 tiles, block-lower-triangular)
+        // Each tile is taken transposed (keys x queries), so that a lane holds
+        // four consecutive columns j of one row t and writes them at once.
         for (int tt = wave; tt < NB * NB; tt += NW) {
             const int I = tt / NB, J = tt % NB;
-            const int row = 16 * I + 4 * lg, col = 16 * J + lr;
+            const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
             if (J > I) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sP[(row + i) * LDC + col] = Op(0);
+                st_group(sP + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
                 continue;
             }
             f32x4 acc = zero4();
             if constexpr (GATED) {
                 if (J == I)
-                    tile_mma_ll<DK>(acc, sQ + 16 * I * LDK, LDK, sKd + 16 * J * LDK, LDK, lane);
+                    tile_mma_ll<DK>(acc, sKd + 16 * J * LDK, LDK, sQ + 16 * I * LDK, LDK, lane);
                 else if (J == I - 1)
-                    tile_mma_ll<DK>(acc, sQ + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, lane);
+                    tile_mma_ll<DK>(acc, sK + 16 * J * LDK, LDK, sQ + 16 * I * LDK, LDK, lane);
                 else
-                    tile_mma_ll_scaled<DK>(acc, sQ + 16 * I * LDK, LDK, sRho + rho_index(I, J) * DK,
-                                           sK + 16 * J * LDK, LDK, lane);
+                    tile_mma_ll_scaled<DK>(acc, sK + 16 * J * LDK, LDK, sRho + rho_index(I, J) * DK,
+                                           sQ + 16 * I * LDK, LDK, lane);
             } else {
-                tile_mma_ll<DK>(acc, sQ + 16 * I * LDK, LDK, sK + 16 * J * LDK, LDK, lane);
+                tile_mma_ll<DK>(acc, sK + 16 * J * LDK, LDK, sQ + 16 * I * LDK, LDK, lane);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) from_f32(sP[(row + i) * LDC + col], col <= row + i ? acc[i] : 0.f);
+            st_group(sP + t * LDC + j0, Gp::make(j0 <= t ? acc[0] : 0.f, j0 + 1 <= t ? acc[1] : 0.f,
+                                                 j0 + 2 <= t ? acc[2] : 0.f, j0 + 3 <= t ? acc[3] : 0.f));
         }
         __syncthreads();
 
@@ -353,21 +373,23 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
             for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
+                // O^T = S0 Q^T + V^T P^T: lane holds values 16*wave + 4*lg..+3 of
+                // token 16 I + lr, stored at once
                 f32x4 o = zero4();
                 if constexpr (GATED) {
-                    if (I == 0) tile_mma_lr<NCB>(o, sQ, LDK, sb, lane);
-                    else tile_mma_lr_scaled<NCB>(o, sQ + 16 * I * LDK, LDK, sE + I * DK, sb, lane);
+                    if (I == 0) tile_mma_rl_n<NCB>(o, sb, sQ, LDK, NCB, lane);
+                    else tile_mma_rl_scaled<NCB>(o, sb, sQ + 16 * I * LDK, LDK, sE + I * DK, lane);
                 } else {
-                    tile_mma_lr<NCB>(o, sQ + 16 * I * LDK, LDK, sb, lane);
+                    tile_mma_rl_n<NCB>(o, sb, sQ + 16 * I * LDK, LDK, NCB, lane);
                 }
-                tile_mma_ll<C>(o, sP + 16 * I * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
+                tile_mma_ll<C>(o, sVt + 16 * wave * LDC, LDC, sP + 16 * I * LDC, LDC, lane);
+                const int t = 16 * I + lr;
+                if constexpr (!GATED) {
+                    const float inv = 1.f / sDen[t];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * I + 4 * lg + i;
-                    float val = o[i];
-                    if constexpr (!GATED) val = val / sDen[t];
-                    if (t < n) store1(oh + static_cast<size_t>(c0 + t) * p.d_v + vch, val);
+                    for (int i = 0; i < 4; ++i) o[i] *= inv;
                 }
+                if (t < n) st_group(oh + static_cast<size_t>(c0 + t) * p.d_v + vb * DVB + 16 * wave + 4 * lg, Gp::make(o));
             }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
