@@ -92,6 +92,31 @@ __device__ __forceinline__ void block_to_head(int bid, int n_heads, int n_vblk, 
     }
 }
 
+// A-operand group of K^T for key channel c = c0 + lane%16 and tokens
+// t0 + 4*(lane/16) .. +3, read from a natural-layout K tile (rows = tokens,
+// ldk elements apart; t0 and c0 multiples of 16).  SW != 0: rows with bit 3
+// set store element column c at c ^ SW.
+// bf16: one transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
+// group, lane a supplies row t0 + 4*(lane/16) + a/4, columns c0 + 4*(a%4)..+3,
+// and lane j receives column c0 + j of the group's four rows.
+template <int SW>
+__device__ __forceinline__ uint2 kt_group(const bf16_t *sK, int ldk, int t0, int c0, int lane) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int a = lane & 15, g = lane >> 4;
+    const int row = t0 + 4 * g + (a >> 2);
+    const bf16_t *src = sK + row * ldk + c0 + ((4 * (a & 3)) ^ (SW * ((row >> 3) & 1)));
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)((__attribute__((address_space(3))) bf16_t *)src));
+    return __builtin_bit_cast(uint2, r);
+}
+// float32: four scalar reads of the column (no swizzle)
+template <int SW>
+__device__ __forceinline__ float4 kt_group(const float *sK, int ldk, int t0, int c0, int lane) {
+    static_assert(SW == 0, "float32 tiles are not swizzled");
+    const float *src = sK + (t0 + 4 * (lane >> 4)) * ldk + c0 + (lane & 15);
+    return make_float4(src[0], src[ldk], src[2 * ldk], src[3 * ldk]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
 #pragma unroll

@@ -75,27 +75,6 @@ constexpr int gdr_lds_bytes() {
            C * (C + 4) * 4 + 2 * (4 * C + 1) * 4;
 }
 
-// A-operand group of K^T for key channel c = c0 + lane%16 and tokens
-// t0 + 4*(lane/16) .. +3, read from the natural-layout K tile (rows = tokens).
-// bf16: one transposing LDS read (ds_read_b64_tr_b16): within each 16-lane
-// group, lane a supplies row t0 + 4*(lane/16) + a/4, columns c0 + 4*(a%4)..+3,
-// and lane j receives column c0 + j of the group's four rows.
-// Rows are in the Q/K layout above (t0 and c0 multiples of 16).
-__device__ __forceinline__ uint2 kt_group(const bf16_t *sK, int ldk, int t0, int c0, int lane) {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    const int a = lane & 15, g = lane >> 4;
-    const int row = t0 + 4 * g + (a >> 2);
-    const bf16_t *src = sK + row * ldk + c0 + swap_col(row, 4 * (a & 3), gdr_kswap<bf16_t>());
-    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)((__attribute__((address_space(3))) bf16_t *)src));
-    return __builtin_bit_cast(uint2, r);
-}
-// float32: four scalar reads of the column
-__device__ __forceinline__ float4 kt_group(const float *sK, int ldk, int t0, int c0, int lane) {
-    const float *src = sK + (t0 + 4 * (lane >> 4)) * ldk + c0 + (lane & 15);
-    return make_float4(src[0], src[ldk], src[2 * ldk], src[3 * ldk]);
-}
-
 template <class DT, int DK, int DVB, int C, int NW>
 __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p) {
     typedef typename DT::storage IO;
@@ -560,9 +539,9 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     for (int i = 0; i < 4; ++i) st[cb][i] *= decay;
 #pragma unroll
                     for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
-                        mma32(st[cb], kt_group(sK[kc], LDK, 16 * s2, 16 * cb, lane),
-                              kt_group(sK[kc], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
-                    if constexpr (NB % 2 == 1) mma16(st[cb], kt_group(sK[kc], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
+                        mma32(st[cb], kt_group<KSW>(sK[kc], LDK, 16 * s2, 16 * cb, lane),
+                              kt_group<KSW>(sK[kc], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
+                    if constexpr (NB % 2 == 1) mma16(st[cb], kt_group<KSW>(sK[kc], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
                 }
                 publish_s0();   // HO: entering state of chunk c+1
             }

@@ -25,8 +25,10 @@
 //     multiply below ~1e-30 (documented precondition).
 //   * inter-chunk: O += (Qhat_t * E_I) S0^T, E_I = prod_{i < 16I} gamma_i;
 //     S_C = S0 diag(prod_all gamma) + V^T (phi(K) o prod_{j < i < C} gamma_i).
-// All gate factors are running products of the gates themselves, so no
-// exponential or logarithm is evaluated.
+// All gate factors are running products of the gates themselves (within a
+// block by a 16-lane scan), so no exponential or logarithm is evaluated; kd
+// multiplies by the hardware reciprocal of the running product (about one
+// ulp), and k~ is kd times the block's whole product.
 //
 // Work decomposition as in the delta-rule kernel: one workgroup per (b, h,
 // block of DVB value channels); wave w keeps the transposed state slice of
@@ -88,6 +90,20 @@ __device__ __forceinline__ void tile_mma_rl_scaled(f32x4 &acc, const G *ag, cons
     if constexpr (NK % 2 == 1) mma16(acc, ag[NK - 1], scaled_group(br + 16 * (NK - 1), sr + 16 * (NK - 1)));
 }
 
+// Inclusive product over each 16-lane row of a wave: lane i of a row gets
+// x_0 * ... * x_i (DPP row shifts; sources outside the row read as 1).
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_scan_mul(float x) {
+    x *= dpp_or_one<0x111>(x);   // row_shr:1
+    x *= dpp_or_one<0x112>(x);   // row_shr:2
+    x *= dpp_or_one<0x114>(x);   // row_shr:4
+    x *= dpp_or_one<0x118>(x);   // row_shr:8
+    return x;
+}
+
 // pair index of an off-diagonal key block J <= I - 2 (blocks strictly between exist)
 __host__ __device__ constexpr int rho_index(int I, int J) { return (I - 2) * (I - 1) / 2 + J; }
 
@@ -103,8 +119,9 @@ struct LinearLds {
     static constexpr int P_BYTES = C * LDC * (int)sizeof(Op);
     static constexpr int G_BYTES = GATED ? C * LDG * 4 : 0;
     static constexpr int PG_BYTES = P_BYTES > G_BYTES ? P_BYTES : G_BYTES;
-    static constexpr int F_FLOATS = GATED ? (2 * NB + 1 + NRHO) * DK : DK + C;
-    static constexpr int BYTES = (GATED ? 3 : 2) * C * LDK * (int)sizeof(Op) + DK * LDC * (int)sizeof(Op) +
+    static constexpr int F_FLOATS = GATED ? (NB + 1 + NRHO) * DK : DK + C;
+    static constexpr int KT_ELEMS = GATED ? C * LDK : DK * LDC;   // state-update key operand
+    static constexpr int BYTES = (GATED ? 3 : 2) * C * LDK * (int)sizeof(Op) + KT_ELEMS * (int)sizeof(Op) +
                                  DVB * LDC * (int)sizeof(Op) + PG_BYTES + F_FLOATS * 4;
 };
 
@@ -127,7 +144,8 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     __shared__ __align__(16) Op sQ[C * LDK];                 // phi(Q) | Qhat
     __shared__ __align__(16) Op sK[C * LDK];                 // phi(K) | k~ (off-diagonal reference)
     __shared__ __align__(16) Op sKd[GATED ? C * LDK : 8];    // kd (diagonal reference)
-    __shared__ __align__(16) Op sKt[DK * LDC];               // key operand of the state update, [c][t]
+    __shared__ __align__(16) Op sKt[L::KT_ELEMS];            // key operand of the state update:
+                                                             // gated [t][c], normalized [c][t]
     __shared__ __align__(16) Op sVt[DVB * LDC];              // this block's values, [v][t]
     __shared__ __align__(16) unsigned char sPG[L::PG_BYTES]; // gates (f32), then P
     __shared__ __align__(16) float sF[L::F_FLOATS];
@@ -136,7 +154,6 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     float *sE = sF;                       // gated: prod of the chunk's gates before block I, [NB][DK]
     float *sD = sF + NB * DK;             // gated: prod of all the chunk's gates, [DK]
     float *sRho = sF + (NB + 1) * DK;     // gated: prod of the blocks strictly between J and I, [NRHO][DK]
-    float *sBT = sF + (NB + 1 + L::NRHO) * DK;  // gated: prod of the gates of block I, [NB][DK]
     float *sZ = sF;                       // normalized: running z, [DK]
     float *sDen = sF + DK;                // normalized: denominators, [C]
 
@@ -183,6 +200,19 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
         if constexpr (GATED) pgt.load(gh + static_cast<size_t>(c0) * DK, DK, n, tid);
     };
     if (p.T > 0) prefetch(0);
+
+    // The state waves keep a chunk's outputs in registers and store them after
+    // the next chunk's commit: the commit's wait on the global-memory counter
+    // (for the staged loads) then never waits for just-issued output stores.
+    f32x4 ob[NB];
+    auto store_outputs = [&](int oc0) {
+        const int on = min(C, p.T - oc0);
+#pragma unroll
+        for (int I = 0; I < NB; ++I) {
+            const int t = 16 * I + lr;
+            if (t < on) st_group(oh + static_cast<size_t>(oc0 + t) * p.d_v + vb * DVB + 16 * wave + 4 * lg, Gp::make(ob[I]));
+        }
+    };
 
     for (int c0 = 0; c0 < p.T; c0 += C) {
         const int n = min(C, p.T - c0);
@@ -254,65 +284,80 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
             }
         }
         __syncthreads();
+        if (wave < WS && c0 > 0) store_outputs(c0 - C);
         if (c0 + C < p.T) prefetch(c0 + C);
 
         if constexpr (GATED) {
-            // ---- gate products, one thread per (key channel, 16-token block)
-            for (int e = tid; e < NB * DK; e += NTHR) {
-                const int c = e % DK, I = e / DK;
-                float run = 1.f;
+            // ---- gate factors.  A wave takes four key channels of every token of
+            // the chunk (lane = token): the products along the tokens of a 16-token
+            // block are scans over a 16-lane DPP row, so every token's factors come
+            // out at once and are written four channels at a time.
+            const int t = lane, I = t >> 4;
+            const bool in_tile = t < C, on = t < n;
+            for (int c = 4 * wave; c < DK; c += 4 * NW) {
+                float g[4] = {1.f, 1.f, 1.f, 1.f}, q[4] = {0.f, 0.f, 0.f, 0.f}, k[4] = {0.f, 0.f, 0.f, 0.f};
+                if (in_tile) {
+                    const float4 g4 = *reinterpret_cast<const float4 *>(sG + t * LDG + c);
+                    g[0] = g4.x; g[1] = g4.y; g[2] = g4.z; g[3] = g4.w;   // 1 past the sequence end
+                    Gp::unpack(ld_group(sQ + t * LDK + c), q);
+                    Gp::unpack(ld_group(sK + t * LDK + c), k);
+                }
+                float run[4], rinv[4];
 #pragma unroll
-                for (int t = 16 * I; t < 16 * I + 16; ++t) run *= sG[t * LDG + c];
-                sBT[I * DK + c] = run;
-            }
-            __syncthreads();
-            for (int e = tid; e < NB * DK; e += NTHR) {
-                const int c = e % DK, I = e / DK;
-                float bt[NB];
+                for (int i = 0; i < 4; ++i) {
+                    run[i] = row_scan_mul(g[i]);   // R_t = prod_{16I <= s <= t} g_s
+                    rinv[i] = __builtin_amdgcn_rcpf(run[i]);
+                }
+                float tot[NB][4];   // whole-block products (uniform)
 #pragma unroll
-                for (int J = 0; J < NB; ++J) bt[J] = sBT[J * DK + c];
-                float after = 1.f;   // prod of the gates of the blocks after I
+                for (int J = 0; J < NB; ++J)
 #pragma unroll
-                for (int J = NB - 1; J > 0; --J)
-                    if (J > I) after *= bt[J];
-                if (I == 0) {
-                    float before = 1.f;
+                    for (int i = 0; i < 4; ++i)
+                        tot[J][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(run[i]), 16 * J + 15));
+                if (lane < NB + 1 + L::NRHO) {
+                    // per-chunk factors, one float4 per lane: E_J (lanes < NB), D, rho
+                    float e[4];
 #pragma unroll
-                    for (int J = 0; J < NB; ++J) {
-                        sE[J * DK + c] = before;
-                        before *= bt[J];
-                    }
-                    sD[c] = before;
+                    for (int i = 0; i < 4; ++i) {
+                        float acc = 1.f;
 #pragma unroll
-                    for (int J1 = 2; J1 < NB; ++J1) {
-                        float r = 1.f;
-#pragma unroll
-                        for (int J0 = J1 - 2; J0 >= 0; --J0) {
-                            r *= bt[J0 + 1];
-                            sRho[rho_index(J1, J0) * DK + c] = r;
+                        for (int J = 0; J < NB; ++J) {
+                            if (lane < NB) acc *= J < lane ? tot[J][i] : 1.f;            // E_lane
+                            else if (lane == NB) acc *= tot[J][i];                        // D
                         }
+#pragma unroll
+                        for (int J1 = 2; J1 < NB; ++J1)
+#pragma unroll
+                            for (int J0 = 0; J0 + 2 <= J1; ++J0)
+                                if (lane == NB + 1 + rho_index(J1, J0))
+#pragma unroll
+                                    for (int J = J0 + 1; J < J1; ++J) acc *= tot[J][i];   // rho_{J1 J0}
+                        e[i] = acc;
                     }
+                    *reinterpret_cast<float4 *>(sE + lane * DK + c) = make_float4(e[0], e[1], e[2], e[3]);
                 }
-                // forward within the block: Qhat = phi(q) R_t, kd = phi(k) / R_t
-                float run = 1.f;
+                // Qhat = phi(q) R_t, kd = phi(k) / R_t, k~ = phi(k) prod_{t<s<=e_I} g_s
+                // = kd * (block product), and the state-update operand k~ times the
+                // product of the later blocks (natural layout)
+                float fq[4], fd[4], fk[4], fa[4];
 #pragma unroll
-                for (int t = 16 * I; t < 16 * I + 16; ++t) {
-                    const bool on = t < n;
-                    run *= sG[t * LDG + c];
-                    const float fq = on ? apply_phi<PHI>(to_f32(sQ[t * LDK + c])) : 0.f;
-                    const float fk = on ? apply_phi<PHI>(to_f32(sK[t * LDK + c])) : 0.f;
-                    from_f32(sQ[t * LDK + c], fq * run);
-                    from_f32(sKd[t * LDK + c], fk / run);
+                for (int i = 0; i < 4; ++i) {
+                    float tb = tot[0][i], after = 1.f;   // this token's block, the blocks after it
+#pragma unroll
+                    for (int J = 1; J < NB; ++J) {
+                        if (J == I) tb = tot[J][i];
+                        if (J > I) after *= tot[J][i];
+                    }
+                    fq[i] = on ? apply_phi<PHI>(q[i]) * run[i] : 0.f;
+                    fd[i] = on ? apply_phi<PHI>(k[i]) * rinv[i] : 0.f;
+                    fk[i] = fd[i] * tb;
+                    fa[i] = fk[i] * after;
                 }
-                // reverse within the block: k~ = phi(k) prod_{t<i<=e_I} gamma, and the
-                // state-update operand phi(k) prod_{t<i<C} gamma
-                float rev = 1.f;
-#pragma unroll
-                for (int t = 16 * I + 15; t >= 16 * I; --t) {
-                    const float fk = t < n ? apply_phi<PHI>(to_f32(sK[t * LDK + c])) : 0.f;
-                    from_f32(sK[t * LDK + c], fk * rev);
-                    from_f32(sKt[c * LDC + t], fk * rev * after);
-                    rev *= sG[t * LDG + c];
+                if (in_tile) {
+                    st_group(sQ + t * LDK + c, Gp::make(fq[0], fq[1], fq[2], fq[3]));
+                    st_group(sKd + t * LDK + c, Gp::make(fd[0], fd[1], fd[2], fd[3]));
+                    st_group(sK + t * LDK + c, Gp::make(fk[0], fk[1], fk[2], fk[3]));
+                    st_group(sKt + t * LDK + c, Gp::make(fa[0], fa[1], fa[2], fa[3]));
                 }
             }
             __syncthreads();   // the gate tile is dead from here on; its space holds P
@@ -383,13 +428,12 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                     tile_mma_rl_n<NCB>(o, sb, sQ + 16 * I * LDK, LDK, NCB, lane);
                 }
                 tile_mma_ll<C>(o, sVt + 16 * wave * LDC, LDC, sP + 16 * I * LDC, LDC, lane);
-                const int t = 16 * I + lr;
                 if constexpr (!GATED) {
-                    const float inv = 1.f / sDen[t];
+                    const float inv = 1.f / sDen[16 * I + lr];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) o[i] *= inv;
                 }
-                if (t < n) st_group(oh + static_cast<size_t>(c0 + t) * p.d_v + vb * DVB + 16 * wave + 4 * lg, Gp::make(o));
+                ob[I] = o;
             }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
@@ -397,12 +441,25 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 #pragma unroll
                     for (int i = 0; i < 4; ++i) st[cb][i] *= sD[16 * cb + 4 * lg + i];
                 }
-                tile_mma_ll<C>(st[cb], sKt + 16 * cb * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
+                if constexpr (GATED) {
+                    // K^T from the natural-layout operand tile by transposing reads
+                    const Op *vrow = sVt + (16 * wave + lr) * LDC + 4 * lg;
+#pragma unroll
+                    for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
+                        mma32(st[cb], kt_group<0>(sKt, LDK, 16 * s2, 16 * cb, lane),
+                              kt_group<0>(sKt, LDK, 16 * s2 + 16, 16 * cb, lane), ld_group(vrow + 16 * s2),
+                              ld_group(vrow + 16 * s2 + 16));
+                    if constexpr (NB % 2 == 1)
+                        mma16(st[cb], kt_group<0>(sKt, LDK, 16 * (NB - 1), 16 * cb, lane), ld_group(vrow + 16 * (NB - 1)));
+                } else {
+                    tile_mma_ll<C>(st[cb], sKt + 16 * cb * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
+                }
             }
         }
         __syncthreads();
     }
 
+    if (wave < WS && p.T > 0) store_outputs(((p.T - 1) / C) * C);
     if (p.S_T && wave < WS) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
