@@ -156,7 +156,13 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // ---------------------------------------------------------------- stages
     // All waves stage the tiles, in step 3: register prefetch one chunk ahead,
     // then LDS (Q, K and the gate values two chunks ahead, V one chunk ahead).
-    TilePrefetch<C, DK, NTHR, IO> pq, pk;
+    // K: with two or more state waves they stage it alone, in step 1, where they
+    // wait for the score jobs anyway (chunk c+2's K goes to the buffer chunk
+    // c-1's used, free for the whole of chunk c)
+    constexpr bool KSTATE = WS >= 2;
+    constexpr int KTHR = KSTATE ? WS * 64 : NTHR;
+    TilePrefetch<C, DK, NTHR, IO> pq;
+    TilePrefetch<C, DK, KTHR, IO> pk;
     TilePrefetch<C, DVB, NTHR, IO> pv;
     // the gate scan runs on the last wave, which has no block column of the
     // off-diagonal inverse to work on
@@ -174,7 +180,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             pb = bth[c0 + (lane < n ? lane : 0)];
         }
     };
-    auto load_k = [&](int c) { pk.load(kh + static_cast<size_t>(c * C) * DK, DK, rows(c), tid); };
+    auto load_k = [&](int c) { pk.load(kh + static_cast<size_t>(c * C) * DK, DK, rows(c), tid); };   // KSTATE: state waves
     auto load_v = [&](int c) { pv.load(vh + static_cast<size_t>(c * C) * p.d_v, p.d_v, rows(c), tid); };
     auto store_q = [&](int buf) { pq.template store<KSW>(sQ[buf], LDK, tid); };
     auto store_k = [&](int kbuf) { pk.template store<KSW>(sK[kbuf], LDK, tid); };
@@ -399,32 +405,40 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // ---------------------------------------------------------------- prologue
     // staging: everyone; chunk 0's tiles and gates, then chunk 0's scores and
     // inverse, chunk 1's Q, K and gates; the registers then hold V(1), Q(2), K(2)
+    const bool k_stager = !KSTATE || state_wave;
     auto stage = [&](int c) {
         if (c + 1 < nchunks) store_v();
         if (c + 2 < nchunks) {
             store_q(c & 1);
-            store_k((c + 2) % 3);
+            if constexpr (!KSTATE) store_k((c + 2) % 3);
             scan(c & 1, c + 2);
             load_v(c + 2);
         }
         if (c + 3 < nchunks) {
             load_q(c + 3);
-            load_k(c + 3);
+            if constexpr (!KSTATE) load_k(c + 3);
+        }
+    };
+    // KSTATE, state waves, step 1: chunk c+2's K
+    auto stage_k = [&](int c) {
+        if constexpr (KSTATE) {
+            if (c + 2 < nchunks) store_k((c + 2) % 3);
+            if (c + 3 < nchunks) load_k(c + 3);
         }
     };
     if (nchunks > 0) {
         load_q(0);
-        load_k(0);
+        if (k_stager) load_k(0);
         load_v(0);
         store_q(0);
-        store_k(0);
+        if (k_stager) store_k(0);
         store_v();
         scan(0, 0);
         if (state_wave) publish_s0();
         __syncthreads();
         if (nchunks > 1) {
             load_q(1);
-            load_k(1);
+            if (k_stager) load_k(1);
             load_v(1);
         }
         if constexpr (S32) {
@@ -440,12 +454,12 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         __syncthreads();
         if (nchunks > 1) {
             store_q(1);
-            store_k(1);
+            if (k_stager) store_k(1);
             scan(1, 1);
             __syncthreads();
             if (nchunks > 2) {
                 load_q(2);
-                load_k(2);
+                if (k_stager) load_k(2);
             }
         }
     }
@@ -498,6 +512,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     yb[I] = Gp::make(y);
                 }
             }
+            stage_k(c);
             __syncthreads();
 
             // step 2: U = T Y and (not HO) the outputs of chunk c
