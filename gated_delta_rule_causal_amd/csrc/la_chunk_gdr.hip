@@ -14,7 +14,8 @@
 // after which
 //   O   = diag(e^b) Q S0^T + (M o Gamma o Q K^T) U        (M: j <= t)
 //   S_C = e^{b_C} S0 + U^T diag(e^{b_C - b}) K.
-// Every exponent used is <= 0.  T = (I + A)^{-1} depends on K, g and beta
+// Every exponent used is <= 0 (the kernel keeps b in base 2 and evaluates
+// each factor with one hardware exp2).  T = (I + A)^{-1} depends on K, g and beta
 // only; it is formed per chunk from 16x16 blocks: the diagonal blocks by
 // forward substitution, the off-diagonal blocks by
 // T_ij = -T_ii sum_{j<=m<i} A_im T_mj, all in float32.
@@ -185,19 +186,21 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     auto store_q = [&](int buf) { pq.template store<KSW>(sQ[buf], LDK, tid); };
     auto store_k = [&](int kbuf) { pk.template store<KSW>(sK[kbuf], LDK, tid); };
     auto store_v = [&]() { pv.store(sV, LDV, tid); };
-    // SCAN_WAVE: cumulative log-gates of the staged chunk c into buffer `buf`
+    // SCAN_WAVE: cumulative log2-gates of the staged chunk c into buffer `buf`
+    // (b and every factor below in base 2: e^{b_t - b_j} = 2^{b2_t - b2_j})
     auto scan = [&](int buf, int c) {
         if (wave == SCAN_WAVE) {
             const bool in = lane < min(C, p.T - c * C);
-            const float b = wave_inclusive_sum(in ? __logf(pg) : 0.f, lane);
+            // b in log2 units: every factor is then one hardware exp2
+            const float b = wave_inclusive_sum(in ? __builtin_amdgcn_logf(pg) : 0.f, lane);
             const float bC = __shfl(b, C - 1, 64);
             if (lane < C) {
                 sB[buf][lane] = b;
-                sEB[buf][lane] = __expf(b);
-                sEBC[buf][lane] = __expf(bC - b);
+                sEB[buf][lane] = __builtin_amdgcn_exp2f(b);
+                sEBC[buf][lane] = __builtin_amdgcn_exp2f(bC - b);
                 sBeta[buf][lane] = in ? pb : 0.f;
             }
-            if (lane == 0) sDecay[buf] = __expf(bC);
+            if (lane == 0) sDecay[buf] = __builtin_amdgcn_exp2f(bC);
         }
     };
     // lower score tiles of buffer `buf`, work split over waves [w0, w0 + nw):
@@ -219,8 +222,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             tile_mma_qk<DK, KSW>(acc, K + 16 * J * LDK, X + 16 * I * LDK, LDK, lane);
             const float bt = bb[t];
             const float4 bs = *reinterpret_cast<const float4 *>(bb + s0);
-            const float g0 = __expf(fminf(bt - bs.x, 0.f)), g1 = __expf(fminf(bt - bs.y, 0.f));
-            const float g2 = __expf(fminf(bt - bs.z, 0.f)), g3 = __expf(fminf(bt - bs.w, 0.f));
+            const float g0 = __builtin_amdgcn_exp2f(fminf(bt - bs.x, 0.f)), g1 = __builtin_amdgcn_exp2f(fminf(bt - bs.y, 0.f));
+            const float g2 = __builtin_amdgcn_exp2f(fminf(bt - bs.z, 0.f)), g3 = __builtin_amdgcn_exp2f(fminf(bt - bs.w, 0.f));
             if (isK) {
                 const float be = beta[t];
                 *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
@@ -267,8 +270,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             for (int q = 0; q < 4; ++q) {
                 const int s0 = 32 * J + 8 * q + 4 * h;
                 const float4 bs = *reinterpret_cast<const float4 *>(sB[buf] + s0);
-                const float g0 = __expf(fminf(bt - bs.x, 0.f)), g1 = __expf(fminf(bt - bs.y, 0.f));
-                const float g2 = __expf(fminf(bt - bs.z, 0.f)), g3 = __expf(fminf(bt - bs.w, 0.f));
+                const float g0 = __builtin_amdgcn_exp2f(fminf(bt - bs.x, 0.f)), g1 = __builtin_amdgcn_exp2f(fminf(bt - bs.y, 0.f));
+                const float g2 = __builtin_amdgcn_exp2f(fminf(bt - bs.z, 0.f)), g3 = __builtin_amdgcn_exp2f(fminf(bt - bs.w, 0.f));
                 if (isK)
                     *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
                         make_float4(s0 < t ? be * g0 * acc[4 * q] : 0.f, s0 + 1 < t ? be * g1 * acc[4 * q + 1] : 0.f,
