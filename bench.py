@@ -183,7 +183,7 @@ def main(argv=None):
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the operator is measured on one GPU's share; "
-              "multi-GPU runs are not part of this build (got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              "multi-GPU runs are not supported (got --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
               file=sys.stderr)
         return 2
 

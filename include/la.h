@@ -69,7 +69,7 @@ extern "C" {
 typedef enum {
     LA_OK = 0,
     LA_EINVAL = 1,        /* bad argument: null pointer, bad size, bad combination, misalignment, aliasing */
-    LA_EUNSUPPORTED = 2,  /* valid request this build has no kernel for (head size, chunk size) */
+    LA_EUNSUPPORTED = 2,  /* valid request the library has no kernel for (head size, chunk size) */
     LA_EHIP = 3           /* the HIP runtime reported an error at launch */
 } la_status;
 
