@@ -293,17 +293,20 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = 4 * pp + i == n ? 1.f : 0.f;
-        float4 row = *reinterpret_cast<const float4 *>(Ab + 1 * LDA + 4 * pp), nxt4;
+        // every row's four entries are read up front: one LDS latency instead
+        // of one per step of the substitution
+        float4 rows[15];
+#pragma unroll
+        for (int t = 1; t < 16; ++t) rows[t - 1] = *reinterpret_cast<const float4 *>(Ab + t * LDA + 4 * pp);
 #pragma unroll
         for (int t = 1; t < 16; ++t) {
-            if (t + 1 < 16) nxt4 = *reinterpret_cast<const float4 *>(Ab + (t + 1) * LDA + 4 * pp);
+            const float4 row = rows[t - 1];
             // A's diagonal and upper part are zero, so the not yet computed
             // entries (zero) and x[n] = 1 above row t add nothing
             float part = (row.x * x[0] + row.y * x[1]) + (row.z * x[2] + row.w * x[3]);
             part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0xB1, 0xF, 0xF, true));  // lanes ^1
             part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x4E, 0xF, 0xF, true));  // lanes ^2
             if (pp == (t >> 2) && t > n) x[t & 3] = -part;
-            row = nxt4;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) Ab[(4 * pp + i) * LDA + n] = x[i];
