@@ -50,16 +50,19 @@ struct TilePrefetch {
     uint4 r[PER];
     uint32_t valid;   // bit i: r[i] holds a row < n
 
+    // Every lane issues every load (lanes past the tile re-read its last
+    // element, rows past n re-read row 0): no load sits behind a branch, so the
+    // compiler's count of loads in flight is the same on every path and its
+    // waits for one tile never extend to loads issued after it.
     __device__ __forceinline__ void load(const E *src, size_t lds, int n, int tid) {
         valid = 0;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int e = tid + i * NTHR;
-            const int row = e / VPR, col = (e % VPR) * VE;
-            if (TOTAL % NTHR == 0 || e < TOTAL) {
-                r[i] = *reinterpret_cast<const uint4 *>(src + (row < n ? row : 0) * lds + col);
-                valid |= (row < n ? 1u : 0u) << i;
-            }
+            const int ec = (TOTAL % NTHR == 0 || e < TOTAL) ? e : TOTAL - 1;
+            const int row = ec / VPR, col = (ec % VPR) * VE;
+            r[i] = *reinterpret_cast<const uint4 *>(src + (row < n ? row : 0) * lds + col);
+            valid |= (row < n && ec == e ? 1u : 0u) << i;
         }
     }
     // SW != 0: on rows with bit 3 set, element column c goes to c ^ SW
@@ -117,14 +120,28 @@ __device__ __forceinline__ float4 kt_group(const float *sK, int ldk, int t0, int
     return make_float4(src[0], src[ldk], src[2 * ldk], src[3 * ldk]);
 }
 
+// DPP move with control CTRL; lanes whose source is invalid read 0
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// value of x in lane l (l uniform), as a scalar
+__device__ __forceinline__ float read_lane(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_inclusive_sum(float x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
+    // within each 16-lane row: DPP row shifts by 1, 2, 4, 8 (sources outside
+    // the row read as 0); then the totals of the rows below, read as scalars.
+    // No LDS access, so the scan does not queue behind other waves' LDS work.
+    x += dpp_or_zero<0x111>(x);
+    x += dpp_or_zero<0x112>(x);
+    x += dpp_or_zero<0x114>(x);
+    x += dpp_or_zero<0x118>(x);
+    const float t0 = read_lane(x, 15), t1 = read_lane(x, 31), t2 = read_lane(x, 47);
+    const int row = lane >> 4;
+    return x + (row >= 1 ? t0 : 0.f) + (row >= 2 ? t1 : 0.f) + (row >= 3 ? t2 : 0.f);
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

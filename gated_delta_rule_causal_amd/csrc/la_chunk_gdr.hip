@@ -193,7 +193,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             const bool in = lane < min(C, p.T - c * C);
             // b in log2 units: every factor is then one hardware exp2
             const float b = wave_inclusive_sum(in ? __builtin_amdgcn_logf(pg) : 0.f, lane);
-            const float bC = __shfl(b, C - 1, 64);
+            const float bC = read_lane(b, C - 1);
             if (lane < C) {
                 sB[buf][lane] = b;
                 sEB[buf][lane] = __builtin_amdgcn_exp2f(b);
@@ -410,26 +410,31 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
 
     // ---------------------------------------------------------------- prologue
     // staging: everyone; chunk 0's tiles and gates, then chunk 0's scores and
-    // inverse, chunk 1's Q, K and gates; the registers then hold V(1), Q(2), K(2)
+    // inverse, chunk 1's Q, K and gates; the registers then hold K(2), V(1),
+    // Q(2), issued in this order, the order in which a chunk of the loop below
+    // leaves them in flight.
+    // The loads are issued whether or not their chunk exists (a chunk past the
+    // end re-reads the last one and is never stored): every path through the
+    // loop then issues the same loads in the same order, and the compiler's
+    // wait for one tile covers that tile alone, not the loads issued after it.
     const bool k_stager = !KSTATE || state_wave;
+    const int clast = nchunks - 1;
     auto stage = [&](int c) {
         if (c + 1 < nchunks) store_v();
         if (c + 2 < nchunks) {
             store_q(c & 1);
             if constexpr (!KSTATE) store_k((c + 2) % 3);
             scan(c & 1, c + 2);
-            load_v(c + 2);
         }
-        if (c + 3 < nchunks) {
-            load_q(c + 3);
-            if constexpr (!KSTATE) load_k(c + 3);
-        }
+        load_v(min(c + 2, clast));
+        load_q(min(c + 3, clast));
+        if constexpr (!KSTATE) load_k(min(c + 3, clast));
     };
     // KSTATE, state waves, step 1: chunk c+2's K
     auto stage_k = [&](int c) {
         if constexpr (KSTATE) {
             if (c + 2 < nchunks) store_k((c + 2) % 3);
-            if (c + 3 < nchunks) load_k(c + 3);
+            load_k(min(c + 3, clast));
         }
     };
     if (nchunks > 0) {
@@ -442,11 +447,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         scan(0, 0);
         if (state_wave) publish_s0();
         __syncthreads();
-        if (nchunks > 1) {
-            load_q(1);
-            if (k_stager) load_k(1);
-            load_v(1);
-        }
+        load_q(min(1, clast));
+        if (k_stager) load_k(min(1, clast));
         if constexpr (S32) {
             if (wave < NJ32) score_job32(0, 0, wave);
         } else {
@@ -462,167 +464,166 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             store_q(1);
             if (k_stager) store_k(1);
             scan(1, 1);
-            __syncthreads();
-            if (nchunks > 2) {
-                load_q(2);
-                if (k_stager) load_k(2);
-            }
         }
-    }
+        __syncthreads();
+        if (k_stager) load_k(min(2, clast));
+        load_v(min(1, clast));
+        load_q(min(2, clast));
 
-    // ---------------------------------------------------------------- chunk loop
-    // The two roles run loops of their own with the same three barriers per
-    // chunk, so that each role's registers are allocated for its own work.
-    if (state_wave) {
-        for (int c = 0; c < nchunks; ++c) {
-            const int cur = c & 1, kc = c % 3;
+        // ---------------------------------------------------------------- chunk loop
+        // The two roles run loops of their own with the same three barriers per
+        // chunk, so that each role's registers are allocated for its own work.
+        if (state_wave) {
+            for (int c = 0; c < nchunks; ++c) {
+                const int cur = c & 1, kc = c % 3;
 
-            // step 1: K S0^T, Q S0^T and the solve's right-hand side Y of chunk c
-            G4 yb[NB];
-            f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
-            {
-                G4 sb[NCB];
+                // step 1: K S0^T, Q S0^T and the solve's right-hand side Y of chunk c
+                G4 yb[NB];
+                f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
+                {
+                    G4 sb[NCB];
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
-                f32x4 ks[NB];
+                    for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
+                    f32x4 ks[NB];
 #pragma unroll
-                for (int I = 0; I < NB; ++I) { ks[I] = zero4(); qs[I] = zero4(); }   // qs: unused with HO
-                const int ko = swap_col(lr, 4 * lg, KSW);   // rows 16 I + lr
+                    for (int I = 0; I < NB; ++I) { ks[I] = zero4(); qs[I] = zero4(); }   // qs: unused with HO
+                    const int ko = swap_col(lr, 4 * lg, KSW);   // rows 16 I + lr
 #pragma unroll
-                for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
+                    for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            const Op *kr = sK[kc] + (16 * I + lr) * LDK + ko + 16 * s2;
+                            const Op *qr = sQ[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
+                            mma32(ks[I], ld_group(kr), ld_group(kr + 16), sb[s2], sb[s2 + 1]);
+                            if constexpr (!HO) mma32(qs[I], sb[s2], sb[s2 + 1], ld_group(qr), ld_group(qr + 16));
+                        }
+                    }
+                    if constexpr (NCB % 2 == 1) {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            mma16(ks[I], ld_group(sK[kc] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
+                            if constexpr (!HO) mma16(qs[I], sb[NCB - 1], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)));
+                        }
+                    }
 #pragma unroll
                     for (int I = 0; I < NB; ++I) {
-                        const Op *kr = sK[kc] + (16 * I + lr) * LDK + ko + 16 * s2;
-                        const Op *qr = sQ[cur] + (16 * I + lr) * LDK + ko + 16 * s2;
-                        mma32(ks[I], ld_group(kr), ld_group(kr + 16), sb[s2], sb[s2 + 1]);
-                        if constexpr (!HO) mma32(qs[I], sb[s2], sb[s2 + 1], ld_group(qr), ld_group(qr + 16));
+                        const float4 be = *reinterpret_cast<const float4 *>(&sBeta[cur][16 * I + 4 * lg]);
+                        const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
+                        const Op *vr = sV + (16 * I + 4 * lg) * LDV + vloc;
+                        f32x4 y;
+                        y[0] = be.x * (to_f32(vr[0]) - eb.x * ks[I][0]);
+                        y[1] = be.y * (to_f32(vr[LDV]) - eb.y * ks[I][1]);
+                        y[2] = be.z * (to_f32(vr[2 * LDV]) - eb.z * ks[I][2]);
+                        y[3] = be.w * (to_f32(vr[3 * LDV]) - eb.w * ks[I][3]);
+                        yb[I] = Gp::make(y);
                     }
                 }
-                if constexpr (NCB % 2 == 1) {
+                stage_k(c);
+                __syncthreads();
+
+                // step 2: U = T Y and (not HO) the outputs of chunk c
+                G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
+                float decay;
+                {
+                    decay = sDecay[cur];
+                    G4 ub[NB];
 #pragma unroll
                     for (int I = 0; I < NB; ++I) {
-                        mma16(ks[I], ld_group(sK[kc] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)), sb[NCB - 1]);
-                        if constexpr (!HO) mma16(qs[I], sb[NCB - 1], ld_group(sQ[cur] + (16 * I + lr) * LDK + ko + 16 * (NCB - 1)));
+                        f32x4 u = zero4();
+                        tile_mma_lr_n<NB>(u, sT + 16 * I * LDC, LDC, yb, I + 1, lane);
+                        ub[I] = Gp::make(u);
+                        // HO: U^T for the output jobs (rows = values, four tokens per write)
+                        if constexpr (HO) st_group(sUT + vloc * LDU + 16 * I + 4 * lg, ub[I]);
+                        const float4 ec = *reinterpret_cast<const float4 *>(&sEBC[cur][16 * I + 4 * lg]);
+                        usb[I] = Gp::make(u[0] * ec.x, u[1] * ec.y, u[2] * ec.z, u[3] * ec.w);
+                    }
+                    if constexpr (!HO) {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            // O^T = U^T P^T: lane holds values 16*wave + 4*lg..+3 of token 16 I + lr
+                            f32x4 o = zero4();
+                            tile_mma_rl_n<NB>(o, ub, sP[cur] + 16 * I * LDC, LDC, I + 1, lane);
+                            const float eb = sEB[cur][16 * I + lr];
+                            st_group(sO + (16 * I + lr) * LDV + 16 * wave + 4 * lg,
+                                     Gp::make(o[0] + eb * qs[I][0], o[1] + eb * qs[I][1], o[2] + eb * qs[I][2],
+                                              o[3] + eb * qs[I][3]));
+                        }
                     }
                 }
+                __syncthreads();
+
+                // step 3: S <- e^{b_C} S + K^T (U e^{b_C - b})
+                {
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    const float4 be = *reinterpret_cast<const float4 *>(&sBeta[cur][16 * I + 4 * lg]);
-                    const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
-                    const Op *vr = sV + (16 * I + 4 * lg) * LDV + vloc;
-                    f32x4 y;
-                    y[0] = be.x * (to_f32(vr[0]) - eb.x * ks[I][0]);
-                    y[1] = be.y * (to_f32(vr[LDV]) - eb.y * ks[I][1]);
-                    y[2] = be.z * (to_f32(vr[2 * LDV]) - eb.z * ks[I][2]);
-                    y[3] = be.w * (to_f32(vr[3 * LDV]) - eb.w * ks[I][3]);
-                    yb[I] = Gp::make(y);
+                    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) st[cb][i] *= decay;
+#pragma unroll
+                        for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
+                            mma32(st[cb], kt_group<KSW>(sK[kc], LDK, 16 * s2, 16 * cb, lane),
+                                  kt_group<KSW>(sK[kc], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
+                        if constexpr (NB % 2 == 1) mma16(st[cb], kt_group<KSW>(sK[kc], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
+                    }
+                    publish_s0();   // HO: entering state of chunk c+1
                 }
+                stage(c);
+                __syncthreads();
             }
-            stage_k(c);
-            __syncthreads();
+        } else {
+            f32x16 oqs = {};   // HO output jobs: S0 Q_I^T of the current chunk and e^{b_t}
+            float oeb = 0.f;
+            for (int c = 0; c < nchunks; ++c) {
+                const int cur = c & 1, nxt = cur ^ 1;
+                const int kn = (c + 1) % 3;   // K buffer of chunk c+1
+                const bool has_next = c + 1 < nchunks;
 
-            // step 2: U = T Y and (not HO) the outputs of chunk c
-            G4 usb[NB];   // U diag(e^{b_C - b}) for the state update
-            float decay;
-            {
-                decay = sDecay[cur];
-                G4 ub[NB];
-#pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    f32x4 u = zero4();
-                    tile_mma_lr_n<NB>(u, sT + 16 * I * LDC, LDC, yb, I + 1, lane);
-                    ub[I] = Gp::make(u);
-                    // HO: U^T for the output jobs (rows = values, four tokens per write)
-                    if constexpr (HO) st_group(sUT + vloc * LDU + 16 * I + 4 * lg, ub[I]);
-                    const float4 ec = *reinterpret_cast<const float4 *>(&sEBC[cur][16 * I + 4 * lg]);
-                    usb[I] = Gp::make(u[0] * ec.x, u[1] * ec.y, u[2] * ec.z, u[3] * ec.w);
-                }
+                // step 1: the scores of chunk c+1 (only its K K^T tiles with 16x16
+                // tiles); without HO the staged outputs of chunk c-1 leave
                 if constexpr (!HO) {
-#pragma unroll
-                    for (int I = 0; I < NB; ++I) {
-                        // O^T = U^T P^T: lane holds values 16*wave + 4*lg..+3 of token 16 I + lr
-                        f32x4 o = zero4();
-                        tile_mma_rl_n<NB>(o, ub, sP[cur] + 16 * I * LDC, LDC, I + 1, lane);
-                        const float eb = sEB[cur][16 * I + lr];
-                        st_group(sO + (16 * I + lr) * LDV + 16 * wave + 4 * lg,
-                                 Gp::make(o[0] + eb * qs[I][0], o[1] + eb * qs[I][1], o[2] + eb * qs[I][2],
-                                          o[3] + eb * qs[I][3]));
+                    if (c > 0) copy_out(c - 1);
+                }
+                if constexpr (S32) {
+                    if (has_next && hw < NJ32) {
+                        // the score jobs bound step 1: raised issue priority
+                        __builtin_amdgcn_s_setprio(1);
+                        score_job32(nxt, kn, hw);
+                        __builtin_amdgcn_s_setprio(0);
                     }
+                } else {
+                    if (has_next) score_tiles(nxt, kn, true, WS, NHW);
                 }
-            }
-            __syncthreads();
+                __syncthreads();
 
-            // step 3: S <- e^{b_C} S + K^T (U e^{b_C - b})
-            {
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) st[cb][i] *= decay;
-#pragma unroll
-                    for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
-                        mma32(st[cb], kt_group<KSW>(sK[kc], LDK, 16 * s2, 16 * cb, lane),
-                              kt_group<KSW>(sK[kc], LDK, 16 * s2 + 16, 16 * cb, lane), usb[s2], usb[s2 + 1]);
-                    if constexpr (NB % 2 == 1) mma16(st[cb], kt_group<KSW>(sK[kc], LDK, 16 * (NB - 1), 16 * cb, lane), usb[NB - 1]);
+                // step 2: one wave per diagonal block of chunk c+1's inverse; with 16x16
+                // tiles, the other helpers: its Q K^T tiles; HO: S0 Q^T of chunk c
+                if (has_next) {
+                    if (hw < NB) diag_block(hw);
+                    else if constexpr (!S32) score_tiles(nxt, kn, false, WS + NB, NHW - NB);
                 }
-                publish_s0();   // HO: entering state of chunk c+1
-            }
-            stage(c);
-            __syncthreads();
-        }
-    } else {
-        f32x16 oqs = {};   // HO output jobs: S0 Q_I^T of the current chunk and e^{b_t}
-        float oeb = 0.f;
-        for (int c = 0; c < nchunks; ++c) {
-            const int cur = c & 1, nxt = cur ^ 1;
-            const int kn = (c + 1) % 3;   // K buffer of chunk c+1
-            const bool has_next = c + 1 < nchunks;
+                if (HO && hw >= OJ0) qs_job(cur, hw - OJ0, oqs, oeb);
+                __syncthreads();
 
-            // step 1: the scores of chunk c+1 (only its K K^T tiles with 16x16
-            // tiles); without HO the staged outputs of chunk c-1 leave
-            if constexpr (!HO) {
-                if (c > 0) copy_out(c - 1);
-            }
-            if constexpr (S32) {
-                if (has_next && hw < NJ32) {
-                    // the score jobs bound step 1: raised issue priority
+                // step 3: first the staging (the loads it stores arrived during the
+                // previous chunk; the new loads then fly while the rest computes): V of
+                // chunk c+1 over chunk c's, chunk c+2's gate values -> gate buffer cur
+                // and its Q and K into buffers no step reads any more (Q of chunk c, K
+                // of chunk c-1), then the loads of V(c+2) and Q, K(c+3).  Then the
+                // off-diagonal inverse of chunk c+1 (over chunk c's T, last read in
+                // step 2) and, HO, the outputs of chunk c.
+                stage(c);
+                if (has_next) {
+                    // the off-diagonal inverse is the longest task of the step: raised
+                    // issue priority over the waves it shares a SIMD with
                     __builtin_amdgcn_s_setprio(1);
-                    score_job32(nxt, kn, hw);
+                    offdiag(WS, NHW);
                     __builtin_amdgcn_s_setprio(0);
                 }
-            } else {
-                if (has_next) score_tiles(nxt, kn, true, WS, NHW);
+                if (HO && hw >= OJ0) out_job(c, cur, hw - OJ0, oqs, oeb);
+                __syncthreads();
             }
-            __syncthreads();
-
-            // step 2: one wave per diagonal block of chunk c+1's inverse; with 16x16
-            // tiles, the other helpers: its Q K^T tiles; HO: S0 Q^T of chunk c
-            if (has_next) {
-                if (hw < NB) diag_block(hw);
-                else if constexpr (!S32) score_tiles(nxt, kn, false, WS + NB, NHW - NB);
+            if constexpr (!HO) {
+                copy_out(clast);
             }
-            if (HO && hw >= OJ0) qs_job(cur, hw - OJ0, oqs, oeb);
-            __syncthreads();
-
-            // step 3: first the staging (the loads it stores arrived during the
-            // previous chunk; the new loads then fly while the rest computes): V of
-            // chunk c+1 over chunk c's, chunk c+2's gate values -> gate buffer cur
-            // and its Q and K into buffers no step reads any more (Q of chunk c, K
-            // of chunk c-1), then the loads of V(c+2) and Q, K(c+3).  Then the
-            // off-diagonal inverse of chunk c+1 (over chunk c's T, last read in
-            // step 2) and, HO, the outputs of chunk c.
-            stage(c);
-            if (has_next) {
-                // the off-diagonal inverse is the longest task of the step: raised
-                // issue priority over the waves it shares a SIMD with
-                __builtin_amdgcn_s_setprio(1);
-                offdiag(WS, NHW);
-                __builtin_amdgcn_s_setprio(0);
-            }
-            if (HO && hw >= OJ0) out_job(c, cur, hw - OJ0, oqs, oeb);
-            __syncthreads();
-        }
-        if constexpr (!HO) {
-            if (nchunks > 0) copy_out(nchunks - 1);
         }
     }
 
