@@ -79,6 +79,21 @@ struct TilePrefetch {
     }
 };
 
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at LDS byte address lds_base + 16 l, whatever global
+// address each lane gives; lds_base must be wave-uniform.  It is issued from
+// inline assembly, so the compiler neither waits for it nor counts it: the
+// issuing wave waits for it (s_waitcnt on the vector-memory counter) before
+// the barrier that hands the tile to its readers.
+__device__ __forceinline__ void lds_dma16(const void *src, unsigned lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+}
+// LDS byte address of a __shared__ object (the low half of its generic address)
+template <class T>
+__device__ __forceinline__ unsigned lds_addr(const T *p) {
+    return static_cast<unsigned>(reinterpret_cast<uintptr_t>(p));
+}
+
 // Workgroup -> (head, value block).  The dispatcher deals workgroups to the
 // 8 XCDs round robin (workgroup i runs on XCD i % 8); when the head count is
 // a multiple of 8 the value blocks of one head are given ids that differ by

@@ -160,7 +160,17 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // K: with two or more state waves they stage it alone, in step 1, where they
     // wait for the score jobs anyway (chunk c+2's K goes to the buffer chunk
     // c-1's used, free for the whole of chunk c)
+    // bfloat16: they fill the K tile by direct global->LDS loads (no registers,
+    // no LDS write instructions), in the layout above: 16-byte slot s of the
+    // tile (LDK/8 slots a row, the last two padding) receives the column chunk
+    // of its row that the swap puts there; rows past the end of the sequence
+    // re-read its last row (their solve rows and columns carry beta = 0 and
+    // their scores are masked).  The loads of chunk c+2 are issued at the start
+    // of chunk c and waited for before its last barrier.
     constexpr bool KSTATE = WS >= 2;
+    constexpr int KRS = LDK * (int)sizeof(Op) / 16;   // 16-byte slots per K tile row
+    constexpr int KNI = C * KRS / 64;                  // direct loads per K tile
+    constexpr bool KDMA = KSTATE && sizeof(Op) == 2 && (C * KRS) % 64 == 0;
     constexpr int KTHR = KSTATE ? WS * 64 : NTHR;
     TilePrefetch<C, DK, NTHR, IO> pq;
     TilePrefetch<C, DK, KTHR, IO> pk;
@@ -186,6 +196,18 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     auto store_q = [&](int buf) { pq.template store<KSW>(sQ[buf], LDK, tid); };
     auto store_k = [&](int kbuf) { pk.template store<KSW>(sK[kbuf], LDK, tid); };
     auto store_v = [&]() { pv.store(sV, LDV, tid); };
+    auto dma_k = [&](int c, int kbuf) {   // KDMA, state waves
+        const int n = rows(c);
+        const IO *src0 = kh + static_cast<size_t>(c * C) * DK;
+        const unsigned base = lds_addr(sK[kbuf]);
+#pragma unroll
+        for (int j = 0; j < KNI; ++j) {
+            if (j % WS != wave) continue;
+            const int slot = 64 * j + lane, row = slot / KRS, pc = slot % KRS;
+            const int lc = pc < DK / 8 ? pc ^ (KSW / 8 * ((row >> 3) & 1)) : 0;
+            lds_dma16(src0 + (row < n ? row : n - 1) * DK + 8 * lc, __builtin_amdgcn_readfirstlane(base + 1024 * j));
+        }
+    };
     // SCAN_WAVE: cumulative log2-gates of the staged chunk c into buffer `buf`
     // (b and every factor below in base 2: e^{b_t - b_j} = 2^{b2_t - b2_j})
     auto scan = [&](int buf, int c) {
@@ -417,7 +439,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // end re-reads the last one and is never stored): every path through the
     // loop then issues the same loads in the same order, and the compiler's
     // wait for one tile covers that tile alone, not the loads issued after it.
-    const bool k_stager = !KSTATE || state_wave;
+    const bool k_stager = !KSTATE || (state_wave && !KDMA);   // register staging of K
     const int clast = nchunks - 1;
     auto stage = [&](int c) {
         if (c + 1 < nchunks) store_v();
@@ -430,9 +452,12 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         load_q(min(c + 3, clast));
         if constexpr (!KSTATE) load_k(min(c + 3, clast));
     };
-    // KSTATE, state waves, step 1: chunk c+2's K
+    // KSTATE, state waves, step 1: chunk c+2's K (KDMA: issued at the start of
+    // the step; registers: stored at its end, chunk c+3's loaded)
     auto stage_k = [&](int c) {
-        if constexpr (KSTATE) {
+        if constexpr (KDMA) {
+            if (c + 2 < nchunks) dma_k(c + 2, (c + 2) % 3);
+        } else if constexpr (KSTATE) {
             if (c + 2 < nchunks) store_k((c + 2) % 3);
             load_k(min(c + 3, clast));
         }
@@ -441,14 +466,17 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         load_q(0);
         if (k_stager) load_k(0);
         load_v(0);
+        if (KDMA && state_wave) dma_k(0, 0);
         store_q(0);
         if (k_stager) store_k(0);
         store_v();
         scan(0, 0);
         if (state_wave) publish_s0();
+        if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         load_q(min(1, clast));
         if (k_stager) load_k(min(1, clast));
+        if (KDMA && state_wave && nchunks > 1) dma_k(1, 1);
         if constexpr (S32) {
             if (wave < NJ32) score_job32(0, 0, wave);
         } else {
@@ -465,6 +493,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             if (k_stager) store_k(1);
             scan(1, 1);
         }
+        if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         __syncthreads();
         if (k_stager) load_k(min(2, clast));
         load_v(min(1, clast));
@@ -478,6 +507,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 const int cur = c & 1, kc = c % 3;
 
                 // step 1: K S0^T, Q S0^T and the solve's right-hand side Y of chunk c
+                if constexpr (KDMA) stage_k(c);
                 G4 yb[NB];
                 f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
                 {
@@ -518,7 +548,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                         yb[I] = Gp::make(y);
                     }
                 }
-                stage_k(c);
+                if constexpr (!KDMA) stage_k(c);
                 __syncthreads();
 
                 // step 2: U = T Y and (not HO) the outputs of chunk c
@@ -566,6 +596,9 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     }
                     publish_s0();   // HO: entering state of chunk c+1
                 }
+                // KDMA: chunk c+2's K tile has landed before this wave's last
+                // barrier of the chunk
+                if constexpr (KDMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
                 stage(c);
                 __syncthreads();
             }
