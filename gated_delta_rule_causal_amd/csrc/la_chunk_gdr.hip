@@ -66,13 +66,22 @@ __device__ __forceinline__ void tile_mma_qk(f32x4 &acc, const Op *x, const Op *y
 template <class Op, int DVB, int C>
 constexpr bool gdr_helper_outputs() { return sizeof(Op) == 2 && C % 32 == 0 && DVB == 32; }
 
+// The state waves read their value channels of the V tile with transposing
+// reads (four tokens of one channel per lane) when the tile is bfloat16 and
+// 32 channels wide; its rows are then 96 bytes apart, so the eight rows of a
+// half-wave read touch each bank once.
+template <class Op, int DVB>
+constexpr bool gdr_v_transposed() { return sizeof(Op) == 2 && DVB == 32; }
+template <class Op, int DVB>
+constexpr int gdr_ldv() { return gdr_v_transposed<Op, DVB>() ? DVB + 16 : DVB + 16 / (int)sizeof(Op); }
+
 template <class DT, int DK, int DVB, int C>
 constexpr int gdr_lds_bytes() {
     typedef typename OpOf<DT>::type Op;
     constexpr int PAD = 16 / sizeof(Op);
     constexpr int tail = gdr_helper_outputs<Op, DVB, C>() ? DVB * (DK + gdr_kpad<Op>()) + DVB * (C + PAD)
                                                           : C * (DVB + PAD);
-    return (5 * C * (DK + gdr_kpad<Op>()) + 3 * C * (C + PAD) + C * (DVB + PAD) + tail) * (int)sizeof(Op) +
+    return (5 * C * (DK + gdr_kpad<Op>()) + 3 * C * (C + PAD) + C * gdr_ldv<Op, DVB>() + tail) * (int)sizeof(Op) +
            C * (C + 4) * 4 + 2 * (4 * C + 1) * 4;
 }
 
@@ -92,6 +101,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     constexpr int KSW = gdr_kswap<Op>();
     constexpr int LDC = C + PAD;
     constexpr int LDV = DVB + PAD;
+    constexpr bool VTR = gdr_v_transposed<Op, DVB>();
+    constexpr int LDVV = gdr_ldv<Op, DVB>();   // row stride of the V tile
     constexpr int LDA = C + 4;
     constexpr int VE = 16 / sizeof(Op);
     constexpr int NLOW = NB * (NB + 1) / 2;
@@ -108,7 +119,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
 
     __shared__ __align__(16) Op sQ[2][C * LDK];
     __shared__ __align__(16) Op sK[3][C * LDK];    // chunk c in buffer c % 3
-    __shared__ __align__(16) Op sV[C * LDV];       // this block's value channels of chunk c (read in step 1)
+    __shared__ __align__(16) Op sV[C * LDVV];      // this block's value channels of chunk c (read in step 1)
     __shared__ __align__(16) Op sP[2][C * LDC];    // M o Gamma o Q K^T
     __shared__ __align__(16) Op sT[C * LDC];       // (I + A)^{-1}: chunk c+1's replaces chunk c's in step 3
     __shared__ __align__(16) Op sO[HO ? VE : C * LDV];     // output tile, staged for 16-byte stores
@@ -195,7 +206,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     auto load_v = [&](int c) { pv.load(vh + static_cast<size_t>(c * C) * p.d_v, p.d_v, rows(c), tid); };
     auto store_q = [&](int buf) { pq.template store<KSW>(sQ[buf], LDK, tid); };
     auto store_k = [&](int kbuf) { pk.template store<KSW>(sK[kbuf], LDK, tid); };
-    auto store_v = [&]() { pv.store(sV, LDV, tid); };
+    auto store_v = [&]() { pv.store(sV, LDVV, tid); };
     auto dma_k = [&](int c, int kbuf) {   // KDMA, state waves
         const int n = rows(c);
         const IO *src0 = kh + static_cast<size_t>(c * C) * DK;
@@ -539,12 +550,21 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     for (int I = 0; I < NB; ++I) {
                         const float4 be = *reinterpret_cast<const float4 *>(&sBeta[cur][16 * I + 4 * lg]);
                         const float4 eb = *reinterpret_cast<const float4 *>(&sEB[cur][16 * I + 4 * lg]);
-                        const Op *vr = sV + (16 * I + 4 * lg) * LDV + vloc;
+                        // v of tokens 16 I + 4 lg .. +3, this lane's channel
+                        float v4[4];
+                        if constexpr (VTR) {
+                            const uint2 w = kt_group<0>(sV, LDVV, 16 * I, 16 * wave, lane);
+                            v4[0] = lo_bf16(w.x); v4[1] = hi_bf16(w.x); v4[2] = lo_bf16(w.y); v4[3] = hi_bf16(w.y);
+                        } else {
+                            const Op *vr = sV + (16 * I + 4 * lg) * LDVV + vloc;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) v4[i] = to_f32(vr[i * LDVV]);
+                        }
                         f32x4 y;
-                        y[0] = be.x * (to_f32(vr[0]) - eb.x * ks[I][0]);
-                        y[1] = be.y * (to_f32(vr[LDV]) - eb.y * ks[I][1]);
-                        y[2] = be.z * (to_f32(vr[2 * LDV]) - eb.z * ks[I][2]);
-                        y[3] = be.w * (to_f32(vr[3 * LDV]) - eb.w * ks[I][3]);
+                        y[0] = be.x * (v4[0] - eb.x * ks[I][0]);
+                        y[1] = be.y * (v4[1] - eb.y * ks[I][1]);
+                        y[2] = be.z * (v4[2] - eb.z * ks[I][2]);
+                        y[3] = be.w * (v4[3] - eb.w * ks[I][3]);
                         yb[I] = Gp::make(y);
                     }
                 }
