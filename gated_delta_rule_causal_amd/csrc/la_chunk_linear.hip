@@ -314,27 +314,36 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         tot[J][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(run[i]), 16 * J + 15));
-                if (lane < NB + 1 + L::NRHO) {
-                    // per-chunk factors, one float4 per lane: E_J (lanes < NB), D, rho
-                    float e[4];
+                {
+                    // per-chunk factors E_J, D and rho_{J1 J0}: products of the block
+                    // totals, the same in every lane (no per-lane selection), written
+                    // by lane 0 as one float4 (four channels) per factor
+                    constexpr int NF = NB + 1 + L::NRHO;
+                    float fe[NF][4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float acc = 1.f;
 #pragma unroll
                         for (int J = 0; J < NB; ++J) {
-                            if (lane < NB) acc *= J < lane ? tot[J][i] : 1.f;            // E_lane
-                            else if (lane == NB) acc *= tot[J][i];                        // D
+                            fe[J][i] = acc;        // E_J: the blocks before J
+                            acc *= tot[J][i];
                         }
+                        fe[NB][i] = acc;           // D: all blocks
 #pragma unroll
                         for (int J1 = 2; J1 < NB; ++J1)
 #pragma unroll
-                            for (int J0 = 0; J0 + 2 <= J1; ++J0)
-                                if (lane == NB + 1 + rho_index(J1, J0))
+                            for (int J0 = 0; J0 + 2 <= J1; ++J0) {
+                                float r = 1.f;     // rho_{J1 J0}: the blocks strictly between
 #pragma unroll
-                                    for (int J = J0 + 1; J < J1; ++J) acc *= tot[J][i];   // rho_{J1 J0}
-                        e[i] = acc;
+                                for (int J = J0 + 1; J < J1; ++J) r *= tot[J][i];
+                                fe[NB + 1 + rho_index(J1, J0)][i] = r;
+                            }
                     }
-                    *reinterpret_cast<float4 *>(sE + lane * DK + c) = make_float4(e[0], e[1], e[2], e[3]);
+                    if (lane == 0) {
+#pragma unroll
+                        for (int f = 0; f < NF; ++f)
+                            *reinterpret_cast<float4 *>(sE + f * DK + c) = make_float4(fe[f][0], fe[f][1], fe[f][2], fe[f][3]);
+                    }
                 }
                 // Qhat = phi(q) R_t, kd = phi(k) / R_t, k~ = phi(k) prod_{t<s<=e_I} g_s
                 // = kd * (block product), and the state-update operand k~ times the
