@@ -91,16 +91,16 @@ __device__ __forceinline__ void tile_mma_rl_scaled(f32x4 &acc, const G *ag, cons
 }
 
 // Inclusive product over each 16-lane row of a wave: lane i of a row gets
-// x_0 * ... * x_i (DPP row shifts; sources outside the row read as 1).
-template <int CTRL>
-__device__ __forceinline__ float dpp_or_one(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
+// x_0 * ... * x_i within each 16-lane row (lane i of the row): four DPP row
+// shifts, each one v_mul_f32_dpp x, x[lane - k], x.  With the DPP bound
+// control clear, a lane whose source lies outside its row is not written and
+// keeps x, i.e. multiplies by 1.  (The s_nop covers the two wait states a DPP
+// read needs after a vector write of its source.)
 __device__ __forceinline__ float row_scan_mul(float x) {
-    x *= dpp_or_one<0x111>(x);   // row_shr:1
-    x *= dpp_or_one<0x112>(x);   // row_shr:2
-    x *= dpp_or_one<0x114>(x);   // row_shr:4
-    x *= dpp_or_one<0x118>(x);   // row_shr:8
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf" : "+v"(x));
     return x;
 }
 
