@@ -205,10 +205,14 @@ def main(argv=None):
     out = torch.empty((w.B, w.H, w.T, w.d_v), dtype=io_t, device="cuda")
     S_T = torch.empty((w.B, w.H, w.d_v, w.d_k), dtype=torch.float32, device="cuda")
     z_T = torch.empty((w.B, w.H, w.d_k), dtype=torch.float32, device="cuda") if w.variant == la.LA_NORMALIZED else None
+    desc = la.make_desc(w.variant, la.LA_BF16 if w.dtype == "bf16" else la.LA_F32, w.B, w.H, w.T, w.d_k, w.d_v,
+                        w.chunk, w.phi_kind)
+    ws_bytes = la.la_chunk_fwd_workspace(desc)   # allocated once, outside the timed steps
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda") if ws_bytes else None
 
     def chunk_step():
         la.la_chunk_fwd(d["q"], d["k"], d["v"], variant=w.variant, gate=d.get("gate"), beta=d.get("beta"),
-                        chunk=w.chunk, phi=w.phi_kind, out=out, S_T=S_T, z_T=z_T)
+                        chunk=w.chunk, phi=w.phi_kind, out=out, S_T=S_T, z_T=z_T, workspace=ws)
 
     wall, ms_avg, _ = time_launches(chunk_step, args.steps, args.warmup, stream)
     if not bool(torch.isfinite(out).all()) or not bool(torch.isfinite(S_T).all()):

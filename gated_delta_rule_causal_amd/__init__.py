@@ -72,13 +72,16 @@ def la_chunk_fwd_workspace(desc: LaDesc) -> int:
 
 
 def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, chunk=0,
-                 phi=None, out=None, S_T=None, z_T=None, return_state=True, stream=None):
+                 phi=None, out=None, S_T=None, z_T=None, return_state=True, workspace=None,
+                 stream=None):
     """Chunkwise-parallel forward (C: ``la_chunk_fwd``).
 
     q, k (B,H,T,d_k) and v (B,H,T,d_v) in float32 or bfloat16; gate / beta /
     S0 / z0 float32 as include/la.h describes.  Outputs that are not passed
     are allocated: out in q's dtype; S_T (and z_T for LA_NORMALIZED) float32
-    unless return_state is False.  Returns (out, S_T, z_T).
+    unless return_state is False.  `workspace`: a device tensor of at least
+    la_chunk_fwd_workspace() bytes, allocated here when not passed and
+    needed.  Returns (out, S_T, z_T).
     """
     lib = load()
     if q.dtype not in _DTYPES:
@@ -93,10 +96,13 @@ def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, ch
     if return_state and variant == LA_NORMALIZED and z_T is None:
         z_T = torch.empty((B, H, d_k), dtype=torch.float32, device=q.device)
     ws_bytes = int(lib.la_chunk_fwd_workspace(ctypes.byref(desc)))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    ws = workspace
+    if ws is None and ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_given = 0 if ws is None else ws.numel() * ws.element_size()
     check(lib.la_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                            _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_T), _ptr(z_T), _ptr(ws),
-                           ws_bytes, _stream(stream)))
+                           ws_given, _stream(stream)))
     return out, S_T, z_T
 
 

@@ -14,6 +14,12 @@ struct ChunkParams {
     void *out;
     float *S_T, *z_T;
     int T, d_v, n_vblk, n_heads;
+    // normalized linear attention over sequence segments (n_seg > 1): the
+    // workgroups of segment s start from slot 0 + ... + slot s of seg_state,
+    // [head][n_seg][d_v * d_k + d_k] float32 (slot 0: the initial state,
+    // slot s >= 1: the state increment of segment s - 1)
+    int seg_len = 0, n_seg = 1;
+    const float *seg_state = nullptr;
 };
 
 // Copy rows [0, n) of a D-wide row-major global tile (row stride `lds`

@@ -741,7 +741,6 @@ static hipError_t gdr_dk(const ChunkArgs &a) {
 
 hipError_t launch_chunk_linear(const ChunkArgs &a);
 hipError_t launch_chunk_gdr(const ChunkArgs &a);
-size_t chunk_workspace_bytes(const ChunkArgs &) { return 0; }
 hipError_t launch_chunk(const ChunkArgs &a) {
     return a.variant == LA_GATED_DELTA ? launch_chunk_gdr(a) : launch_chunk_linear(a);
 }

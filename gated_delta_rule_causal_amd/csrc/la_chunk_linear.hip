@@ -33,6 +33,8 @@
 // Work decomposition as in the delta-rule kernel: one workgroup per (b, h,
 // block of DVB value channels); wave w keeps the transposed state slice of
 // its 16 value channels in matrix-core accumulators across the sequence.
+#include <algorithm>
+
 #include "la_chunk_common.hpp"
 
 namespace la {
@@ -116,13 +118,14 @@ struct LinearLds {
     static constexpr int LDK = DK + PAD;
     static constexpr int LDC = C + PAD;
     static constexpr int LDG = DK + 4;
+    static constexpr int LDV = DVB + PAD;   // value tile, rows = tokens
     static constexpr int P_BYTES = C * LDC * (int)sizeof(Op);
     static constexpr int G_BYTES = GATED ? C * LDG * 4 : 0;
     static constexpr int PG_BYTES = P_BYTES > G_BYTES ? P_BYTES : G_BYTES;
     static constexpr int F_FLOATS = GATED ? (NB + 1 + NRHO) * DK : DK + C;
-    static constexpr int KT_ELEMS = GATED ? C * LDK : DK * LDC;   // state-update key operand
+    static constexpr int KT_ELEMS = GATED ? C * LDK : 8;   // gated: state-update key operand
     static constexpr int BYTES = (GATED ? 3 : 2) * C * LDK * (int)sizeof(Op) + KT_ELEMS * (int)sizeof(Op) +
-                                 DVB * LDC * (int)sizeof(Op) + PG_BYTES + F_FLOATS * 4;
+                                 C * LDV * (int)sizeof(Op) + PG_BYTES + F_FLOATS * 4;
 };
 
 template <bool GATED, int PHI, class DT, int DK, int DVB, int C, int NW>
@@ -136,7 +139,7 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     constexpr int NTHR = NW * 64;
     constexpr int NB = C / 16;
     constexpr int NCB = DK / 16;
-    constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG, LDV = L::LDV;
     constexpr int VE = 16 / sizeof(IO);                   // elements per 16-byte vector
     static_assert(C <= 64 && C % 16 == 0 && DK % 16 == 0 && DVB % 16 == 0 && WS <= NW, "tiling");
     static_assert(L::BYTES <= 160 * 1024, "LDS budget");
@@ -144,9 +147,8 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     __shared__ __align__(16) Op sQ[C * LDK];                 // phi(Q) | Qhat
     __shared__ __align__(16) Op sK[C * LDK];                 // phi(K) | k~ (off-diagonal reference)
     __shared__ __align__(16) Op sKd[GATED ? C * LDK : 8];    // kd (diagonal reference)
-    __shared__ __align__(16) Op sKt[L::KT_ELEMS];            // key operand of the state update:
-                                                             // gated [t][c], normalized [c][t]
-    __shared__ __align__(16) Op sVt[DVB * LDC];              // this block's values, [v][t]
+    __shared__ __align__(16) Op sKt[L::KT_ELEMS];            // gated: key operand of the state update, [t][c]
+    __shared__ __align__(16) Op sV[C * LDV];                 // this block's values, [t][v]
     __shared__ __align__(16) unsigned char sPG[L::PG_BYTES]; // gates (f32), then P
     __shared__ __align__(16) float sF[L::F_FLOATS];
     Op *sP = reinterpret_cast<Op *>(sPG);
@@ -160,11 +162,17 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     // the wave index is uniform: role branches compile to scalar branches
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
+    // the workgroup's segment of the sequence: the whole of it unless the
+    // normalized variant is split (n_seg > 1; see ChunkParams::seg_state)
+    const int nhb = p.n_heads * p.n_vblk;
+    const int seg = blockIdx.x / nhb;
     int bh, vb;
-    block_to_head(blockIdx.x, p.n_heads, p.n_vblk, bh, vb);
+    block_to_head(blockIdx.x - seg * nhb, p.n_heads, p.n_vblk, bh, vb);
+    const int tb = seg * p.seg_len;
+    const int Tn = p.n_seg > 1 ? min(p.seg_len, p.T - tb) : p.T;   // tokens of this workgroup
     const int vloc = 16 * wave + lr;
     const int vch = vb * DVB + vloc;
-    const size_t tok0 = static_cast<size_t>(bh) * p.T;
+    const size_t tok0 = static_cast<size_t>(bh) * p.T + tb;
     const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
     const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
     const IO *vh = static_cast<const IO *>(p.v) + tok0 * p.d_v + vb * DVB;
@@ -173,16 +181,35 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 
     f32x4 st[NCB];
     const size_t srow = (static_cast<size_t>(bh) * p.d_v + (wave < WS ? vch : 0)) * DK;
+    const size_t slot = static_cast<size_t>(p.d_v) * DK + DK;   // floats per seg_state slot
+    const float *segs = p.n_seg > 1 ? p.seg_state + static_cast<size_t>(bh) * p.n_seg * slot : nullptr;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         st[cb] = zero4();
-        if (p.S0 && wave < WS) {
+        if (p.n_seg > 1) {
+            // entering state of segment seg: the initial state plus the
+            // increments of the segments before it, added in order
+            if (wave < WS) {
+                for (int s2 = 0; s2 <= seg; ++s2) {
+                    const float4 s = *reinterpret_cast<const float4 *>(segs + s2 * slot + static_cast<size_t>(vch) * DK + 16 * cb + 4 * lg);
+                    st[cb] += f32x4{s.x, s.y, s.z, s.w};
+                }
+            }
+        } else if (p.S0 && wave < WS) {
             const float4 s = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
             st[cb] = f32x4{s.x, s.y, s.z, s.w};
         }
     }
     if constexpr (!GATED) {
-        for (int c = tid; c < DK; c += NTHR) sZ[c] = p.z0 ? p.z0[static_cast<size_t>(bh) * DK + c] : 0.f;
+        for (int c = tid; c < DK; c += NTHR) {
+            float z = 0.f;
+            if (p.n_seg > 1) {
+                for (int s2 = 0; s2 <= seg; ++s2) z += segs[s2 * slot + static_cast<size_t>(p.d_v) * DK + c];
+            } else if (p.z0) {
+                z = p.z0[static_cast<size_t>(bh) * DK + c];
+            }
+            sZ[c] = z;
+        }
     }
     // the entering state is in registers before any tile load is issued, so
     // the loop never waits on the global-memory counter for it
@@ -193,20 +220,20 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     TilePrefetch<C, DVB, NTHR, IO> pv;
     TilePrefetch<C, GATED ? DK : 4, NTHR, float> pgt;
     auto prefetch = [&](int c0) {
-        const int n = min(C, p.T - c0);
+        const int n = min(C, Tn - c0);
         pq.load(qh + static_cast<size_t>(c0) * DK, DK, n, tid);
         pk.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
         pv.load(vh + static_cast<size_t>(c0) * p.d_v, p.d_v, n, tid);
         if constexpr (GATED) pgt.load(gh + static_cast<size_t>(c0) * DK, DK, n, tid);
     };
-    if (p.T > 0) prefetch(0);
+    if (Tn > 0) prefetch(0);
 
     // The state waves keep a chunk's outputs in registers and store them after
     // the next chunk's commit: the commit's wait on the global-memory counter
     // (for the staged loads) then never waits for just-issued output stores.
     f32x4 ob[NB];
     auto store_outputs = [&](int oc0) {
-        const int on = min(C, p.T - oc0);
+        const int on = min(C, Tn - oc0);
 #pragma unroll
         for (int I = 0; I < NB; ++I) {
             const int t = 16 * I + lr;
@@ -214,32 +241,14 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
         }
     };
 
-    for (int c0 = 0; c0 < p.T; c0 += C) {
-        const int n = min(C, p.T - c0);
+    for (int c0 = 0; c0 < Tn; c0 += C) {
+        const int n = min(C, Tn - c0);
 
-        // ---- commit the staged chunk.  Values transposed; queries/keys raw
-        // (gated) or with phi applied and keys also transposed (normalized);
-        // gates as float32 with padded tokens set to 1 (no decay).
-#pragma unroll
-        for (int i = 0; i < pv.PER; ++i) {
-            const int e = tid + i * NTHR;
-            if (pv.TOTAL % NTHR != 0 && e >= pv.TOTAL) continue;
-            const int t = e / pv.VPR, v = (e % pv.VPR) * VE;
-            const uint4 w = pv.r[i];
-            if constexpr (VE == 8) {
-                const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sVt[(v + 2 * j) * LDC + t] = static_cast<bf16_t>(u[j] & 0xffffu);
-                    sVt[(v + 2 * j + 1) * LDC + t] = static_cast<bf16_t>(u[j] >> 16);
-                }
-            } else {
-                sVt[(v + 0) * LDC + t] = __uint_as_float(w.x);
-                sVt[(v + 1) * LDC + t] = __uint_as_float(w.y);
-                sVt[(v + 2) * LDC + t] = __uint_as_float(w.z);
-                sVt[(v + 3) * LDC + t] = __uint_as_float(w.w);
-            }
-        }
+        // ---- commit the staged chunk.  Values as they are (the products that
+        // contract over tokens read them transposed); queries/keys raw (gated)
+        // or with phi applied (normalized); gates as float32 with padded tokens
+        // set to 1 (no decay).
+        pv.store(sV, LDV, tid);
         if constexpr (!GATED) {
 #pragma unroll
             for (int i = 0; i < pq.PER; ++i) {
@@ -261,13 +270,16 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                     xk[2] = __uint_as_float(b.z); xk[3] = __uint_as_float(b.w);
                 }
                 const bool on = t < n;   // padded tokens carry no feature (phi(0) would be 1)
+                float fq[8], fk[8];
 #pragma unroll
                 for (int j = 0; j < VE; ++j) {
-                    const float fq = on ? apply_phi<PHI>(xq[j]) : 0.f;
-                    const float fk = on ? apply_phi<PHI>(xk[j]) : 0.f;
-                    from_f32(sQ[t * LDK + c + j], fq);
-                    from_f32(sK[t * LDK + c + j], fk);
-                    from_f32(sKt[(c + j) * LDC + t], fk);
+                    fq[j] = on ? apply_phi<PHI>(xq[j]) : 0.f;
+                    fk[j] = on ? apply_phi<PHI>(xk[j]) : 0.f;
+                }
+#pragma unroll
+                for (int j = 0; j < VE; j += 4) {
+                    st_group(sQ + t * LDK + c + j, Gp::make(fq[j], fq[j + 1], fq[j + 2], fq[j + 3]));
+                    st_group(sK + t * LDK + c + j, Gp::make(fk[j], fk[j + 1], fk[j + 2], fk[j + 3]));
                 }
             }
         } else {
@@ -285,7 +297,7 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
         }
         __syncthreads();
         if (wave < WS && c0 > 0) store_outputs(c0 - C);
-        if (c0 + C < p.T) prefetch(c0 + C);
+        if (c0 + C < Tn) prefetch(c0 + C);
 
         if constexpr (GATED) {
             // ---- gate factors.  A wave takes four key channels of every token of
@@ -415,7 +427,7 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
             for (int c = tid; c < DK; c += NTHR) {
                 float s = 0.f;
 #pragma unroll 8
-                for (int t = 0; t < C; ++t) s += to_f32(sKt[c * LDC + t]);
+                for (int t = 0; t < C; ++t) s += to_f32(sK[t * LDK + c]);
                 sZ[c] += s;
             }
         }
@@ -436,7 +448,13 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                 } else {
                     tile_mma_rl_n<NCB>(o, sb, sQ + 16 * I * LDK, LDK, NCB, lane);
                 }
-                tile_mma_ll<C>(o, sVt + 16 * wave * LDC, LDC, sP + 16 * I * LDC, LDC, lane);
+                // + V^T P^T: V^T by transposing reads of the value tile
+                const Op *prow = sP + (16 * I + lr) * LDC + 4 * lg;
+#pragma unroll
+                for (int t0 = 0; t0 + 32 <= C; t0 += 32)
+                    mma32(o, kt_group<0>(sV, LDV, t0, 16 * wave, lane), kt_group<0>(sV, LDV, t0 + 16, 16 * wave, lane),
+                          ld_group(prow + t0), ld_group(prow + t0 + 16));
+                if constexpr (C % 32 == 16) mma16(o, kt_group<0>(sV, LDV, C - 16, 16 * wave, lane), ld_group(prow + C - 16));
                 if constexpr (!GATED) {
                     const float inv = 1.f / sDen[16 * I + lr];
 #pragma unroll
@@ -450,40 +468,191 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 #pragma unroll
                     for (int i = 0; i < 4; ++i) st[cb][i] *= sD[16 * cb + 4 * lg + i];
                 }
-                if constexpr (GATED) {
-                    // K^T from the natural-layout operand tile by transposing reads
-                    const Op *vrow = sVt + (16 * wave + lr) * LDC + 4 * lg;
+                // S^T += K^T V (gated: the scaled key operand): both from the
+                // token-major tiles by transposing reads
+                const Op *kt = GATED ? sKt : sK;
 #pragma unroll
-                    for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
-                        mma32(st[cb], kt_group<0>(sKt, LDK, 16 * s2, 16 * cb, lane),
-                              kt_group<0>(sKt, LDK, 16 * s2 + 16, 16 * cb, lane), ld_group(vrow + 16 * s2),
-                              ld_group(vrow + 16 * s2 + 16));
-                    if constexpr (NB % 2 == 1)
-                        mma16(st[cb], kt_group<0>(sKt, LDK, 16 * (NB - 1), 16 * cb, lane), ld_group(vrow + 16 * (NB - 1)));
-                } else {
-                    tile_mma_ll<C>(st[cb], sKt + 16 * cb * LDC, LDC, sVt + 16 * wave * LDC, LDC, lane);
-                }
+                for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
+                    mma32(st[cb], kt_group<0>(kt, LDK, 16 * s2, 16 * cb, lane),
+                          kt_group<0>(kt, LDK, 16 * s2 + 16, 16 * cb, lane), kt_group<0>(sV, LDV, 16 * s2, 16 * wave, lane),
+                          kt_group<0>(sV, LDV, 16 * s2 + 16, 16 * wave, lane));
+                if constexpr (NB % 2 == 1)
+                    mma16(st[cb], kt_group<0>(kt, LDK, 16 * (NB - 1), 16 * cb, lane),
+                          kt_group<0>(sV, LDV, 16 * (NB - 1), 16 * wave, lane));
             }
         }
         __syncthreads();
     }
 
-    if (wave < WS && p.T > 0) store_outputs(((p.T - 1) / C) * C);
-    if (p.S_T && wave < WS) {
+    if (wave < WS && Tn > 0) store_outputs(((Tn - 1) / C) * C);
+    const bool last_seg = seg == p.n_seg - 1;
+    if (p.S_T && wave < WS && last_seg) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
             *reinterpret_cast<float4 *>(p.S_T + srow + 16 * cb + 4 * lg) =
                 make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
     }
     if constexpr (!GATED) {
-        if (p.z_T && vb == 0)
+        if (p.z_T && vb == 0 && last_seg)
             for (int c = tid; c < DK; c += NTHR) p.z_T[static_cast<size_t>(bh) * DK + c] = sZ[c];
     }
+}
+
+// ------------------------------------------------------------------ segments
+// Normalized variant only: its state is a plain sum over the tokens
+// (S_C = S0 + V^T phiK, z_C = z0 + phiK^T 1), so the sequence can be cut into
+// segments that run concurrently, each entering with the initial state plus
+// the increments of the segments before it.  la_segment_state_kernel fills
+// the slots of ChunkParams::seg_state: slot 0 of a head is (S0, z0) (zeros
+// when absent), slot s >= 1 the increment of segment s - 1,
+//   dS = V^T phiK  (value rows x key columns),   dz = phiK^T 1,
+// over that segment's tokens, with phiK rounded to the operand type as the
+// chunk kernel rounds it.  Copying S0 here also lets S_T alias S0: every read
+// of S0 is done before the chunk kernel starts.  One workgroup per (head,
+// slot, 16-channel value block), four waves; wave w owns key tiles w, w+4, ..
+template <class DT, int DK, int C>
+__global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams p, float *ws) {
+    typedef typename DT::storage IO;
+    typedef typename OpOf<DT>::type Op;
+    constexpr int NKT = DK / 16;
+    constexpr int NT = (NKT + 3) / 4;            // key tiles per wave
+    constexpr int PAD = 16 / sizeof(Op);
+    constexpr int LDK = DK + PAD, LDV = 16 + PAD;
+    __shared__ __align__(16) Op sK[C * LDK];       // phi(K), rows = tokens
+    __shared__ __align__(16) Op sV[C * LDV];       // this block's 16 value channels
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int nvb = p.d_v / 16;
+    const int vb = blockIdx.x % nvb, s = (blockIdx.x / nvb) % p.n_seg, bh = blockIdx.x / (nvb * p.n_seg);
+    const size_t slot = static_cast<size_t>(p.d_v) * DK + DK;
+    float *dst = ws + (static_cast<size_t>(bh) * p.n_seg + s) * slot;
+    if (s == 0) {
+        for (int e = tid; e < 16 * DK; e += 256) {
+            const size_t o = static_cast<size_t>(16 * vb + e / DK) * DK + e % DK;
+            dst[o] = p.S0 ? p.S0[static_cast<size_t>(bh) * p.d_v * DK + o] : 0.f;
+        }
+        if (vb == 0)
+            for (int c = tid; c < DK; c += 256)
+                dst[static_cast<size_t>(p.d_v) * DK + c] = p.z0 ? p.z0[static_cast<size_t>(bh) * DK + c] : 0.f;
+        return;
+    }
+    const int tb = (s - 1) * p.seg_len;
+    const int Tn = min(p.seg_len, p.T - tb);
+    const IO *kh = static_cast<const IO *>(p.k) + (static_cast<size_t>(bh) * p.T + tb) * DK;
+    const IO *vh = static_cast<const IO *>(p.v) + (static_cast<size_t>(bh) * p.T + tb) * p.d_v + 16 * vb;
+    // the next chunk's rows are loaded into registers while this one is used
+    TilePrefetch<C, DK, 256, IO> pk;
+    TilePrefetch<C, 16, 256, IO> pv;
+    auto prefetch = [&](int c0) {
+        const int n = min(C, Tn - c0);
+        pk.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
+        pv.load(vh + static_cast<size_t>(c0) * p.d_v, p.d_v, n, tid);
+    };
+    // one staged 16-byte vector as floats (8 bf16 or 4 f32)
+    auto unpack = [](const uint4 &w, float (&x)[8]) {
+        if constexpr (sizeof(IO) == 2) {
+            x[0] = lo_bf16(w.x); x[1] = hi_bf16(w.x); x[2] = lo_bf16(w.y); x[3] = hi_bf16(w.y);
+            x[4] = lo_bf16(w.z); x[5] = hi_bf16(w.z); x[6] = lo_bf16(w.w); x[7] = hi_bf16(w.w);
+        } else {
+            x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y); x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+        }
+    };
+    f32x4 acc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = zero4();
+    float zs = 0.f;
+    prefetch(0);
+    for (int c0 = 0; c0 < Tn; c0 += C) {
+        const int n = min(C, Tn - c0);
+        // phi(K) and V rows of the chunk; rows past the segment end are zero
+#pragma unroll
+        for (int i = 0; i < pk.PER; ++i) {
+            const int e = tid + i * 256;
+            if (pk.TOTAL % 256 != 0 && e >= pk.TOTAL) continue;
+            const int t = e / pk.VPR, c = (e % pk.VPR) * pk.VE;
+            const bool ok = (pk.valid >> i) & 1u;
+            float x[8];
+            unpack(pk.r[i], x);
+#pragma unroll
+            for (int j = 0; j < pk.VE; ++j) from_f32(sK[t * LDK + c + j], ok ? phi_elu1(x[j]) : 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < pv.PER; ++i) {
+            const int e = tid + i * 256;
+            if (pv.TOTAL % 256 != 0 && e >= pv.TOTAL) continue;
+            const int t = e / pv.VPR, c = (e % pv.VPR) * pv.VE;
+            const bool ok = (pv.valid >> i) & 1u;
+            float x[8];
+            unpack(pv.r[i], x);
+#pragma unroll
+            for (int j = 0; j < pv.VE; ++j) from_f32(sV[t * LDV + c + j], ok ? x[j] : 0.f);
+        }
+        __syncthreads();
+        if (c0 + C < Tn) prefetch(c0 + C);
+        // dS tiles (value rows x key tile kt): both operands by transposing reads
+        // of the token-major tiles (contraction over the tokens)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+            const int kt = wave + 4 * i;
+            if (kt < NKT) {
+#pragma unroll
+                for (int t0 = 0; t0 + 32 <= C; t0 += 32)
+                    mma32(acc[i], kt_group<0>(sV, LDV, t0, 0, lane), kt_group<0>(sV, LDV, t0 + 16, 0, lane),
+                          kt_group<0>(sK, LDK, t0, 16 * kt, lane), kt_group<0>(sK, LDK, t0 + 16, 16 * kt, lane));
+                if constexpr (C % 32 == 16)
+                    mma16(acc[i], kt_group<0>(sV, LDV, C - 16, 0, lane), kt_group<0>(sK, LDK, C - 16, 16 * kt, lane));
+            }
+        }
+        if (vb == 0 && tid < DK)
+            for (int t = 0; t < n; ++t) zs += to_f32(sK[t * LDK + tid]);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const int kt = wave + 4 * i;
+        if (kt < NKT) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[static_cast<size_t>(16 * vb + 4 * lg + r) * DK + 16 * kt + lr] = acc[i][r];
+        }
+    }
+    if (vb == 0 && tid < DK) dst[static_cast<size_t>(p.d_v) * DK + tid] = zs;
 }
 
 // ------------------------------------------------------------------ dispatch
 
 constexpr int kLinearWaves = 8;   // waves per workgroup
+
+constexpr int kComputeUnits = 256;
+
+// Work split of the normalized variant: its state is a plain sum over the
+// tokens, so a sequence can run as concurrent segments.  When the heads (with
+// value blocks of up to 64 channels, the fewest duplicated state-independent
+// passes) give fewer workgroups than compute units, the sequence is cut into
+// enough segments for about one workgroup per unit, each at least two chunks
+// long (chunks are at least 16 tokens).  max_segments bounds the count for
+// any chunk length; it sizes the workspace.
+static int64_t linear_max_segments(const ChunkArgs &a) {
+    if (a.variant != LA_NORMALIZED || a.T <= 0) return 1;
+    const int64_t wgs = static_cast<int64_t>(a.B) * a.H * (a.d_v / std::min(a.d_v, 64));
+    if (wgs <= 0 || wgs >= kComputeUnits) return 1;
+    return std::max<int64_t>(1, std::min<int64_t>((kComputeUnits + wgs - 1) / wgs, (a.T + 15) / 16 / 2));
+}
+static int linear_segment_chunks(const ChunkArgs &a, int C) {   // chunks per segment
+    const int nchunks = (a.T + C - 1) / C;
+    const int64_t n = std::min<int64_t>(linear_max_segments(a), nchunks / 2);
+    return n < 2 ? nchunks : static_cast<int>((nchunks + n - 1) / n);
+}
+
+// Value-block width: with segments, up to 64 channels; otherwise the widest
+// block that still gives about one workgroup per compute unit.
+static int linear_value_block(const ChunkArgs &a) {
+    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
+    const int nchunks = (a.T + a.chunk - 1) / a.chunk;
+    if (linear_segment_chunks(a, a.chunk) < nchunks) return std::min(a.d_v, 64);
+    if (a.d_v >= 64 && heads * (a.d_v / 64) >= kComputeUnits) return 64;
+    if (a.d_v >= 32 && heads * (a.d_v / 32) >= kComputeUnits) return 32;
+    return 16;
+}
 
 template <bool GATED, int PHI, class DT, int DK, int DVB, int C>
 static hipError_t launch_linear_t(const ChunkArgs &a) {
@@ -491,7 +660,19 @@ static hipError_t launch_linear_t(const ChunkArgs &a) {
     p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.beta = nullptr; p.S0 = a.S0; p.z0 = a.z0;
     p.out = a.out; p.S_T = a.S_T; p.z_T = a.z_T;
     p.T = a.T; p.d_v = a.d_v; p.n_vblk = a.d_v / DVB; p.n_heads = a.B * a.H;
-    const int64_t blocks = static_cast<int64_t>(p.n_heads) * p.n_vblk;
+    if constexpr (!GATED) {
+        const int per = linear_segment_chunks(a, C);
+        const int nchunks = (a.T + C - 1) / C;
+        if (a.T > 0 && per < nchunks) {
+            p.seg_len = per * C;
+            p.n_seg = (nchunks + per - 1) / per;
+            p.seg_state = static_cast<const float *>(a.workspace);
+            const int64_t sblocks = static_cast<int64_t>(p.n_heads) * p.n_seg * (a.d_v / 16);
+            hipLaunchKernelGGL((la_segment_state_kernel<DT, DK, C>), dim3(static_cast<uint32_t>(sblocks)), dim3(256), 0,
+                               a.stream, p, static_cast<float *>(a.workspace));
+        }
+    }
+    const int64_t blocks = static_cast<int64_t>(p.n_heads) * p.n_vblk * p.n_seg;
     hipLaunchKernelGGL((linear_chunk_kernel<GATED, PHI, DT, DK, DVB, C, kLinearWaves>),
                        dim3(static_cast<uint32_t>(blocks)), dim3(kLinearWaves * 64), 0, a.stream, p);
     return hipGetLastError();
@@ -515,15 +696,12 @@ static hipError_t linear_chunk(const ChunkArgs &a) {
     return hipErrorInvalidValue;
 }
 
-// Value-block width: the widest block (fewest duplicated state-independent
-// passes per head) that still gives about one workgroup per compute unit.
-constexpr int kComputeUnits = 256;
-
 template <bool GATED, int PHI, class DT, int DK>
 static hipError_t linear_dvb(const ChunkArgs &a) {
-    const int64_t heads = static_cast<int64_t>(a.B) * a.H;
-    if (a.d_v >= 64 && heads * (a.d_v / 64) >= kComputeUnits) return linear_chunk<GATED, PHI, DT, DK, 64>(a);
-    if (a.d_v >= 32 && heads * (a.d_v / 32) >= kComputeUnits) return linear_chunk<GATED, PHI, DT, DK, 32>(a);
+    switch (linear_value_block(a)) {
+        case 64: return linear_chunk<GATED, PHI, DT, DK, 64>(a);
+        case 32: return linear_chunk<GATED, PHI, DT, DK, 32>(a);
+    }
     return linear_chunk<GATED, PHI, DT, DK, 16>(a);
 }
 
@@ -543,6 +721,14 @@ static hipError_t linear_variant(const ChunkArgs &a) {
     if (a.variant == LA_NORMALIZED) return linear_dk<false, LA_PHI_ELU1, DT>(a);
     if (a.phi == LA_PHI_ELU1) return linear_dk<true, LA_PHI_ELU1, DT>(a);
     return linear_dk<true, LA_PHI_IDENTITY, DT>(a);
+}
+
+// Workspace of the chunked forward: the segment slots of the normalized
+// variant (none for the other variants).
+size_t chunk_workspace_bytes(const ChunkArgs &a) {
+    const int64_t n = linear_max_segments(a);
+    if (n < 2) return 0;
+    return static_cast<size_t>(a.B) * a.H * n * (static_cast<size_t>(a.d_v) * a.d_k + a.d_k) * sizeof(float);
 }
 
 hipError_t launch_chunk_linear(const ChunkArgs &a) {

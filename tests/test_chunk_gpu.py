@@ -138,7 +138,9 @@ def test_decode_steps_equal_chunked_forward(name):
 def test_in_place_state_and_empty_sequence(name):
     variant, phi = VARIANTS[name]
     w = wl.variant_workload(variant, "bf16", 64, 64, phi=phi, seed=53)
-    inp = wl.chunk_inputs(w, B=1, H=2, T=70, S0_std=0.1, z0=True)
+    # T = 300: five chunks, so the normalized variant runs in two concurrent
+    # segments and S_T aliasing S0 crosses them
+    inp = wl.chunk_inputs(w, B=1, H=2, T=300, S0_std=0.1, z0=True)
     d = {k: dev(v) for k, v in inp.items()}
     ref = la.la_chunk_fwd(d["q"], d["k"], d["v"], variant=variant, gate=d.get("gate"), beta=d.get("beta"),
                           S0=d["S0"], z0=d.get("z0"), phi=phi)
@@ -154,6 +156,20 @@ def test_in_place_state_and_empty_sequence(name):
     assert o0.numel() == 0 and torch.equal(S0o, d["S0"])
     if z0o is not None:
         assert torch.equal(z0o, d["z0"])
+
+
+@pytest.mark.parametrize("B,H,T,d,chunk", [(1, 1, 64 * 20 + 7, 64, 64), (2, 3, 16 * 9, 32, 16),
+                                             (16, 16, 100, 16, 16)])
+def test_la_segment_counts(B, H, T, d, chunk):
+    """Normalized variant: many concurrent segments with a ragged last one (the
+    first two shapes), and enough heads for one unsegmented pass (the last)."""
+    w = wl.variant_workload(la.LA_NORMALIZED, "f32", d, d, chunk=chunk, phi=la.LA_PHI_ELU1, seed=67)
+    inp = wl.chunk_inputs(w, B=B, H=H, T=T, S0_std=0.1, z0=True)
+    nh = B * H
+    sample = None if nh <= 8 else [0, 1, nh // 2, nh - 1]
+    print("la segments", B, H, T, d, chunk, flush=True)
+    errs, _ = run_chunk(w, inp, chunk, sample=sample, B=B, H=H)
+    assert max(errs.values()) <= TOL["f32"], errs
 
 
 def test_chunk_is_deterministic():
