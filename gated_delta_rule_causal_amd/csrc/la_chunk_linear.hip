@@ -509,26 +509,28 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 // over that segment's tokens, with phiK rounded to the operand type as the
 // chunk kernel rounds it.  Copying S0 here also lets S_T alias S0: every read
 // of S0 is done before the chunk kernel starts.  One workgroup per (head,
-// slot, 16-channel value block), four waves; wave w owns key tiles w, w+4, ..
-template <class DT, int DK, int C>
+// slot, DVA-channel value block), four waves; the (value, key) 16x16 tiles of
+// the block are dealt to the waves round robin.
+template <class DT, int DK, int DVA, int C>
 __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams p, float *ws) {
     typedef typename DT::storage IO;
     typedef typename OpOf<DT>::type Op;
     constexpr int NKT = DK / 16;
-    constexpr int NT = (NKT + 3) / 4;            // key tiles per wave
+    constexpr int NTILE = (DVA / 16) * NKT;
+    constexpr int NT = (NTILE + 3) / 4;          // tiles per wave
     constexpr int PAD = 16 / sizeof(Op);
-    constexpr int LDK = DK + PAD, LDV = 16 + PAD;
+    constexpr int LDK = DK + PAD, LDV = DVA + PAD;
     __shared__ __align__(16) Op sK[C * LDK];       // phi(K), rows = tokens
-    __shared__ __align__(16) Op sV[C * LDV];       // this block's 16 value channels
+    __shared__ __align__(16) Op sV[C * LDV];       // this block's value channels
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
-    const int nvb = p.d_v / 16;
+    const int nvb = p.d_v / DVA;
     const int vb = blockIdx.x % nvb, s = (blockIdx.x / nvb) % p.n_seg, bh = blockIdx.x / (nvb * p.n_seg);
     const size_t slot = static_cast<size_t>(p.d_v) * DK + DK;
     float *dst = ws + (static_cast<size_t>(bh) * p.n_seg + s) * slot;
     if (s == 0) {
-        for (int e = tid; e < 16 * DK; e += 256) {
-            const size_t o = static_cast<size_t>(16 * vb + e / DK) * DK + e % DK;
+        for (int e = tid; e < DVA * DK; e += 256) {
+            const size_t o = static_cast<size_t>(DVA * vb + e / DK) * DK + e % DK;
             dst[o] = p.S0 ? p.S0[static_cast<size_t>(bh) * p.d_v * DK + o] : 0.f;
         }
         if (vb == 0)
@@ -539,10 +541,10 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
     const int tb = (s - 1) * p.seg_len;
     const int Tn = min(p.seg_len, p.T - tb);
     const IO *kh = static_cast<const IO *>(p.k) + (static_cast<size_t>(bh) * p.T + tb) * DK;
-    const IO *vh = static_cast<const IO *>(p.v) + (static_cast<size_t>(bh) * p.T + tb) * p.d_v + 16 * vb;
+    const IO *vh = static_cast<const IO *>(p.v) + (static_cast<size_t>(bh) * p.T + tb) * p.d_v + DVA * vb;
     // the next chunk's rows are loaded into registers while this one is used
     TilePrefetch<C, DK, 256, IO> pk;
-    TilePrefetch<C, 16, 256, IO> pv;
+    TilePrefetch<C, DVA, 256, IO> pv;
     auto prefetch = [&](int c0) {
         const int n = min(C, Tn - c0);
         pk.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
@@ -589,18 +591,18 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
         }
         __syncthreads();
         if (c0 + C < Tn) prefetch(c0 + C);
-        // dS tiles (value rows x key tile kt): both operands by transposing reads
-        // of the token-major tiles (contraction over the tokens)
+        // dS tiles (value tile vt x key tile kt): both operands by transposing
+        // reads of the token-major tiles (contraction over the tokens)
 #pragma unroll
         for (int i = 0; i < NT; ++i) {
-            const int kt = wave + 4 * i;
-            if (kt < NKT) {
+            const int tile = wave + 4 * i, vt = tile / NKT, kt = tile % NKT;
+            if (tile < NTILE) {
 #pragma unroll
                 for (int t0 = 0; t0 + 32 <= C; t0 += 32)
-                    mma32(acc[i], kt_group<0>(sV, LDV, t0, 0, lane), kt_group<0>(sV, LDV, t0 + 16, 0, lane),
+                    mma32(acc[i], kt_group<0>(sV, LDV, t0, 16 * vt, lane), kt_group<0>(sV, LDV, t0 + 16, 16 * vt, lane),
                           kt_group<0>(sK, LDK, t0, 16 * kt, lane), kt_group<0>(sK, LDK, t0 + 16, 16 * kt, lane));
                 if constexpr (C % 32 == 16)
-                    mma16(acc[i], kt_group<0>(sV, LDV, C - 16, 0, lane), kt_group<0>(sK, LDK, C - 16, 16 * kt, lane));
+                    mma16(acc[i], kt_group<0>(sV, LDV, C - 16, 16 * vt, lane), kt_group<0>(sK, LDK, C - 16, 16 * kt, lane));
             }
         }
         if (vb == 0 && tid < DK)
@@ -609,10 +611,11 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        const int kt = wave + 4 * i;
-        if (kt < NKT) {
+        const int tile = wave + 4 * i, vt = tile / NKT, kt = tile % NKT;
+        if (tile < NTILE) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[static_cast<size_t>(16 * vb + 4 * lg + r) * DK + 16 * kt + lr] = acc[i][r];
+            for (int r = 0; r < 4; ++r)
+                dst[static_cast<size_t>(DVA * vb + 16 * vt + 4 * lg + r) * DK + 16 * kt + lr] = acc[i][r];
         }
     }
     if (vb == 0 && tid < DK) dst[static_cast<size_t>(p.d_v) * DK + tid] = zs;
@@ -667,8 +670,8 @@ static hipError_t launch_linear_t(const ChunkArgs &a) {
             p.seg_len = per * C;
             p.n_seg = (nchunks + per - 1) / per;
             p.seg_state = static_cast<const float *>(a.workspace);
-            const int64_t sblocks = static_cast<int64_t>(p.n_heads) * p.n_seg * (a.d_v / 16);
-            hipLaunchKernelGGL((la_segment_state_kernel<DT, DK, C>), dim3(static_cast<uint32_t>(sblocks)), dim3(256), 0,
+            const int64_t sblocks = static_cast<int64_t>(p.n_heads) * p.n_seg * (a.d_v / DVB);
+            hipLaunchKernelGGL((la_segment_state_kernel<DT, DK, DVB, C>), dim3(static_cast<uint32_t>(sblocks)), dim3(256), 0,
                                a.stream, p, static_cast<float *>(a.workspace));
         }
     }
