@@ -186,25 +186,44 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         st[cb] = zero4();
-        if (p.n_seg > 1) {
-            // entering state of segment seg: the initial state plus the
-            // increments of the segments before it, added in order
-            if (wave < WS) {
-                for (int s2 = 0; s2 <= seg; ++s2) {
-                    const float4 s = *reinterpret_cast<const float4 *>(segs + s2 * slot + static_cast<size_t>(vch) * DK + 16 * cb + 4 * lg);
-                    st[cb] += f32x4{s.x, s.y, s.z, s.w};
-                }
-            }
-        } else if (p.S0 && wave < WS) {
+        if (p.n_seg == 1 && p.S0 && wave < WS) {
             const float4 s = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
             st[cb] = f32x4{s.x, s.y, s.z, s.w};
+        }
+    }
+    if (p.n_seg > 1 && wave < WS) {
+        // entering state of segment seg: the initial state plus the increments
+        // of the segments before it, added in order; the slots are read SB at
+        // a time, so that their loads are in flight together
+        constexpr int SB = NCB >= 8 ? 2 : 16 / NCB;
+        const float *col = segs + static_cast<size_t>(vch) * DK + 4 * lg;
+        for (int s0 = 0; s0 <= seg; s0 += SB) {
+            float4 v[SB][NCB];
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    v[j][cb] = *reinterpret_cast<const float4 *>(col + min(s0 + j, seg) * slot + 16 * cb);
+#pragma unroll
+            for (int j = 0; j < SB; ++j)
+                if (s0 + j <= seg)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) st[cb] += f32x4{v[j][cb].x, v[j][cb].y, v[j][cb].z, v[j][cb].w};
         }
     }
     if constexpr (!GATED) {
         for (int c = tid; c < DK; c += NTHR) {
             float z = 0.f;
             if (p.n_seg > 1) {
-                for (int s2 = 0; s2 <= seg; ++s2) z += segs[s2 * slot + static_cast<size_t>(p.d_v) * DK + c];
+                const float *zc = segs + static_cast<size_t>(p.d_v) * DK + c;
+                for (int s0 = 0; s0 <= seg; s0 += 8) {
+                    float v[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) v[j] = zc[min(s0 + j, seg) * slot];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (s0 + j <= seg) z += v[j];
+                }
             } else if (p.z0) {
                 z = p.z0[static_cast<size_t>(bh) * DK + c];
             }
@@ -515,6 +534,7 @@ template <class DT, int DK, int DVA, int C>
 __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams p, float *ws) {
     typedef typename DT::storage IO;
     typedef typename OpOf<DT>::type Op;
+    typedef Group<Op> Gp;
     constexpr int NKT = DK / 16;
     constexpr int NTILE = (DVA / 16) * NKT;
     constexpr int NT = (NTILE + 3) / 4;          // tiles per wave
@@ -522,6 +542,7 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
     constexpr int LDK = DK + PAD, LDV = DVA + PAD;
     __shared__ __align__(16) Op sK[C * LDK];       // phi(K), rows = tokens
     __shared__ __align__(16) Op sV[C * LDV];       // this block's value channels
+    __shared__ float sZp[256 * 8];                  // per-thread partial dz, reduced at the end
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int nvb = p.d_v / DVA;
@@ -542,13 +563,18 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
     const int Tn = min(p.seg_len, p.T - tb);
     const IO *kh = static_cast<const IO *>(p.k) + (static_cast<size_t>(bh) * p.T + tb) * DK;
     const IO *vh = static_cast<const IO *>(p.v) + (static_cast<size_t>(bh) * p.T + tb) * p.d_v + DVA * vb;
-    // the next chunk's rows are loaded into registers while this one is used
-    TilePrefetch<C, DK, 256, IO> pk;
-    TilePrefetch<C, DVA, 256, IO> pv;
-    auto prefetch = [&](int c0) {
+    // the rows of the next two chunks are loaded into registers (two sets,
+    // used alternately) while this one is used.  Every load is issued on
+    // every path (offsets past the end re-read the last chunk, which a
+    // chunk past the end then commits as zeros), so that the compiler's wait
+    // for one set never covers the other.
+    const int clast = ((Tn - 1) / C) * C;
+    TilePrefetch<C, DK, 256, IO> pk[2];
+    TilePrefetch<C, DVA, 256, IO> pv[2];
+    auto prefetch = [&](int c0, TilePrefetch<C, DK, 256, IO> &k, TilePrefetch<C, DVA, 256, IO> &v) {
         const int n = min(C, Tn - c0);
-        pk.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
-        pv.load(vh + static_cast<size_t>(c0) * p.d_v, p.d_v, n, tid);
+        k.load(kh + static_cast<size_t>(c0) * DK, DK, n, tid);
+        v.load(vh + static_cast<size_t>(c0) * p.d_v, p.d_v, n, tid);
     };
     // one staged 16-byte vector as floats (8 bf16 or 4 f32)
     auto unpack = [](const uint4 &w, float (&x)[8]) {
@@ -562,35 +588,46 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
     f32x4 acc[NT];
 #pragma unroll
     for (int i = 0; i < NT; ++i) acc[i] = zero4();
-    float zs = 0.f;
-    prefetch(0);
-    for (int c0 = 0; c0 < Tn; c0 += C) {
-        const int n = min(C, Tn - c0);
+    // dz: each thread sums phi(K) over the rows it commits, for the same
+    // VE channels in every chunk (256 is a multiple of the vectors per row)
+    float zp[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    auto chunk = [&](int c0, TilePrefetch<C, DK, 256, IO> &k, TilePrefetch<C, DVA, 256, IO> &v) {
+        const int n = min(C, Tn - c0);   // <= 0 past the end
         // phi(K) and V rows of the chunk; rows past the segment end are zero
 #pragma unroll
-        for (int i = 0; i < pk.PER; ++i) {
+        for (int i = 0; i < k.PER; ++i) {
             const int e = tid + i * 256;
-            if (pk.TOTAL % 256 != 0 && e >= pk.TOTAL) continue;
-            const int t = e / pk.VPR, c = (e % pk.VPR) * pk.VE;
-            const bool ok = (pk.valid >> i) & 1u;
+            if (k.TOTAL % 256 != 0 && e >= k.TOTAL) continue;
+            const int t = e / k.VPR, c = (e % k.VPR) * k.VE;
+            const bool ok = ((k.valid >> i) & 1u) && t < n;
             float x[8];
-            unpack(pk.r[i], x);
+            unpack(k.r[i], x);
 #pragma unroll
-            for (int j = 0; j < pk.VE; ++j) from_f32(sK[t * LDK + c + j], ok ? phi_elu1(x[j]) : 0.f);
+            for (int j = 0; j < k.VE; ++j) x[j] = ok ? phi_elu1(x[j]) : 0.f;
+#pragma unroll
+            for (int j = 0; j < k.VE; j += 4) {
+                const typename Gp::type g = Gp::make(x[j], x[j + 1], x[j + 2], x[j + 3]);
+                st_group(sK + t * LDK + c + j, g);
+                float r[4];
+                Gp::unpack(g, r);   // the rounded values the products use
+#pragma unroll
+                for (int u = 0; u < 4; ++u) zp[j + u] += r[u];
+            }
         }
 #pragma unroll
-        for (int i = 0; i < pv.PER; ++i) {
+        for (int i = 0; i < v.PER; ++i) {
             const int e = tid + i * 256;
-            if (pv.TOTAL % 256 != 0 && e >= pv.TOTAL) continue;
-            const int t = e / pv.VPR, c = (e % pv.VPR) * pv.VE;
-            const bool ok = (pv.valid >> i) & 1u;
+            if (v.TOTAL % 256 != 0 && e >= v.TOTAL) continue;
+            const int t = e / v.VPR, c = (e % v.VPR) * v.VE;
+            const bool ok = ((v.valid >> i) & 1u) && t < n;
             float x[8];
-            unpack(pv.r[i], x);
+            unpack(v.r[i], x);
 #pragma unroll
-            for (int j = 0; j < pv.VE; ++j) from_f32(sV[t * LDV + c + j], ok ? x[j] : 0.f);
+            for (int j = 0; j < v.VE; j += 4)
+                st_group(sV + t * LDV + c + j, Gp::make(ok ? x[j] : 0.f, ok ? x[j + 1] : 0.f, ok ? x[j + 2] : 0.f, ok ? x[j + 3] : 0.f));
         }
         __syncthreads();
-        if (c0 + C < Tn) prefetch(c0 + C);
+        prefetch(min(c0 + 2 * C, clast), k, v);
         // dS tiles (value tile vt x key tile kt): both operands by transposing
         // reads of the token-major tiles (contraction over the tokens)
 #pragma unroll
@@ -605,9 +642,13 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
                     mma16(acc[i], kt_group<0>(sV, LDV, C - 16, 16 * vt, lane), kt_group<0>(sK, LDK, C - 16, 16 * kt, lane));
             }
         }
-        if (vb == 0 && tid < DK)
-            for (int t = 0; t < n; ++t) zs += to_f32(sK[t * LDK + tid]);
         __syncthreads();
+    };
+    prefetch(0, pk[0], pv[0]);
+    prefetch(min(C, clast), pk[1], pv[1]);
+    for (int c0 = 0; c0 < Tn; c0 += 2 * C) {
+        chunk(c0, pk[0], pv[0]);
+        chunk(c0 + C, pk[1], pv[1]);
     }
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -618,7 +659,19 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
                 dst[static_cast<size_t>(DVA * vb + 16 * vt + 4 * lg + r) * DK + 16 * kt + lr] = acc[i][r];
         }
     }
-    if (vb == 0 && tid < DK) dst[static_cast<size_t>(p.d_v) * DK + tid] = zs;
+    if (vb == 0) {
+        // dz[c]: the partials of the threads that committed channel c, in thread order
+        constexpr int VPR = DK / (16 / (int)sizeof(IO)), VE = 16 / (int)sizeof(IO);
+#pragma unroll
+        for (int j = 0; j < VE; ++j) sZp[j * 256 + tid] = zp[j];
+        __syncthreads();
+        if (tid < DK) {
+            const int g = tid / VE, j = tid % VE;   // threads g, g + VPR, ... hold channel tid
+            float z = 0.f;
+            for (int th = g; th < 256; th += VPR) z += sZp[j * 256 + th];
+            dst[static_cast<size_t>(p.d_v) * DK + tid] = z;
+        }
+    }
 }
 
 // ------------------------------------------------------------------ dispatch
