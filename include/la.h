@@ -102,7 +102,12 @@ typedef struct {
 
 /*
  * Bytes of device workspace la_chunk_fwd needs for `desc` (0 when none).
- * Returns 0 for an invalid descriptor as well; la_chunk_fwd reports it.
+ * Only LA_NORMALIZED uses one, when its heads alone cannot occupy the GPU:
+ * its state is a plain sum over the tokens, so the sequence then runs as
+ * concurrent segments whose state increments are staged in the workspace
+ * (one d_v x d_k + d_k float32 slot per head and segment).  The size depends
+ * on B, H, T, d_k and d_v only.  Returns 0 for an invalid descriptor as
+ * well; la_chunk_fwd reports it.
  */
 size_t la_chunk_fwd_workspace(const la_desc *desc);
 
@@ -132,7 +137,9 @@ size_t la_chunk_fwd_workspace(const la_desc *desc);
  *         z0.  Otherwise must be NULL.
  *   workspace, workspace_bytes
  *         caller-owned device scratch of at least la_chunk_fwd_workspace()
- *         bytes (may be NULL when that is 0).
+ *         bytes, 16-byte aligned, overlapping no other argument (may be NULL
+ *         when that is 0).  Its contents on entry do not matter; calls that
+ *         share one workspace must not run concurrently.
  *   stream  hipStream_t to run on.
  */
 la_status la_chunk_fwd(const la_desc *desc,

@@ -149,6 +149,33 @@ def test_workspace_query_of_invalid_desc_is_zero(lib):
     assert la.la_chunk_fwd_workspace(D(d_k=48)) == 0
 
 
+def test_workspace_sizes(lib):
+    # Only the normalized variant uses a workspace: one slot of d_v*d_k + d_k
+    # floats per head and segment, when the heads (value blocks of up to 64
+    # channels) give fewer workgroups than the 256 compute units.  The segment
+    # count is bounded by 256 / workgroups and by the 16-token chunks over two.
+    slot = lambda dk, dv: (dv * dk + dk) * 4  # noqa: E731
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=4, H=8, T=2048)) == 32 * 8 * slot(64, 64)
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=1, H=1, T=100, d_k=16, d_v=16)) == 3 * slot(16, 16)
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=16, H=16, T=2048)) == 0   # 256 heads
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=0)) == 0
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=31)) == 0                 # one 16-token chunk pair at most
+    assert la.la_chunk_fwd_workspace(D(la.LA_GATED, T=2048)) == 0
+    assert la.la_chunk_fwd_workspace(D(la.LA_GATED_DELTA, T=2048)) == 0
+
+
+def test_missing_workspace_is_rejected(lib):
+    d = D(la.LA_NORMALIZED, B=1, H=1, T=4096)
+    need = la.la_chunk_fwd_workspace(d)
+    assert need > 0
+    assert call_chunk(lib, d) == la.LA_EINVAL
+    assert "workspace" in la.la_last_error()
+    assert call_chunk(lib, d, ws=fake(8), ws_bytes=need - 1) == la.LA_EINVAL
+    # overlapping an input is rejected too
+    assert call_chunk(lib, d, ws=fake(0), ws_bytes=need) == la.LA_EINVAL
+    assert "overlaps" in la.la_last_error()
+
+
 def test_empty_problem_is_a_no_op(lib):
     # B*H == 0: valid and nothing to launch, so no HIP call happens
     assert call_chunk(lib, D(B=0), q=None, k=None, v=None, out=None, S_T=None,
