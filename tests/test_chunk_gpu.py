@@ -172,6 +172,19 @@ def test_la_segment_counts(B, H, T, d, chunk):
     assert max(errs.values()) <= TOL["f32"], errs
 
 
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("bf16", 128, 32), ("f32", 64, 64)])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 128, 129, 191, 192, 200])
+def test_gdr_chunk_counts(dtype, d, chunk, T):
+    """Delta rule at one to four chunks, whole and ragged: the prologue stages
+    up to three chunks ahead and the loop's staging re-reads the last chunk
+    when the ones ahead do not exist."""
+    w = wl.variant_workload(la.LA_GATED_DELTA, dtype, d, d, chunk=chunk, seed=71)
+    inp = wl.chunk_inputs(w, B=1, H=2, T=T, S0_std=0.1)
+    print("gdr chunk counts", dtype, d, chunk, T, flush=True)
+    errs, _ = run_chunk(w, inp, chunk, B=1, H=2)
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
 def test_chunk_is_deterministic():
     w = wl.WORKLOADS["gdr_bf16_b4h16t8192d128"]
     inp = wl.chunk_inputs(w, B=1, H=4, T=1000)
