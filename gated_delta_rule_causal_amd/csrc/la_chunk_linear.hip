@@ -517,6 +517,292 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     }
 }
 
+// ------------------------------------------------------------------ gated, pipelined
+// Gated linear attention with the commit of chunk c+1 overlapping the
+// state-dependent part of chunk c:
+//   step A  state waves (DVB/16, each owning the state slice of 16 value
+//           channels): the outputs of chunk c (kept in registers) and its
+//           state update; the other waves: commit chunk c+1's staged q, k, v
+//           and load chunk c+2's;
+//   step B  all waves: the gate factors of chunk c+1; then the state waves
+//           store chunk c's outputs, and every wave loads its gates of
+//           chunk c+2;
+//   step C  all waves: the scores of chunk c+1.
+// The raw q and V tiles are double-buffered (chunk c+1's are written while
+// chunk c's are read).  The gates never touch LDS: each lane loads the gates
+// of its token for exactly the channels its gate-factor passes handle.  The
+// arithmetic is the gated path of linear_chunk_kernel, term for term.
+template <class DT, int DK, int DVB, int C, int NW>
+struct GlaLds {
+    typedef typename OpOf<DT>::type Op;
+    static constexpr int NB = C / 16;
+    static constexpr int NRHO = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 0;
+    static constexpr int PAD = 16 / sizeof(Op);
+    static constexpr int LDK = DK + PAD, LDC = C + PAD, LDV = DVB + PAD;
+    static constexpr int F_FLOATS = (NB + 1 + NRHO) * DK;
+    static constexpr int BYTES = (5 * C * LDK + 2 * C * LDV + C * LDC) * (int)sizeof(Op) + F_FLOATS * 4;
+    static constexpr int WS = DVB / 16, NH = NW - WS;
+    static constexpr bool FITS = BYTES <= 160 * 1024 && NH >= 2;
+};
+
+template <int PHI, class DT, int DK, int DVB, int C, int NW>
+__global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParams p) {
+    typedef typename DT::storage IO;
+    typedef typename OpOf<DT>::type Op;
+    typedef Group<Op> Gp;
+    typedef typename Gp::type G4;
+    typedef GlaLds<DT, DK, DVB, C, NW> L;
+    constexpr int WS = L::WS, NH = L::NH;
+    constexpr int NB = C / 16, NCB = DK / 16;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDV = L::LDV;
+    constexpr int GI = (DK + 4 * NW - 1) / (4 * NW);   // gate-factor passes per wave and chunk
+    static_assert(L::FITS, "pipelined layout does not fit");
+
+    __shared__ __align__(16) Op sQ[2][C * LDK];    // raw q of the chunk being prepared, then Qhat
+    __shared__ __align__(16) Op sK[C * LDK];       // raw k, then k~
+    __shared__ __align__(16) Op sKd[C * LDK];      // kd (diagonal blocks)
+    __shared__ __align__(16) Op sKt[C * LDK];      // state-update key operand
+    __shared__ __align__(16) Op sV[2][C * LDV];    // values, [t][v]
+    __shared__ __align__(16) Op sP[C * LDC];       // scores
+    __shared__ __align__(16) float sF[L::F_FLOATS];   // E_J, D, rho
+    float *sE = sF, *sD = sF + NB * DK, *sRho = sF + (NB + 1) * DK;
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    const bool state_wave = wave < WS;
+    const int htid = tid - WS * 64;   // helper thread index (waves >= WS)
+    int bh, vb;
+    block_to_head(blockIdx.x, p.n_heads, p.n_vblk, bh, vb);
+    const int vloc = 16 * wave + lr;
+    const int vch = vb * DVB + vloc;
+    const size_t tok0 = static_cast<size_t>(bh) * p.T;
+    const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
+    const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
+    const IO *vh = static_cast<const IO *>(p.v) + tok0 * p.d_v + vb * DVB;
+    IO *oh = static_cast<IO *>(p.out) + tok0 * p.d_v;
+    const float *gh = p.gate + tok0 * DK;
+    const int nchunks = (p.T + C - 1) / C;
+    const int clast = nchunks - 1;
+    auto rows = [&](int c) { return min(C, p.T - c * C); };
+
+    f32x4 st[NCB];
+    const size_t srow = (static_cast<size_t>(bh) * p.d_v + (state_wave ? vch : 0)) * DK;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        st[cb] = zero4();
+        if (p.S0 && state_wave) {
+            const float4 s = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
+            st[cb] = f32x4{s.x, s.y, s.z, s.w};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // q, k, v (helpers) and the gates (every wave) two chunks ahead of the
+    // state part.  Every load is issued whether or not its chunk exists (a
+    // chunk past the end re-reads the last one and is never used), so the
+    // compiler's wait for one set never covers another.
+    TilePrefetch<C, DK, NH * 64, IO> pq, pk;
+    TilePrefetch<C, DVB, NH * 64, IO> pv;
+    float4 pg[GI];   // gates of token `lane`, channels 4 wave + 4 NW i .. +3
+    auto load_qkv = [&](int c) {
+        const int n = rows(c);
+        pq.load(qh + static_cast<size_t>(c * C) * DK, DK, n, htid);
+        pk.load(kh + static_cast<size_t>(c * C) * DK, DK, n, htid);
+        pv.load(vh + static_cast<size_t>(c * C) * p.d_v, p.d_v, n, htid);
+    };
+    auto load_gates = [&](int c) {
+        const int n = rows(c);
+        const float *g = gh + static_cast<size_t>(c * C + (lane < n ? lane : n - 1)) * DK + 4 * wave;
+#pragma unroll
+        for (int i = 0; i < GI; ++i)
+            if (4 * wave + 4 * NW * i < DK) pg[i] = *reinterpret_cast<const float4 *>(g + 4 * NW * i);
+    };
+    f32x4 ob[NB];   // state waves: outputs of chunk c, stored in step B
+    if (nchunks > 0) {
+        if (!state_wave) load_qkv(0);
+        load_gates(0);
+    }
+
+    for (int c = -1; c < nchunks && nchunks > 0; ++c) {
+        const int cur = c & 1, nb = (c + 1) & 1;   // raw-tile buffers of chunk c and chunk c+1
+        const bool prep = c + 1 < nchunks;          // chunk c+1 is prepared
+        const int n1 = prep ? rows(c + 1) : 0;
+
+        // ---- step A.  State waves: the outputs of chunk c (to registers) and
+        // its state update.  Helpers: commit chunk c+1, load chunk c+2.
+        if (state_wave) {
+            if (c >= 0) {
+                G4 sb[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    // O^T = (Qhat E_I) S0^T + V^T P^T: lane holds values 16*wave + 4*lg..+3
+                    // of token 16 I + lr
+                    f32x4 o = zero4();
+                    if (I == 0) tile_mma_rl_n<NCB>(o, sb, sQ[cur], LDK, NCB, lane);
+                    else tile_mma_rl_scaled<NCB>(o, sb, sQ[cur] + 16 * I * LDK, LDK, sE + I * DK, lane);
+                    const Op *prow = sP + (16 * I + lr) * LDC + 4 * lg;
+#pragma unroll
+                    for (int t0 = 0; t0 + 32 <= C; t0 += 32)
+                        mma32(o, kt_group<0>(sV[cur], LDV, t0, 16 * wave, lane),
+                              kt_group<0>(sV[cur], LDV, t0 + 16, 16 * wave, lane), ld_group(prow + t0),
+                              ld_group(prow + t0 + 16));
+                    if constexpr (C % 32 == 16)
+                        mma16(o, kt_group<0>(sV[cur], LDV, C - 16, 16 * wave, lane), ld_group(prow + C - 16));
+                    ob[I] = o;
+                }
+                // S^T <- S^T diag(D) + K~a^T V, both operands by transposing reads
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[cb][i] *= sD[16 * cb + 4 * lg + i];
+#pragma unroll
+                    for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
+                        mma32(st[cb], kt_group<0>(sKt, LDK, 16 * s2, 16 * cb, lane),
+                              kt_group<0>(sKt, LDK, 16 * s2 + 16, 16 * cb, lane),
+                              kt_group<0>(sV[cur], LDV, 16 * s2, 16 * wave, lane),
+                              kt_group<0>(sV[cur], LDV, 16 * s2 + 16, 16 * wave, lane));
+                    if constexpr (NB % 2 == 1)
+                        mma16(st[cb], kt_group<0>(sKt, LDK, 16 * (NB - 1), 16 * cb, lane),
+                              kt_group<0>(sV[cur], LDV, 16 * (NB - 1), 16 * wave, lane));
+                }
+            }
+        } else {
+            if (prep) {
+                pq.store(sQ[nb], LDK, htid);
+                pk.store(sK, LDK, htid);
+                pv.store(sV[nb], LDV, htid);
+            }
+            load_qkv(min(c + 2, clast));
+        }
+        __syncthreads();
+
+        // ---- step B.  All waves: the gate factors of chunk c+1 (lane = token,
+        // four channels per pass; the products along a 16-token block are
+        // 16-lane DPP row scans).  Then the state waves store chunk c's outputs
+        // and every wave loads its gates of chunk c+2.
+        if (prep) {
+            const int t = lane, I = t >> 4;
+            const bool in_tile = t < C, on = t < n1;
+#pragma unroll
+            for (int it = 0; it < GI; ++it) {
+                const int cc = 4 * wave + 4 * NW * it;
+                if (cc >= DK) break;   // uniform: the last pass covers fewer waves
+                float g[4] = {1.f, 1.f, 1.f, 1.f}, q[4] = {0.f, 0.f, 0.f, 0.f}, k[4] = {0.f, 0.f, 0.f, 0.f};
+                if (on) { g[0] = pg[it].x; g[1] = pg[it].y; g[2] = pg[it].z; g[3] = pg[it].w; }   // 1 past the end
+                if (in_tile) {
+                    Gp::unpack(ld_group(sQ[nb] + t * LDK + cc), q);
+                    Gp::unpack(ld_group(sK + t * LDK + cc), k);
+                }
+                float run[4], rinv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    run[i] = row_scan_mul(g[i]);   // R_t = prod_{16I <= s <= t} g_s
+                    rinv[i] = __builtin_amdgcn_rcpf(run[i]);
+                }
+                float tot[NB][4];   // whole-block products (uniform)
+#pragma unroll
+                for (int J = 0; J < NB; ++J)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        tot[J][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(run[i]), 16 * J + 15));
+                {
+                    // per-chunk factors E_J, D and rho_{J1 J0} (uniform), by lane 0
+                    constexpr int NF = NB + 1 + L::NRHO;
+                    float fe[NF][4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float acc = 1.f;
+#pragma unroll
+                        for (int J = 0; J < NB; ++J) {
+                            fe[J][i] = acc;
+                            acc *= tot[J][i];
+                        }
+                        fe[NB][i] = acc;
+#pragma unroll
+                        for (int J1 = 2; J1 < NB; ++J1)
+#pragma unroll
+                            for (int J0 = 0; J0 + 2 <= J1; ++J0) {
+                                float r = 1.f;
+#pragma unroll
+                                for (int J = J0 + 1; J < J1; ++J) r *= tot[J][i];
+                                fe[NB + 1 + rho_index(J1, J0)][i] = r;
+                            }
+                    }
+                    if (lane == 0) {
+#pragma unroll
+                        for (int f = 0; f < NF; ++f)
+                            *reinterpret_cast<float4 *>(sE + f * DK + cc) = make_float4(fe[f][0], fe[f][1], fe[f][2], fe[f][3]);
+                    }
+                }
+                float fq[4], fd[4], fk[4], fa[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float tb = tot[0][i], after = 1.f;
+#pragma unroll
+                    for (int J = 1; J < NB; ++J) {
+                        if (J == I) tb = tot[J][i];
+                        if (J > I) after *= tot[J][i];
+                    }
+                    fq[i] = on ? apply_phi<PHI>(q[i]) * run[i] : 0.f;
+                    fd[i] = on ? apply_phi<PHI>(k[i]) * rinv[i] : 0.f;
+                    fk[i] = fd[i] * tb;
+                    fa[i] = fk[i] * after;
+                }
+                if (in_tile) {
+                    st_group(sQ[nb] + t * LDK + cc, Gp::make(fq[0], fq[1], fq[2], fq[3]));
+                    st_group(sKd + t * LDK + cc, Gp::make(fd[0], fd[1], fd[2], fd[3]));
+                    st_group(sK + t * LDK + cc, Gp::make(fk[0], fk[1], fk[2], fk[3]));
+                    st_group(sKt + t * LDK + cc, Gp::make(fa[0], fa[1], fa[2], fa[3]));
+                }
+            }
+        }
+        if (state_wave && c >= 0) {
+            const int n = rows(c);
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                const int t = 16 * I + lr;
+                if (t < n)
+                    st_group(oh + static_cast<size_t>(c * C + t) * p.d_v + vb * DVB + 16 * wave + 4 * lg, Gp::make(ob[I]));
+            }
+        }
+        load_gates(min(c + 2, clast));
+        __syncthreads();
+
+        // ---- step C.  All waves: the scores of chunk c+1 (16x16 tiles, taken
+        // transposed so that a lane writes four consecutive columns of a row).
+        if (prep) {
+            for (int tt = wave; tt < NB * NB; tt += NW) {
+                const int I = tt / NB, J = tt % NB;
+                const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
+                if (J > I) {
+                    st_group(sP + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
+                    continue;
+                }
+                f32x4 acc = zero4();
+                if (J == I)
+                    tile_mma_ll<DK>(acc, sKd + 16 * J * LDK, LDK, sQ[nb] + 16 * I * LDK, LDK, lane);
+                else if (J == I - 1)
+                    tile_mma_ll<DK>(acc, sK + 16 * J * LDK, LDK, sQ[nb] + 16 * I * LDK, LDK, lane);
+                else
+                    tile_mma_ll_scaled<DK>(acc, sK + 16 * J * LDK, LDK, sRho + rho_index(I, J) * DK,
+                                           sQ[nb] + 16 * I * LDK, LDK, lane);
+                st_group(sP + t * LDC + j0, Gp::make(j0 <= t ? acc[0] : 0.f, j0 + 1 <= t ? acc[1] : 0.f,
+                                                     j0 + 2 <= t ? acc[2] : 0.f, j0 + 3 <= t ? acc[3] : 0.f));
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.S_T && state_wave) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            *reinterpret_cast<float4 *>(p.S_T + srow + 16 * cb + 4 * lg) =
+                make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
+    }
+}
+
 // ------------------------------------------------------------------ segments
 // Normalized variant only: its state is a plain sum over the tokens
 // (S_C = S0 + V^T phiK, z_C = z0 + phiK^T 1), so the sequence can be cut into
@@ -729,8 +1015,13 @@ static hipError_t launch_linear_t(const ChunkArgs &a) {
         }
     }
     const int64_t blocks = static_cast<int64_t>(p.n_heads) * p.n_vblk * p.n_seg;
-    hipLaunchKernelGGL((linear_chunk_kernel<GATED, PHI, DT, DK, DVB, C, kLinearWaves>),
-                       dim3(static_cast<uint32_t>(blocks)), dim3(kLinearWaves * 64), 0, a.stream, p);
+    if constexpr (GATED && GlaLds<DT, DK, DVB, C, kLinearWaves>::FITS) {
+        hipLaunchKernelGGL((gla_pipelined_kernel<PHI, DT, DK, DVB, C, kLinearWaves>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kLinearWaves * 64), 0, a.stream, p);
+    } else {
+        hipLaunchKernelGGL((linear_chunk_kernel<GATED, PHI, DT, DK, DVB, C, kLinearWaves>),
+                           dim3(static_cast<uint32_t>(blocks)), dim3(kLinearWaves * 64), 0, a.stream, p);
+    }
     return hipGetLastError();
 }
 
