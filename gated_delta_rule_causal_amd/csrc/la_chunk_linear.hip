@@ -92,6 +92,13 @@ __device__ __forceinline__ void tile_mma_rl_scaled(f32x4 &acc, const G *ag, cons
     if constexpr (NK % 2 == 1) mma16(acc, ag[NK - 1], scaled_group(br + 16 * (NK - 1), sr + 16 * (NK - 1)));
 }
 
+// DPP move with control CTRL on the rows in ROWMASK; lanes of the other rows
+// (and lanes whose source is invalid) read 1
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), CTRL, ROWMASK, 0xF, false));
+}
+
 // Inclusive product over each 16-lane row of a wave: lane i of a row gets
 // x_0 * ... * x_i within each 16-lane row (lane i of the row): four DPP row
 // shifts, each one v_mul_f32_dpp x, x[lane - k], x.  With the DPP bound
@@ -708,32 +715,34 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                     for (int i = 0; i < 4; ++i)
                         tot[J][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(run[i]), 16 * J + 15));
                 {
-                    // per-chunk factors E_J, D and rho_{J1 J0} (uniform), by lane 0
-                    constexpr int NF = NB + 1 + L::NRHO;
-                    float fe[NF][4];
+                    // per-chunk factors, from a scan across the block ends: after
+                    // two DPP row broadcasts lane t holds P_t = prod_{s <= t} g_s, so
+                    // E_J = P at lane 16J - 1 (J >= 1; E_0 = 1 is never read), D = P at
+                    // lane 63, and rho_{J1 J0} (blocks strictly between) is the block
+                    // total of lane 31 or 47, or their product.  Each value is written
+                    // by the lane that holds it.
+                    float pre[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        float acc = 1.f;
-#pragma unroll
-                        for (int J = 0; J < NB; ++J) {
-                            fe[J][i] = acc;
-                            acc *= tot[J][i];
-                        }
-                        fe[NB][i] = acc;
-#pragma unroll
-                        for (int J1 = 2; J1 < NB; ++J1)
-#pragma unroll
-                            for (int J0 = 0; J0 + 2 <= J1; ++J0) {
-                                float r = 1.f;
-#pragma unroll
-                                for (int J = J0 + 1; J < J1; ++J) r *= tot[J][i];
-                                fe[NB + 1 + rho_index(J1, J0)][i] = r;
-                            }
+                        pre[i] = run[i] * dpp_or_one<0x142, 0xA>(run[i]);   // rows 1, 3: last lane of the row before
+                        pre[i] *= dpp_or_one<0x143, 0xC>(pre[i]);       // rows 2, 3: lane 31's prefix
                     }
-                    if (lane == 0) {
+                    if ((lane & 15) == 15 && (lane >> 4) < NB) {
+                        const int J = lane >> 4;   // E_{J+1} for J < NB - 1, D for the last block
+                        *reinterpret_cast<float4 *>(sE + (J + 1) * DK + cc) = make_float4(pre[0], pre[1], pre[2], pre[3]);
+                    }
+                    if constexpr (NB == 4) {
+                        // rho_{2,0} = tot_1 (lane 31), rho_{3,1} = tot_2 and rho_{3,0} = tot_1 tot_2 (lane 47)
+                        if (lane == 31)
+                            *reinterpret_cast<float4 *>(sRho + rho_index(2, 0) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
+                        float t1[4];   // row 2: tot_1 (lane 31's row total)
 #pragma unroll
-                        for (int f = 0; f < NF; ++f)
-                            *reinterpret_cast<float4 *>(sE + f * DK + cc) = make_float4(fe[f][0], fe[f][1], fe[f][2], fe[f][3]);
+                        for (int i = 0; i < 4; ++i) t1[i] = dpp_or_one<0x142, 0x4>(run[i]);
+                        if (lane == 47) {
+                            *reinterpret_cast<float4 *>(sRho + rho_index(3, 1) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
+                            *reinterpret_cast<float4 *>(sRho + rho_index(3, 0) * DK + cc) =
+                                make_float4(t1[0] * run[0], t1[1] * run[1], t1[2] * run[2], t1[3] * run[3]);
+                        }
                     }
                 }
                 float fq[4], fd[4], fk[4], fa[4];
