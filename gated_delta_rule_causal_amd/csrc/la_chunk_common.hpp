@@ -94,6 +94,12 @@ struct TilePrefetch {
 __device__ __forceinline__ void lds_dma16(const void *src, unsigned lds_base) {
     asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
+// The same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
+// (global address = base + offset), so that a caller whose lane offsets do
+// not change between calls keeps them in registers and moves only the base.
+__device__ __forceinline__ void lds_dma16(const void *base, unsigned offset, unsigned lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base), "{m0}"(lds_base) : "memory");
+}
 // LDS byte address of a __shared__ object (the low half of its generic address)
 template <class T>
 __device__ __forceinline__ unsigned lds_addr(const T *p) {

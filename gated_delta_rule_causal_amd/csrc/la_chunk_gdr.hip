@@ -207,16 +207,38 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     auto store_q = [&](int buf) { pq.template store<KSW>(sQ[buf], LDK, tid); };
     auto store_k = [&](int kbuf) { pk.template store<KSW>(sK[kbuf], LDK, tid); };
     auto store_v = [&]() { pv.store(sV, LDVV, tid); };
+    // a state wave issues the direct loads j = wave, wave + WS, ... of a tile;
+    // for a whole chunk their per-lane byte offsets are the same in every
+    // chunk, so they are formed once and each load moves only a scalar base
+    constexpr int KPW = (KNI + WS - 1) / WS;
+    uint32_t koff[KDMA ? KPW : 1];
+    auto k_slot = [&](int j, int n) {   // element offset of slot 64 j + lane in a chunk of n rows
+        const int slot = 64 * j + lane, row = slot / KRS, pc = slot % KRS;
+        const int lc = pc < DK / 8 ? pc ^ (KSW / 8 * ((row >> 3) & 1)) : 0;
+        return (row < n ? row : n - 1) * DK + 8 * lc;
+    };
+    if constexpr (KDMA) {
+#pragma unroll
+        for (int jj = 0; jj < KPW; ++jj) koff[jj] = k_slot(wave + WS * jj, C) * sizeof(IO);
+    }
     auto dma_k = [&](int c, int kbuf) {   // KDMA, state waves
         const int n = rows(c);
         const IO *src0 = kh + static_cast<size_t>(c * C) * DK;
         const unsigned base = lds_addr(sK[kbuf]);
+        if (n == C) {
 #pragma unroll
-        for (int j = 0; j < KNI; ++j) {
-            if (j % WS != wave) continue;
-            const int slot = 64 * j + lane, row = slot / KRS, pc = slot % KRS;
-            const int lc = pc < DK / 8 ? pc ^ (KSW / 8 * ((row >> 3) & 1)) : 0;
-            lds_dma16(src0 + (row < n ? row : n - 1) * DK + 8 * lc, __builtin_amdgcn_readfirstlane(base + 1024 * j));
+            for (int jj = 0; jj < KPW; ++jj) {
+                const int j = wave + WS * jj;
+                if (KNI % WS != 0 && j >= KNI) break;
+                lds_dma16(src0, koff[jj], __builtin_amdgcn_readfirstlane(base + 1024 * j));
+            }
+        } else {   // the last, partial chunk
+#pragma unroll
+            for (int jj = 0; jj < KPW; ++jj) {
+                const int j = wave + WS * jj;
+                if (KNI % WS != 0 && j >= KNI) break;
+                lds_dma16(src0 + k_slot(j, n), __builtin_amdgcn_readfirstlane(base + 1024 * j));
+            }
         }
     };
     // SCAN_WAVE: cumulative log2-gates of the staged chunk c into buffer `buf`
