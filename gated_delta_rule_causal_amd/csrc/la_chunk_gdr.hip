@@ -107,7 +107,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     constexpr int VE = 16 / sizeof(Op);
     constexpr int NLOW = NB * (NB + 1) / 2;
     constexpr bool S32 = sizeof(Op) == 2 && C % 32 == 0;   // scores in 32x32 jobs
-    constexpr int NJ32 = (C / 32) * (C / 32 + 1);   // score jobs: two per 32-block pair
+    constexpr int NJ32 = (C / 32) * (C / 32 + 1) / 2;   // score jobs: one per 32-block pair
     static_assert(!S32 || NJ32 <= NHW, "one helper wave per score job");
     constexpr bool HO = gdr_helper_outputs<Op, DVB, C>();   // outputs on helper waves
     constexpr int NJO = C / 32;                     // output jobs of 32 tokens (HO)
@@ -291,33 +291,36 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             }
         }
     };
-    // bfloat16 chunks of 32 or 64 tokens: the scores in 32x32 jobs.  Job j
-    // covers the 32-token block pair (I, J), I >= J, given by j / 2 and forms
-    // K_J Q_I^T (j even: P) or K_J K_I^T (j odd: A; on the diagonal K_J is
-    // both operands); each lane then holds sixteen columns s of one row t,
-    // written four at a time.
-    auto score_job32 = [&](int buf, int kbuf, int job) {
+    // bfloat16 chunks of 32 or 64 tokens: the scores in 32x32 jobs, one per
+    // 32-token block pair (I, J), I >= J, given by `pair`: K_J Q_I^T (P) and
+    // K_J K_I^T (A; on the diagonal K_J is both operands), so that K_J is read
+    // once for both and the decay factors are formed once.  Each lane then
+    // holds sixteen columns s of one row t of each, written four at a time.
+    auto score_pair32 = [&](int buf, int kbuf, int pair) {
         if constexpr (S32) {
-            const int pair = job >> 1;
-            const bool isK = job & 1;
             int I = 0;
             while ((I + 1) * (I + 2) / 2 <= pair) ++I;
             const int J = pair - I * (I + 1) / 2;
             const int r = lane & 31, h = lane >> 5;
             const int off = r * LDK + swap_col(r, 8 * h, KSW);
             const Op *aJ = sK[kbuf] + 32 * J * LDK + off;
-            const Op *bX = (isK ? sK[kbuf] : sQ[buf]) + 32 * I * LDK + off;
-            f32x16 acc = {};
-            if (isK && I == J) {
+            const Op *qI = sQ[buf] + 32 * I * LDK + off;
+            const Op *kI = sK[kbuf] + 32 * I * LDK + off;
+            f32x16 accP = {}, accA = {};
+            if (I == J) {
 #pragma unroll
                 for (int kk = 0; kk < DK / 16; ++kk) {
                     const uint4 a = *reinterpret_cast<const uint4 *>(aJ + 16 * kk);
-                    mma32x32(acc, a, a);
+                    mma32x32(accP, a, *reinterpret_cast<const uint4 *>(qI + 16 * kk));
+                    mma32x32(accA, a, a);
                 }
             } else {
 #pragma unroll
-                for (int kk = 0; kk < DK / 16; ++kk)
-                    mma32x32(acc, *reinterpret_cast<const uint4 *>(aJ + 16 * kk), *reinterpret_cast<const uint4 *>(bX + 16 * kk));
+                for (int kk = 0; kk < DK / 16; ++kk) {
+                    const uint4 a = *reinterpret_cast<const uint4 *>(aJ + 16 * kk);
+                    mma32x32(accP, a, *reinterpret_cast<const uint4 *>(qI + 16 * kk));
+                    mma32x32(accA, a, *reinterpret_cast<const uint4 *>(kI + 16 * kk));
+                }
             }
             const int t = 32 * I + r;
             const float bt = sB[buf][t], be = sBeta[buf][t];
@@ -327,14 +330,12 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 const float4 bs = *reinterpret_cast<const float4 *>(sB[buf] + s0);
                 const float g0 = __builtin_amdgcn_exp2f(fminf(bt - bs.x, 0.f)), g1 = __builtin_amdgcn_exp2f(fminf(bt - bs.y, 0.f));
                 const float g2 = __builtin_amdgcn_exp2f(fminf(bt - bs.z, 0.f)), g3 = __builtin_amdgcn_exp2f(fminf(bt - bs.w, 0.f));
-                if (isK)
-                    *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
-                        make_float4(s0 < t ? be * g0 * acc[4 * q] : 0.f, s0 + 1 < t ? be * g1 * acc[4 * q + 1] : 0.f,
-                                    s0 + 2 < t ? be * g2 * acc[4 * q + 2] : 0.f, s0 + 3 < t ? be * g3 * acc[4 * q + 3] : 0.f);
-                else
-                    st_group(sP[buf] + t * LDC + s0,
-                             Gp::make(s0 <= t ? g0 * acc[4 * q] : 0.f, s0 + 1 <= t ? g1 * acc[4 * q + 1] : 0.f,
-                                      s0 + 2 <= t ? g2 * acc[4 * q + 2] : 0.f, s0 + 3 <= t ? g3 * acc[4 * q + 3] : 0.f));
+                *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
+                    make_float4(s0 < t ? be * g0 * accA[4 * q] : 0.f, s0 + 1 < t ? be * g1 * accA[4 * q + 1] : 0.f,
+                                s0 + 2 < t ? be * g2 * accA[4 * q + 2] : 0.f, s0 + 3 < t ? be * g3 * accA[4 * q + 3] : 0.f);
+                st_group(sP[buf] + t * LDC + s0,
+                         Gp::make(s0 <= t ? g0 * accP[4 * q] : 0.f, s0 + 1 <= t ? g1 * accP[4 * q + 1] : 0.f,
+                                  s0 + 2 <= t ? g2 * accP[4 * q + 2] : 0.f, s0 + 3 <= t ? g3 * accP[4 * q + 3] : 0.f));
             }
         }
     };
@@ -511,7 +512,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         if (k_stager) load_k(min(1, clast));
         if (KDMA && state_wave && nchunks > 1) dma_k(1, 1);
         if constexpr (S32) {
-            if (wave < NJ32) score_job32(0, 0, wave);
+            if (wave < NJ32) score_pair32(0, 0, wave);
         } else {
             if (wave < NW / 2) score_tiles(0, 0, true, 0, NW / 2);
             else score_tiles(0, 0, false, NW / 2, NW - NW / 2);
@@ -661,7 +662,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     if (has_next && hw < NJ32) {
                         // the score jobs bound step 1: raised issue priority
                         __builtin_amdgcn_s_setprio(1);
-                        score_job32(nxt, kn, hw);
+                        score_pair32(nxt, kn, hw);
                         __builtin_amdgcn_s_setprio(0);
                     }
                 } else {
