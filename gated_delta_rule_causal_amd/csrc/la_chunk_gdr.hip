@@ -324,19 +324,27 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             }
             const int t = 32 * I + r;
             const float bt = sB[buf][t], be = sBeta[buf][t];
+            // e^{b_t - b_s} <= 1 for s <= t (b does not increase); above the
+            // diagonal the factor may overflow, and the select drops it
+            auto out = [&](bool diag) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int s0 = 32 * J + 8 * q + 4 * h;
-                const float4 bs = *reinterpret_cast<const float4 *>(sB[buf] + s0);
-                const float g0 = __builtin_amdgcn_exp2f(fminf(bt - bs.x, 0.f)), g1 = __builtin_amdgcn_exp2f(fminf(bt - bs.y, 0.f));
-                const float g2 = __builtin_amdgcn_exp2f(fminf(bt - bs.z, 0.f)), g3 = __builtin_amdgcn_exp2f(fminf(bt - bs.w, 0.f));
-                *reinterpret_cast<float4 *>(sA + t * LDA + s0) =
-                    make_float4(s0 < t ? be * g0 * accA[4 * q] : 0.f, s0 + 1 < t ? be * g1 * accA[4 * q + 1] : 0.f,
-                                s0 + 2 < t ? be * g2 * accA[4 * q + 2] : 0.f, s0 + 3 < t ? be * g3 * accA[4 * q + 3] : 0.f);
-                st_group(sP[buf] + t * LDC + s0,
-                         Gp::make(s0 <= t ? g0 * accP[4 * q] : 0.f, s0 + 1 <= t ? g1 * accP[4 * q + 1] : 0.f,
-                                  s0 + 2 <= t ? g2 * accP[4 * q + 2] : 0.f, s0 + 3 <= t ? g3 * accP[4 * q + 3] : 0.f));
-            }
+                for (int q = 0; q < 4; ++q) {
+                    const int s0 = 32 * J + 8 * q + 4 * h;
+                    const float4 bs = *reinterpret_cast<const float4 *>(sB[buf] + s0);
+                    const float g[4] = {__builtin_amdgcn_exp2f(bt - bs.x), __builtin_amdgcn_exp2f(bt - bs.y),
+                                        __builtin_amdgcn_exp2f(bt - bs.z), __builtin_amdgcn_exp2f(bt - bs.w)};
+                    float a[4], pp[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        a[i] = !diag || s0 + i < t ? be * g[i] * accA[4 * q + i] : 0.f;
+                        pp[i] = !diag || s0 + i <= t ? g[i] * accP[4 * q + i] : 0.f;
+                    }
+                    *reinterpret_cast<float4 *>(sA + t * LDA + s0) = make_float4(a[0], a[1], a[2], a[3]);
+                    st_group(sP[buf] + t * LDC + s0, Gp::make(pp[0], pp[1], pp[2], pp[3]));
+                }
+            };
+            if (I == J) out(true);
+            else out(false);   // every column s precedes the row t
         }
     };
     // diagonal 16x16 block `blk` of T = (I + A)^{-1} by forward substitution,
