@@ -549,7 +549,6 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 const int cur = c & 1, kc = c % 3;
 
                 // step 1: K S0^T, Q S0^T and the solve's right-hand side Y of chunk c
-                if constexpr (KDMA) stage_k(c);
                 G4 yb[NB];
                 f32x4 qs[NB];   // S0 Q^T: lane holds values 4*lg..+3 of token 16 I + lr
                 {
@@ -599,7 +598,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                         yb[I] = Gp::make(y);
                     }
                 }
-                if constexpr (!KDMA) stage_k(c);
+                stage_k(c);
                 __syncthreads();
 
                 // step 2: U = T Y and (not HO) the outputs of chunk c
@@ -694,7 +693,6 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 // of chunk c-1), then the loads of V(c+2) and Q, K(c+3).  Then the
                 // off-diagonal inverse of chunk c+1 (over chunk c's T, last read in
                 // step 2) and, HO, the outputs of chunk c.
-                stage(c);
                 if (has_next) {
                     // the off-diagonal inverse is the longest task of the step: raised
                     // issue priority over the waves it shares a SIMD with
@@ -702,6 +700,7 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                     offdiag(WS, NHW);
                     __builtin_amdgcn_s_setprio(0);
                 }
+                stage(c);
                 if (HO && hw >= OJ0) out_job(c, cur, hw - OJ0, oqs, oeb);
                 __syncthreads();
             }
