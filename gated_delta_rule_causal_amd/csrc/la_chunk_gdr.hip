@@ -168,15 +168,15 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
     // ---------------------------------------------------------------- stages
     // All waves stage the tiles, in step 3: register prefetch one chunk ahead,
     // then LDS (Q, K and the gate values two chunks ahead, V one chunk ahead).
-    // K: with two or more state waves they stage it alone, in step 1, where they
-    // wait for the score jobs anyway (chunk c+2's K goes to the buffer chunk
-    // c-1's used, free for the whole of chunk c)
+    // K: with two or more state waves they stage it alone, at the end of step
+    // 1, where they wait for the score jobs anyway (chunk c+2's K goes to the
+    // buffer chunk c-1's used, free for the whole of chunk c)
     // bfloat16: they fill the K tile by direct global->LDS loads (no registers,
     // no LDS write instructions), in the layout above: 16-byte slot s of the
     // tile (LDK/8 slots a row, the last two padding) receives the column chunk
     // of its row that the swap puts there; rows past the end of the sequence
     // re-read its last row (their solve rows and columns carry beta = 0 and
-    // their scores are masked).  The loads of chunk c+2 are issued at the start
+    // their scores are masked).  The loads of chunk c+2 are issued in step 1
     // of chunk c and waited for before its last barrier.
     constexpr bool KSTATE = WS >= 2;
     constexpr int KRS = LDK * (int)sizeof(Op) / 16;   // 16-byte slots per K tile row
@@ -494,8 +494,8 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
         load_q(min(c + 3, clast));
         if constexpr (!KSTATE) load_k(min(c + 3, clast));
     };
-    // KSTATE, state waves, step 1: chunk c+2's K (KDMA: issued at the start of
-    // the step; registers: stored at its end, chunk c+3's loaded)
+    // KSTATE, state waves, end of step 1: chunk c+2's K (KDMA: the direct
+    // loads; registers: stored, and chunk c+3's loaded)
     auto stage_k = [&](int c) {
         if constexpr (KDMA) {
             if (c + 2 < nchunks) dma_k(c + 2, (c + 2) % 3);
@@ -686,13 +686,13 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 if (HO && hw >= OJ0) qs_job(cur, hw - OJ0, oqs, oeb);
                 __syncthreads();
 
-                // step 3: first the staging (the loads it stores arrived during the
-                // previous chunk; the new loads then fly while the rest computes): V of
-                // chunk c+1 over chunk c's, chunk c+2's gate values -> gate buffer cur
-                // and its Q and K into buffers no step reads any more (Q of chunk c, K
-                // of chunk c-1), then the loads of V(c+2) and Q, K(c+3).  Then the
-                // off-diagonal inverse of chunk c+1 (over chunk c's T, last read in
-                // step 2) and, HO, the outputs of chunk c.
+                // step 3: first the off-diagonal inverse of chunk c+1 (over chunk
+                // c's T, last read in step 2), then the staging (the loads it stores
+                // arrived during the previous chunk): V of chunk c+1 over chunk c's,
+                // chunk c+2's gate values -> gate buffer cur and its Q (and K) into
+                // buffers no step reads any more (Q of chunk c, K of chunk c-1), then
+                // the loads of V(c+2) and Q (K) of chunk c+3; HO: the outputs of
+                // chunk c.
                 if (has_next) {
                     // the off-diagonal inverse is the longest task of the step: raised
                     // issue priority over the waves it shares a SIMD with
