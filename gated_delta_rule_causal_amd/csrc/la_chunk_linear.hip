@@ -113,6 +113,22 @@ __device__ __forceinline__ float row_scan_mul(float x) {
     return x;
 }
 
+// x times y taken from the last lane of the row before (DPP row broadcast 15)
+// or from lane 31 (row broadcast 31), on the rows of the row mask; the other
+// rows keep x.  Written in place, as in row_scan_mul.
+__device__ __forceinline__ float mul_bcast15_rows13(float y, float x) {
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(x) : "v"(y));
+    return x;
+}
+__device__ __forceinline__ float mul_bcast15_row2(float y, float x) {
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_bcast:15 row_mask:0x4 bank_mask:0xf" : "+v"(x) : "v"(y));
+    return x;
+}
+__device__ __forceinline__ float mul_bcast31_rows23(float y, float x) {
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_bcast:31 row_mask:0xc bank_mask:0xf" : "+v"(x) : "v"(y));
+    return x;
+}
+
 // pair index of an off-diagonal key block J <= I - 2 (blocks strictly between exist)
 __host__ __device__ constexpr int rho_index(int I, int J) { return (I - 2) * (I - 1) / 2 + J; }
 
@@ -546,7 +562,8 @@ struct GlaLds {
     static constexpr int NRHO = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 0;
     static constexpr int PAD = 16 / sizeof(Op);
     static constexpr int LDK = DK + PAD, LDC = C + PAD, LDV = DVB + PAD;
-    static constexpr int F_FLOATS = (NB + 1 + NRHO) * DK;
+    static constexpr int NTOT = NB + 3;   // block-total slots: NB totals, then three of ones
+    static constexpr int F_FLOATS = (NB + 1 + NRHO + NTOT) * DK;
     static constexpr int BYTES = (5 * C * LDK + 2 * C * LDV + C * LDC) * (int)sizeof(Op) + F_FLOATS * 4;
     static constexpr int WS = DVB / 16, NH = NW - WS;
     static constexpr bool FITS = BYTES <= 160 * 1024 && NH >= 2;
@@ -571,8 +588,8 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
     __shared__ __align__(16) Op sKt[C * LDK];      // state-update key operand
     __shared__ __align__(16) Op sV[2][C * LDV];    // values, [t][v]
     __shared__ __align__(16) Op sP[C * LDC];       // scores
-    __shared__ __align__(16) float sF[L::F_FLOATS];   // E_J, D, rho
-    float *sE = sF, *sD = sF + NB * DK, *sRho = sF + (NB + 1) * DK;
+    __shared__ __align__(16) float sF[L::F_FLOATS];   // E_J, D, rho, block totals
+    float *sE = sF, *sD = sF + NB * DK, *sRho = sF + (NB + 1) * DK, *sTot = sRho + L::NRHO * DK;
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
@@ -603,6 +620,9 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // block-total slots NB.. are ones: a token's product over the blocks after
+    // its own reads the NB - 1 slots that follow its block's
+    for (int e = tid; e < (L::NTOT - NB) * DK; e += NW * 64) sTot[NB * DK + e] = 1.f;
 
     // q, k, v (helpers) and the gates (every wave) two chunks ahead of the
     // state part.  Every load is issued whether or not its chunk exists (a
@@ -708,12 +728,6 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                     run[i] = row_scan_mul(g[i]);   // R_t = prod_{16I <= s <= t} g_s
                     rinv[i] = __builtin_amdgcn_rcpf(run[i]);
                 }
-                float tot[NB][4];   // whole-block products (uniform)
-#pragma unroll
-                for (int J = 0; J < NB; ++J)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        tot[J][i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(run[i]), 16 * J + 15));
                 {
                     // per-chunk factors, from a scan across the block ends: after
                     // two DPP row broadcasts lane t holds P_t = prod_{s <= t} g_s, so
@@ -724,40 +738,54 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                     float pre[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        pre[i] = run[i] * dpp_or_one<0x142, 0xA>(run[i]);   // rows 1, 3: last lane of the row before
-                        pre[i] *= dpp_or_one<0x143, 0xC>(pre[i]);       // rows 2, 3: lane 31's prefix
+                        pre[i] = mul_bcast15_rows13(run[i], run[i]);   // rows 1, 3: times the last lane of the row before
+                        pre[i] = mul_bcast31_rows23(pre[i], pre[i]);   // rows 2, 3: times lane 31's prefix
                     }
                     if ((lane & 15) == 15 && (lane >> 4) < NB) {
                         const int J = lane >> 4;   // E_{J+1} for J < NB - 1, D for the last block
                         *reinterpret_cast<float4 *>(sE + (J + 1) * DK + cc) = make_float4(pre[0], pre[1], pre[2], pre[3]);
+                        // the block's total, for every token of the chunk below
+                        *reinterpret_cast<float4 *>(sTot + J * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
                     }
                     if constexpr (NB == 4) {
                         // rho_{2,0} = tot_1 (lane 31), rho_{3,1} = tot_2 and rho_{3,0} = tot_1 tot_2 (lane 47)
                         if (lane == 31)
                             *reinterpret_cast<float4 *>(sRho + rho_index(2, 0) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
-                        float t1[4];   // row 2: tot_1 (lane 31's row total)
+                        float t12[4];   // row 2: tot_1 (lane 31's row total) times the row's own products
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) t1[i] = dpp_or_one<0x142, 0x4>(run[i]);
+                        for (int i = 0; i < 4; ++i) t12[i] = mul_bcast15_row2(run[i], run[i]);
                         if (lane == 47) {
                             *reinterpret_cast<float4 *>(sRho + rho_index(3, 1) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
-                            *reinterpret_cast<float4 *>(sRho + rho_index(3, 0) * DK + cc) =
-                                make_float4(t1[0] * run[0], t1[1] * run[1], t1[2] * run[2], t1[3] * run[3]);
+                            *reinterpret_cast<float4 *>(sRho + rho_index(3, 0) * DK + cc) = make_float4(t12[0], t12[1], t12[2], t12[3]);
                         }
+                    }
+                }
+                // the total of the token's own block and the product of the totals
+                // of the blocks after it, read back from the slots the block-end
+                // lanes just wrote.  The wave executes its LDS operations in
+                // order; the empty asm keeps the compiler from moving these reads
+                // (of values other lanes wrote) above those writes.
+                asm volatile("" ::: "memory");
+                float tb[4], after[4];
+                {
+                    const float4 b = *reinterpret_cast<const float4 *>(sTot + I * DK + cc);
+                    tb[0] = b.x; tb[1] = b.y; tb[2] = b.z; tb[3] = b.w;
+                    after[0] = after[1] = after[2] = after[3] = 1.f;
+#pragma unroll
+                    for (int m = 1; m < NB; ++m) {
+                        const float4 a = *reinterpret_cast<const float4 *>(sTot + (I + m) * DK + cc);
+                        after[0] *= a.x; after[1] *= a.y; after[2] *= a.z; after[3] *= a.w;
                     }
                 }
                 float fq[4], fd[4], fk[4], fa[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float tb = tot[0][i], after = 1.f;
-#pragma unroll
-                    for (int J = 1; J < NB; ++J) {
-                        if (J == I) tb = tot[J][i];
-                        if (J > I) after *= tot[J][i];
-                    }
-                    fq[i] = on ? apply_phi<PHI>(q[i]) * run[i] : 0.f;
-                    fd[i] = on ? apply_phi<PHI>(k[i]) * rinv[i] : 0.f;
-                    fk[i] = fd[i] * tb;
-                    fa[i] = fk[i] * after;
+                    // tokens past the end: zero operands (selects, not branches)
+                    const float rq = on ? run[i] : 0.f, rk = on ? rinv[i] : 0.f;
+                    fq[i] = apply_phi<PHI>(q[i]) * rq;
+                    fd[i] = apply_phi<PHI>(k[i]) * rk;
+                    fk[i] = fd[i] * tb[i];
+                    fa[i] = fk[i] * after[i];
                 }
                 if (in_tile) {
                     st_group(sQ[nb] + t * LDK + cc, Gp::make(fq[0], fq[1], fq[2], fq[3]));
