@@ -113,20 +113,32 @@ __device__ __forceinline__ float row_scan_mul(float x) {
     return x;
 }
 
-// x times y taken from the last lane of the row before (DPP row broadcast 15)
-// or from lane 31 (row broadcast 31), on the rows of the row mask; the other
-// rows keep x.  Written in place, as in row_scan_mul.
-__device__ __forceinline__ float mul_bcast15_rows13(float y, float x) {
-    asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_bcast:15 row_mask:0xa bank_mask:0xf" : "+v"(x) : "v"(y));
-    return x;
+// Four independent channels at once, one DPP step of all four before the next
+// step of any: each DPP read then follows the write of its source by three
+// other instructions, which covers the two wait states, so only the first
+// instruction of the group needs the s_nop.
+#define LA_DPP4(CTRL)                                                                                                   \
+    "s_nop 1\n\t"                                                                                                   \
+    "v_mul_f32_dpp %0, %4, %0 " CTRL "\n\tv_mul_f32_dpp %1, %5, %1 " CTRL "\n\t"                                     \
+    "v_mul_f32_dpp %2, %6, %2 " CTRL "\n\tv_mul_f32_dpp %3, %7, %3 " CTRL
+// x[i] <- y[i] (moved by the DPP control) times x[i]
+#define LA_DPP4_OPS(x, y) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3])
+__device__ __forceinline__ void row_scan_mul4(float (&x)[4]) {
+    asm(LA_DPP4("row_shr:1 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4("row_shr:2 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4("row_shr:4 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4("row_shr:8 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
 }
-__device__ __forceinline__ float mul_bcast15_row2(float y, float x) {
-    asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_bcast:15 row_mask:0x4 bank_mask:0xf" : "+v"(x) : "v"(y));
-    return x;
+// x <- y[last lane of the row before] * x on rows 1 and 3, then
+// x <- x[lane 31] * x on rows 2 and 3 (with x = y on entry: the inclusive
+// prefix over the whole wave, from the row-wise one)
+__device__ __forceinline__ void wave_prefix_from_rows4(const float (&y)[4], float (&x)[4]) {
+    asm(LA_DPP4("row_bcast:15 row_mask:0xa bank_mask:0xf") : LA_DPP4_OPS(x, y));
+    asm(LA_DPP4("row_bcast:31 row_mask:0xc bank_mask:0xf") : LA_DPP4_OPS(x, x));
 }
-__device__ __forceinline__ float mul_bcast31_rows23(float y, float x) {
-    asm("s_nop 1\n\tv_mul_f32_dpp %0, %1, %0 row_bcast:31 row_mask:0xc bank_mask:0xf" : "+v"(x) : "v"(y));
-    return x;
+// x <- y[lane 31] * x on row 2
+__device__ __forceinline__ void mul_bcast15_row2_4(const float (&y)[4], float (&x)[4]) {
+    asm(LA_DPP4("row_bcast:15 row_mask:0x4 bank_mask:0xf") : LA_DPP4_OPS(x, y));
 }
 
 // pair index of an off-diagonal key block J <= I - 2 (blocks strictly between exist)
@@ -722,12 +734,10 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                     Gp::unpack(ld_group(sQ[nb] + t * LDK + cc), q);
                     Gp::unpack(ld_group(sK + t * LDK + cc), k);
                 }
-                float run[4], rinv[4];
+                float run[4] = {g[0], g[1], g[2], g[3]}, rinv[4];
+                row_scan_mul4(run);   // R_t = prod_{16I <= s <= t} g_s
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    run[i] = row_scan_mul(g[i]);   // R_t = prod_{16I <= s <= t} g_s
-                    rinv[i] = __builtin_amdgcn_rcpf(run[i]);
-                }
+                for (int i = 0; i < 4; ++i) rinv[i] = __builtin_amdgcn_rcpf(run[i]);
                 {
                     // per-chunk factors, from a scan across the block ends: after
                     // two DPP row broadcasts lane t holds P_t = prod_{s <= t} g_s, so
@@ -735,12 +745,8 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                     // lane 63, and rho_{J1 J0} (blocks strictly between) is the block
                     // total of lane 31 or 47, or their product.  Each value is written
                     // by the lane that holds it.
-                    float pre[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pre[i] = mul_bcast15_rows13(run[i], run[i]);   // rows 1, 3: times the last lane of the row before
-                        pre[i] = mul_bcast31_rows23(pre[i], pre[i]);   // rows 2, 3: times lane 31's prefix
-                    }
+                    float pre[4] = {run[0], run[1], run[2], run[3]};
+                    wave_prefix_from_rows4(run, pre);
                     if ((lane & 15) == 15 && (lane >> 4) < NB) {
                         const int J = lane >> 4;   // E_{J+1} for J < NB - 1, D for the last block
                         *reinterpret_cast<float4 *>(sE + (J + 1) * DK + cc) = make_float4(pre[0], pre[1], pre[2], pre[3]);
@@ -751,9 +757,8 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                         // rho_{2,0} = tot_1 (lane 31), rho_{3,1} = tot_2 and rho_{3,0} = tot_1 tot_2 (lane 47)
                         if (lane == 31)
                             *reinterpret_cast<float4 *>(sRho + rho_index(2, 0) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
-                        float t12[4];   // row 2: tot_1 (lane 31's row total) times the row's own products
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) t12[i] = mul_bcast15_row2(run[i], run[i]);
+                        float t12[4] = {run[0], run[1], run[2], run[3]};   // row 2: tot_1 (lane 31) times the row's products
+                        mul_bcast15_row2_4(run, t12);
                         if (lane == 47) {
                             *reinterpret_cast<float4 *>(sRho + rho_index(3, 1) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
                             *reinterpret_cast<float4 *>(sRho + rho_index(3, 0) * DK + cc) = make_float4(t12[0], t12[1], t12[2], t12[3]);
