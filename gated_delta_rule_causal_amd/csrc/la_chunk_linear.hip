@@ -560,12 +560,15 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 //           state update; the other waves: commit chunk c+1's staged q, k, v
 //           and load chunk c+2's;
 //   step B  all waves: the gate factors of chunk c+1; then the state waves
-//           store chunk c's outputs, and every wave loads its gates of
-//           chunk c+2;
-//   step C  all waves: the scores of chunk c+1.
+//           store chunk c's outputs;
+//   step C  all waves: the scores of chunk c+1; the state waves load chunk
+//           c+2's gates.
 // The raw q and V tiles are double-buffered (chunk c+1's are written while
-// chunk c's are read).  The gates never touch LDS: each lane loads the gates
-// of its token for exactly the channels its gate-factor passes handle.  The
+// chunk c's are read).  The gate tile goes straight from global memory to LDS
+// (direct loads, whole rows per instruction, in rows padded by 16 bytes so
+// that the gate pass's reads of one channel group over 16 tokens touch every
+// bank once); where that tile does not fit, each lane loads the gates of its
+// token for exactly the channels its gate-factor passes handle instead.  The
 // arithmetic is the gated path of linear_chunk_kernel, term for term.
 template <class DT, int DK, int DVB, int C, int NW>
 struct GlaLds {
@@ -579,6 +582,8 @@ struct GlaLds {
     static constexpr int BYTES = (5 * C * LDK + 2 * C * LDV + C * LDC) * (int)sizeof(Op) + F_FLOATS * 4;
     static constexpr int WS = DVB / 16, NH = NW - WS;
     static constexpr bool FITS = BYTES <= 160 * 1024 && NH >= 2;
+    static constexpr int GLD = DK + 4;   // gate tile row stride (floats)
+    static constexpr bool GDMA = BYTES + C * GLD * 4 <= 160 * 1024;
 };
 
 template <int PHI, class DT, int DK, int DVB, int C, int NW>
@@ -601,6 +606,9 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
     __shared__ __align__(16) Op sV[2][C * LDV];    // values, [t][v]
     __shared__ __align__(16) Op sP[C * LDC];       // scores
     __shared__ __align__(16) float sF[L::F_FLOATS];   // E_J, D, rho, block totals
+    constexpr bool GDMA = L::GDMA;
+    constexpr int GLD = L::GLD;
+    __shared__ __align__(16) float sG[GDMA ? C * GLD : 4];   // gates of the chunk being prepared
     float *sE = sF, *sD = sF + NB * DK, *sRho = sF + (NB + 1) * DK, *sTot = sRho + L::NRHO * DK;
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -656,10 +664,30 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
         for (int i = 0; i < GI; ++i)
             if (4 * wave + 4 * NW * i < DK) pg[i] = *reinterpret_cast<const float4 *>(g + 4 * NW * i);
     };
+    // GDMA, state waves: chunk c's gate tile by direct loads, 16-byte slot s
+    // of the tile (GLD / 4 slots a row, the last one padding) receiving the
+    // four gates of its row and column group (rows past the end re-read the
+    // last row; their gates are replaced by 1)
+    auto dma_gates = [&](int c) {
+        constexpr int GRS = GLD / 4, GNI = (C * GRS + 63) / 64;
+        const int n = rows(c);
+        const float *src0 = gh + static_cast<size_t>(c * C) * DK;
+        const unsigned base = lds_addr(sG);
+        for (int j = wave; j < GNI; j += WS) {
+            const int slot = 64 * j + lane, row = slot / GRS, col = slot % GRS;
+            if ((C * GRS) % 64 == 0 || slot < C * GRS)
+                lds_dma16(src0 + (row < n ? row : n - 1) * DK + 4 * (col < DK / 4 ? col : 0),
+                          __builtin_amdgcn_readfirstlane(base + 1024 * j));
+        }
+    };
     f32x4 ob[NB];   // state waves: outputs of chunk c, stored in step B
     if (nchunks > 0) {
         if (!state_wave) load_qkv(0);
-        load_gates(0);
+        if constexpr (GDMA) {
+            if (state_wave) dma_gates(0);
+        } else {
+            load_gates(0);
+        }
     }
 
     for (int c = -1; c < nchunks && nchunks > 0; ++c) {
@@ -715,6 +743,11 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
             }
             load_qkv(min(c + 2, clast));
         }
+        // GDMA: the gate tile of chunk c+1 (loaded in the previous step C, or
+        // before the loop) has landed before the barrier
+        if constexpr (GDMA) {
+            if (state_wave) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        }
         __syncthreads();
 
         // ---- step B.  All waves: the gate factors of chunk c+1 (lane = token,
@@ -729,7 +762,12 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                 const int cc = 4 * wave + 4 * NW * it;
                 if (cc >= DK) break;   // uniform: the last pass covers fewer waves
                 float g[4] = {1.f, 1.f, 1.f, 1.f}, q[4] = {0.f, 0.f, 0.f, 0.f}, k[4] = {0.f, 0.f, 0.f, 0.f};
-                if (on) { g[0] = pg[it].x; g[1] = pg[it].y; g[2] = pg[it].z; g[3] = pg[it].w; }   // 1 past the end
+                if constexpr (GDMA) {
+                    const float4 gv = *reinterpret_cast<const float4 *>(sG + (in_tile ? t : 0) * GLD + cc);
+                    if (on) { g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w; }   // 1 past the end
+                } else {
+                    if (on) { g[0] = pg[it].x; g[1] = pg[it].y; g[2] = pg[it].z; g[3] = pg[it].w; }
+                }
                 if (in_tile) {
                     Gp::unpack(ld_group(sQ[nb] + t * LDK + cc), q);
                     Gp::unpack(ld_group(sK + t * LDK + cc), k);
@@ -809,11 +847,16 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                     st_group(oh + static_cast<size_t>(c * C + t) * p.d_v + vb * DVB + 16 * wave + 4 * lg, Gp::make(ob[I]));
             }
         }
-        load_gates(min(c + 2, clast));
+        if constexpr (!GDMA) load_gates(min(c + 2, clast));
         __syncthreads();
 
         // ---- step C.  All waves: the scores of chunk c+1 (16x16 tiles, taken
         // transposed so that a lane writes four consecutive columns of a row).
+        // GDMA: the state waves first issue the loads of chunk c+2's gate tile
+        // (every read of the tile, in step B, is behind the barrier above).
+        if constexpr (GDMA) {
+            if (state_wave && c + 2 < nchunks) dma_gates(c + 2);
+        }
         if (prep) {
             for (int tt = wave; tt < NB * NB; tt += NW) {
                 const int I = tt / NB, J = tt % NB;
