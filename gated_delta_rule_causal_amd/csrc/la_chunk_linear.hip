@@ -858,12 +858,12 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
             if (state_wave && c + 2 < nchunks) dma_gates(c + 2);
         }
         if (prep) {
-            for (int tt = wave; tt < NB * NB; tt += NW) {
+            auto score_tile = [&](int tt) {   // tile (I, J) = (tt / NB, tt % NB)
                 const int I = tt / NB, J = tt % NB;
                 const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
                 if (J > I) {
                     st_group(sP + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
-                    continue;
+                    return;
                 }
                 f32x4 acc = zero4();
                 if (J == I)
@@ -875,6 +875,17 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                                            sQ[nb] + 16 * I * LDK, LDK, lane);
                 st_group(sP + t * LDC + j0, Gp::make(j0 <= t ? acc[0] : 0.f, j0 + 1 <= t ? acc[1] : 0.f,
                                                      j0 + 2 <= t ? acc[2] : 0.f, j0 + 3 <= t ? acc[3] : 0.f));
+            };
+            if constexpr (NB == 4 && NW == 8) {
+                // two tiles per wave (tile ids 4 I + J, a nibble each): the three
+                // rho-scaled tiles alone on the state waves (with a zero tile),
+                // the other helpers two plain products or one and a zero tile
+                // (order 8,1 | 12,2 | 13,3 | 15,6 | 0,4 | 5,9 | 10,7 | 14,11)
+                constexpr unsigned long long kOrder = 0xbe7a95406f3d2c18ull;
+                score_tile(static_cast<int>((kOrder >> (8 * wave)) & 15));
+                score_tile(static_cast<int>((kOrder >> (8 * wave + 4)) & 15));
+            } else {
+                for (int tt = wave; tt < NB * NB; tt += NW) score_tile(tt);
             }
         }
         __syncthreads();
