@@ -557,12 +557,11 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 // state-dependent part of chunk c:
 //   step A  state waves (DVB/16, each owning the state slice of 16 value
 //           channels): the outputs of chunk c (kept in registers) and its
-//           state update; the other waves: commit chunk c+1's staged q, k, v
-//           and load chunk c+2's;
+//           state update; the other waves: commit chunk c+1's staged q, k, v,
+//           load chunk c+1's gate tile and chunk c+2's q, k, v;
 //   step B  all waves: the gate factors of chunk c+1; then the state waves
 //           store chunk c's outputs;
-//   step C  all waves: the scores of chunk c+1; the state waves load chunk
-//           c+2's gates.
+//   step C  all waves: the scores of chunk c+1.
 // The raw q and V tiles are double-buffered (chunk c+1's are written while
 // chunk c's are read).  The gate tile goes straight from global memory to LDS
 // (direct loads, whole rows per instruction, in rows padded by 16 bytes so
@@ -664,7 +663,7 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
         for (int i = 0; i < GI; ++i)
             if (4 * wave + 4 * NW * i < DK) pg[i] = *reinterpret_cast<const float4 *>(g + 4 * NW * i);
     };
-    // GDMA, state waves: chunk c's gate tile by direct loads, 16-byte slot s
+    // GDMA, helper waves: chunk c's gate tile by direct loads, 16-byte slot s
     // of the tile (GLD / 4 slots a row, the last one padding) receiving the
     // four gates of its row and column group (rows past the end re-read the
     // last row; their gates are replaced by 1)
@@ -673,7 +672,7 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
         const int n = rows(c);
         const float *src0 = gh + static_cast<size_t>(c * C) * DK;
         const unsigned base = lds_addr(sG);
-        for (int j = wave; j < GNI; j += WS) {
+        for (int j = wave - WS; j < GNI; j += NH) {
             const int slot = 64 * j + lane, row = slot / GRS, col = slot % GRS;
             if ((C * GRS) % 64 == 0 || slot < C * GRS)
                 lds_dma16(src0 + (row < n ? row : n - 1) * DK + 4 * (col < DK / 4 ? col : 0),
@@ -683,21 +682,142 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
     f32x4 ob[NB];   // state waves: outputs of chunk c, stored in step B
     if (nchunks > 0) {
         if (!state_wave) load_qkv(0);
-        if constexpr (GDMA) {
-            if (state_wave) dma_gates(0);
-        } else {
-            load_gates(0);
-        }
+        if constexpr (!GDMA) load_gates(0);
     }
 
-    for (int c = -1; c < nchunks && nchunks > 0; ++c) {
-        const int cur = c & 1, nb = (c + 1) & 1;   // raw-tile buffers of chunk c and chunk c+1
-        const bool prep = c + 1 < nchunks;          // chunk c+1 is prepared
-        const int n1 = prep ? rows(c + 1) : 0;
+    // step B, every wave: the gate factors of chunk c+1 (lane = token, four
+    // channels per pass; the products along a 16-token block are 16-lane DPP
+    // row scans)
+    auto gate_pass = [&](int c) {
+        if (c + 1 >= nchunks) return;
+        const int nb = (c + 1) & 1, n1 = rows(c + 1);
+        const int t = lane, I = t >> 4;
+        const bool in_tile = t < C, on = t < n1;
+#pragma unroll
+        for (int it = 0; it < GI; ++it) {
+            const int cc = 4 * wave + 4 * NW * it;
+            if (cc >= DK) break;   // uniform: the last pass covers fewer waves
+            float g[4] = {1.f, 1.f, 1.f, 1.f}, q[4] = {0.f, 0.f, 0.f, 0.f}, k[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (GDMA) {
+                const float4 gv = *reinterpret_cast<const float4 *>(sG + (in_tile ? t : 0) * GLD + cc);
+                if (on) { g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w; }   // 1 past the end
+            } else {
+                if (on) { g[0] = pg[it].x; g[1] = pg[it].y; g[2] = pg[it].z; g[3] = pg[it].w; }
+            }
+            if (in_tile) {
+                Gp::unpack(ld_group(sQ[nb] + t * LDK + cc), q);
+                Gp::unpack(ld_group(sK + t * LDK + cc), k);
+            }
+            float run[4] = {g[0], g[1], g[2], g[3]}, rinv[4];
+            row_scan_mul4(run);   // R_t = prod_{16I <= s <= t} g_s
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rinv[i] = __builtin_amdgcn_rcpf(run[i]);
+            {
+                // per-chunk factors, from a scan across the block ends: after
+                // two DPP row broadcasts lane t holds P_t = prod_{s <= t} g_s, so
+                // E_J = P at lane 16J - 1 (J >= 1; E_0 = 1 is never read), D = P at
+                // lane 63, and rho_{J1 J0} (blocks strictly between) is the block
+                // total of lane 31 or 47, or their product.  Each value is written
+                // by the lane that holds it.
+                float pre[4] = {run[0], run[1], run[2], run[3]};
+                wave_prefix_from_rows4(run, pre);
+                if ((lane & 15) == 15 && (lane >> 4) < NB) {
+                    const int J = lane >> 4;   // E_{J+1} for J < NB - 1, D for the last block
+                    *reinterpret_cast<float4 *>(sE + (J + 1) * DK + cc) = make_float4(pre[0], pre[1], pre[2], pre[3]);
+                    // the block's total, for every token of the chunk below
+                    *reinterpret_cast<float4 *>(sTot + J * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
+                }
+                if constexpr (NB == 4) {
+                    // rho_{2,0} = tot_1 (lane 31), rho_{3,1} = tot_2 and rho_{3,0} = tot_1 tot_2 (lane 47)
+                    if (lane == 31)
+                        *reinterpret_cast<float4 *>(sRho + rho_index(2, 0) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
+                    float t12[4] = {run[0], run[1], run[2], run[3]};   // row 2: tot_1 (lane 31) times the row's products
+                    mul_bcast15_row2_4(run, t12);
+                    if (lane == 47) {
+                        *reinterpret_cast<float4 *>(sRho + rho_index(3, 1) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
+                        *reinterpret_cast<float4 *>(sRho + rho_index(3, 0) * DK + cc) = make_float4(t12[0], t12[1], t12[2], t12[3]);
+                    }
+                }
+            }
+            // the total of the token's own block and the product of the totals
+            // of the blocks after it, read back from the slots the block-end
+            // lanes just wrote.  The wave executes its LDS operations in
+            // order; the empty asm keeps the compiler from moving these reads
+            // (of values other lanes wrote) above those writes.
+            asm volatile("" ::: "memory");
+            float tb[4], after[4];
+            {
+                const float4 b = *reinterpret_cast<const float4 *>(sTot + I * DK + cc);
+                tb[0] = b.x; tb[1] = b.y; tb[2] = b.z; tb[3] = b.w;
+                after[0] = after[1] = after[2] = after[3] = 1.f;
+#pragma unroll
+                for (int m = 1; m < NB; ++m) {
+                    const float4 a = *reinterpret_cast<const float4 *>(sTot + (I + m) * DK + cc);
+                    after[0] *= a.x; after[1] *= a.y; after[2] *= a.z; after[3] *= a.w;
+                }
+            }
+            float fq[4], fd[4], fk[4], fa[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                // tokens past the end: zero operands (selects, not branches)
+                const float rq = on ? run[i] : 0.f, rk = on ? rinv[i] : 0.f;
+                fq[i] = apply_phi<PHI>(q[i]) * rq;
+                fd[i] = apply_phi<PHI>(k[i]) * rk;
+                fk[i] = fd[i] * tb[i];
+                fa[i] = fk[i] * after[i];
+            }
+            if (in_tile) {
+                st_group(sQ[nb] + t * LDK + cc, Gp::make(fq[0], fq[1], fq[2], fq[3]));
+                st_group(sKd + t * LDK + cc, Gp::make(fd[0], fd[1], fd[2], fd[3]));
+                st_group(sK + t * LDK + cc, Gp::make(fk[0], fk[1], fk[2], fk[3]));
+                st_group(sKt + t * LDK + cc, Gp::make(fa[0], fa[1], fa[2], fa[3]));
+            }
+        }
+    };
+    // step C, every wave: the scores of chunk c+1 (16x16 tiles, taken
+    // transposed so that a lane writes four consecutive columns of a row)
+    auto scores = [&](int c) {
+        if (c + 1 >= nchunks) return;
+        const int nb = (c + 1) & 1;
+        auto score_tile = [&](int tt) {   // tile (I, J) = (tt / NB, tt % NB)
+            const int I = tt / NB, J = tt % NB;
+            const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
+            if (J > I) {
+                st_group(sP + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
+                return;
+            }
+            f32x4 acc = zero4();
+            if (J == I)
+                tile_mma_ll<DK>(acc, sKd + 16 * J * LDK, LDK, sQ[nb] + 16 * I * LDK, LDK, lane);
+            else if (J == I - 1)
+                tile_mma_ll<DK>(acc, sK + 16 * J * LDK, LDK, sQ[nb] + 16 * I * LDK, LDK, lane);
+            else
+                tile_mma_ll_scaled<DK>(acc, sK + 16 * J * LDK, LDK, sRho + rho_index(I, J) * DK,
+                                       sQ[nb] + 16 * I * LDK, LDK, lane);
+            st_group(sP + t * LDC + j0, Gp::make(j0 <= t ? acc[0] : 0.f, j0 + 1 <= t ? acc[1] : 0.f,
+                                                 j0 + 2 <= t ? acc[2] : 0.f, j0 + 3 <= t ? acc[3] : 0.f));
+        };
+        if constexpr (NB == 4 && NW == 8) {
+            // two tiles per wave (tile ids 4 I + J, a nibble each): the three
+            // rho-scaled tiles alone on the state waves (with a zero tile),
+            // the other helpers two plain products or one and a zero tile
+            // (order 8,1 | 12,2 | 13,3 | 15,6 | 0,4 | 5,9 | 10,7 | 14,11)
+            constexpr unsigned long long kOrder = 0xbe7a95406f3d2c18ull;
+            score_tile(static_cast<int>((kOrder >> (8 * wave)) & 15));
+            score_tile(static_cast<int>((kOrder >> (8 * wave + 4)) & 15));
+        } else {
+            for (int tt = wave; tt < NB * NB; tt += NW) score_tile(tt);
+        }
+    };
 
-        // ---- step A.  State waves: the outputs of chunk c (to registers) and
-        // its state update.  Helpers: commit chunk c+1, load chunk c+2.
-        if (state_wave) {
+    // The two roles run loops of their own with the same three barriers per
+    // chunk, so that each role's registers are allocated for its own work (in
+    // one loop the staged q, k, v registers were copied at the end of step A,
+    // which waited for the loads just issued).
+    if (state_wave) {
+        for (int c = -1; c < nchunks && nchunks > 0; ++c) {
+            const int cur = c & 1;
+            // ---- step A: the outputs of chunk c (to registers) and its state update
             if (c >= 0) {
                 G4 sb[NCB];
 #pragma unroll
@@ -735,160 +855,55 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                               kt_group<0>(sV[cur], LDV, 16 * (NB - 1), 16 * wave, lane));
                 }
             }
-        } else {
-            if (prep) {
-                pq.store(sQ[nb], LDK, htid);
-                pk.store(sK, LDK, htid);
-                pv.store(sV[nb], LDV, htid);
+            __syncthreads();
+            // ---- step B: the gate factors of chunk c+1, then chunk c's outputs
+            gate_pass(c);
+            if (c >= 0) {
+                const int n = rows(c);
+#pragma unroll
+                for (int I = 0; I < NB; ++I) {
+                    const int t = 16 * I + lr;
+                    if (t < n)
+                        st_group(oh + static_cast<size_t>(c * C + t) * p.d_v + vb * DVB + 16 * wave + 4 * lg, Gp::make(ob[I]));
+                }
+            }
+            if constexpr (!GDMA) load_gates(min(c + 2, clast));
+            __syncthreads();
+            // ---- step C
+            scores(c);
+            __syncthreads();
+        }
+    } else {
+        for (int c = -1; c < nchunks && nchunks > 0; ++c) {
+            const int nb = (c + 1) & 1;
+            const bool prep = c + 1 < nchunks;   // chunk c+1 is prepared
+            // ---- step A: commit chunk c+1, load its gate tile and chunk c+2's q, k, v
+            // committed on every chunk (after the last one into buffers that
+            // nothing reads any more), so that every path through the loop
+            // consumes the staged registers and the compiler's waits for them
+            // stay exact
+            pq.store(sQ[nb], LDK, htid);
+            pk.store(sK, LDK, htid);
+            pv.store(sV[nb], LDV, htid);
+            // GDMA: chunk c+1's gate tile (sG was last read in the previous
+            // step B), issued after the stores above, whose waits for the
+            // staged registers would otherwise cover these loads too
+            if constexpr (GDMA) {
+                if (prep) dma_gates(c + 1);
             }
             load_qkv(min(c + 2, clast));
+            // GDMA: the gate tile has landed before the barrier; only the q, k,
+            // v loads issued after it stay in flight
+            if constexpr (GDMA) __builtin_amdgcn_s_waitcnt(wait_vmcnt(pq.PER + pk.PER + pv.PER));
+            __syncthreads();
+            // ---- step B
+            gate_pass(c);
+            if constexpr (!GDMA) load_gates(min(c + 2, clast));
+            __syncthreads();
+            // ---- step C
+            scores(c);
+            __syncthreads();
         }
-        // GDMA: the gate tile of chunk c+1 (loaded in the previous step C, or
-        // before the loop) has landed before the barrier
-        if constexpr (GDMA) {
-            if (state_wave) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        }
-        __syncthreads();
-
-        // ---- step B.  All waves: the gate factors of chunk c+1 (lane = token,
-        // four channels per pass; the products along a 16-token block are
-        // 16-lane DPP row scans).  Then the state waves store chunk c's outputs
-        // and every wave loads its gates of chunk c+2.
-        if (prep) {
-            const int t = lane, I = t >> 4;
-            const bool in_tile = t < C, on = t < n1;
-#pragma unroll
-            for (int it = 0; it < GI; ++it) {
-                const int cc = 4 * wave + 4 * NW * it;
-                if (cc >= DK) break;   // uniform: the last pass covers fewer waves
-                float g[4] = {1.f, 1.f, 1.f, 1.f}, q[4] = {0.f, 0.f, 0.f, 0.f}, k[4] = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (GDMA) {
-                    const float4 gv = *reinterpret_cast<const float4 *>(sG + (in_tile ? t : 0) * GLD + cc);
-                    if (on) { g[0] = gv.x; g[1] = gv.y; g[2] = gv.z; g[3] = gv.w; }   // 1 past the end
-                } else {
-                    if (on) { g[0] = pg[it].x; g[1] = pg[it].y; g[2] = pg[it].z; g[3] = pg[it].w; }
-                }
-                if (in_tile) {
-                    Gp::unpack(ld_group(sQ[nb] + t * LDK + cc), q);
-                    Gp::unpack(ld_group(sK + t * LDK + cc), k);
-                }
-                float run[4] = {g[0], g[1], g[2], g[3]}, rinv[4];
-                row_scan_mul4(run);   // R_t = prod_{16I <= s <= t} g_s
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rinv[i] = __builtin_amdgcn_rcpf(run[i]);
-                {
-                    // per-chunk factors, from a scan across the block ends: after
-                    // two DPP row broadcasts lane t holds P_t = prod_{s <= t} g_s, so
-                    // E_J = P at lane 16J - 1 (J >= 1; E_0 = 1 is never read), D = P at
-                    // lane 63, and rho_{J1 J0} (blocks strictly between) is the block
-                    // total of lane 31 or 47, or their product.  Each value is written
-                    // by the lane that holds it.
-                    float pre[4] = {run[0], run[1], run[2], run[3]};
-                    wave_prefix_from_rows4(run, pre);
-                    if ((lane & 15) == 15 && (lane >> 4) < NB) {
-                        const int J = lane >> 4;   // E_{J+1} for J < NB - 1, D for the last block
-                        *reinterpret_cast<float4 *>(sE + (J + 1) * DK + cc) = make_float4(pre[0], pre[1], pre[2], pre[3]);
-                        // the block's total, for every token of the chunk below
-                        *reinterpret_cast<float4 *>(sTot + J * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
-                    }
-                    if constexpr (NB == 4) {
-                        // rho_{2,0} = tot_1 (lane 31), rho_{3,1} = tot_2 and rho_{3,0} = tot_1 tot_2 (lane 47)
-                        if (lane == 31)
-                            *reinterpret_cast<float4 *>(sRho + rho_index(2, 0) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
-                        float t12[4] = {run[0], run[1], run[2], run[3]};   // row 2: tot_1 (lane 31) times the row's products
-                        mul_bcast15_row2_4(run, t12);
-                        if (lane == 47) {
-                            *reinterpret_cast<float4 *>(sRho + rho_index(3, 1) * DK + cc) = make_float4(run[0], run[1], run[2], run[3]);
-                            *reinterpret_cast<float4 *>(sRho + rho_index(3, 0) * DK + cc) = make_float4(t12[0], t12[1], t12[2], t12[3]);
-                        }
-                    }
-                }
-                // the total of the token's own block and the product of the totals
-                // of the blocks after it, read back from the slots the block-end
-                // lanes just wrote.  The wave executes its LDS operations in
-                // order; the empty asm keeps the compiler from moving these reads
-                // (of values other lanes wrote) above those writes.
-                asm volatile("" ::: "memory");
-                float tb[4], after[4];
-                {
-                    const float4 b = *reinterpret_cast<const float4 *>(sTot + I * DK + cc);
-                    tb[0] = b.x; tb[1] = b.y; tb[2] = b.z; tb[3] = b.w;
-                    after[0] = after[1] = after[2] = after[3] = 1.f;
-#pragma unroll
-                    for (int m = 1; m < NB; ++m) {
-                        const float4 a = *reinterpret_cast<const float4 *>(sTot + (I + m) * DK + cc);
-                        after[0] *= a.x; after[1] *= a.y; after[2] *= a.z; after[3] *= a.w;
-                    }
-                }
-                float fq[4], fd[4], fk[4], fa[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // tokens past the end: zero operands (selects, not branches)
-                    const float rq = on ? run[i] : 0.f, rk = on ? rinv[i] : 0.f;
-                    fq[i] = apply_phi<PHI>(q[i]) * rq;
-                    fd[i] = apply_phi<PHI>(k[i]) * rk;
-                    fk[i] = fd[i] * tb[i];
-                    fa[i] = fk[i] * after[i];
-                }
-                if (in_tile) {
-                    st_group(sQ[nb] + t * LDK + cc, Gp::make(fq[0], fq[1], fq[2], fq[3]));
-                    st_group(sKd + t * LDK + cc, Gp::make(fd[0], fd[1], fd[2], fd[3]));
-                    st_group(sK + t * LDK + cc, Gp::make(fk[0], fk[1], fk[2], fk[3]));
-                    st_group(sKt + t * LDK + cc, Gp::make(fa[0], fa[1], fa[2], fa[3]));
-                }
-            }
-        }
-        if (state_wave && c >= 0) {
-            const int n = rows(c);
-#pragma unroll
-            for (int I = 0; I < NB; ++I) {
-                const int t = 16 * I + lr;
-                if (t < n)
-                    st_group(oh + static_cast<size_t>(c * C + t) * p.d_v + vb * DVB + 16 * wave + 4 * lg, Gp::make(ob[I]));
-            }
-        }
-        if constexpr (!GDMA) load_gates(min(c + 2, clast));
-        __syncthreads();
-
-        // ---- step C.  All waves: the scores of chunk c+1 (16x16 tiles, taken
-        // transposed so that a lane writes four consecutive columns of a row).
-        // GDMA: the state waves first issue the loads of chunk c+2's gate tile
-        // (every read of the tile, in step B, is behind the barrier above).
-        if constexpr (GDMA) {
-            if (state_wave && c + 2 < nchunks) dma_gates(c + 2);
-        }
-        if (prep) {
-            auto score_tile = [&](int tt) {   // tile (I, J) = (tt / NB, tt % NB)
-                const int I = tt / NB, J = tt % NB;
-                const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
-                if (J > I) {
-                    st_group(sP + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
-                    return;
-                }
-                f32x4 acc = zero4();
-                if (J == I)
-                    tile_mma_ll<DK>(acc, sKd + 16 * J * LDK, LDK, sQ[nb] + 16 * I * LDK, LDK, lane);
-                else if (J == I - 1)
-                    tile_mma_ll<DK>(acc, sK + 16 * J * LDK, LDK, sQ[nb] + 16 * I * LDK, LDK, lane);
-                else
-                    tile_mma_ll_scaled<DK>(acc, sK + 16 * J * LDK, LDK, sRho + rho_index(I, J) * DK,
-                                           sQ[nb] + 16 * I * LDK, LDK, lane);
-                st_group(sP + t * LDC + j0, Gp::make(j0 <= t ? acc[0] : 0.f, j0 + 1 <= t ? acc[1] : 0.f,
-                                                     j0 + 2 <= t ? acc[2] : 0.f, j0 + 3 <= t ? acc[3] : 0.f));
-            };
-            if constexpr (NB == 4 && NW == 8) {
-                // two tiles per wave (tile ids 4 I + J, a nibble each): the three
-                // rho-scaled tiles alone on the state waves (with a zero tile),
-                // the other helpers two plain products or one and a zero tile
-                // (order 8,1 | 12,2 | 13,3 | 15,6 | 0,4 | 5,9 | 10,7 | 14,11)
-                constexpr unsigned long long kOrder = 0xbe7a95406f3d2c18ull;
-                score_tile(static_cast<int>((kOrder >> (8 * wave)) & 15));
-                score_tile(static_cast<int>((kOrder >> (8 * wave + 4)) & 15));
-            } else {
-                for (int tt = wave; tt < NB * NB; tt += NW) score_tile(tt);
-            }
-        }
-        __syncthreads();
     }
 
     if (p.S_T && state_wave) {

@@ -66,6 +66,9 @@ __device__ __forceinline__ void store1(bf16_t *p, float x) { *p = f32_to_bf16(x)
 // s_waitcnt immediate (gfx9 encoding) that waits for every outstanding vector
 // memory load and leaves the LDS and export counters free.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// the same, leaving the n most recently issued vector memory loads in flight
+// (loads complete in the order they were issued)
+constexpr int wait_vmcnt(int n) { return kWaitVmcnt0 | (n & 15) | ((n >> 4) << 14); }
 
 // ------------------------------------------------------------- feature map
 
