@@ -283,8 +283,9 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     if (Tn > 0) prefetch(0);
 
     // The state waves keep a chunk's outputs in registers and store them after
-    // the next chunk's commit: the commit's wait on the global-memory counter
-    // (for the staged loads) then never waits for just-issued output stores.
+    // the next chunk's commit and prefetch: the commit's wait on the
+    // global-memory counter (for the staged loads) then never waits for
+    // just-issued output stores.
     f32x4 ob[NB];
     auto store_outputs = [&](int oc0) {
         const int on = min(C, Tn - oc0);
@@ -350,8 +351,11 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
             }
         }
         __syncthreads();
+        // the next chunk's loads first (a chunk past the end re-reads the last
+        // one, never used), then the stores: every path issues the same loads,
+        // so the compiler's waits for them stay exact and never cover stores
+        prefetch(min(c0 + C, ((Tn - 1) / C) * C));
         if (wave < WS && c0 > 0) store_outputs(c0 - C);
-        if (c0 + C < Tn) prefetch(c0 + C);
 
         if constexpr (GATED) {
             // ---- gate factors.  A wave takes four key channels of every token of
