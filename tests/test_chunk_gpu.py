@@ -185,6 +185,33 @@ def test_gdr_chunk_counts(dtype, d, chunk, T):
     assert max(errs.values()) <= TOL[dtype], errs
 
 
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("bf16", 64, 32), ("f32", 64, 64)])
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 128, 129, 191, 200])
+def test_gla_chunk_counts(dtype, d, chunk, T):
+    """Gated linear attention at one to four chunks, whole and ragged: the
+    two role loops run one iteration more than there are chunks (the first
+    prepares chunk 0), the helpers commit staged tiles even when nothing
+    follows, and the gate tile of a ragged last chunk re-reads its last row."""
+    w = wl.variant_workload(la.LA_GATED, dtype, d, d, chunk=chunk, phi=la.LA_PHI_ELU1, seed=73)
+    inp = wl.chunk_inputs(w, B=1, H=2, T=T, S0_std=0.1)
+    print("gla chunk counts", dtype, d, chunk, T, flush=True)
+    errs, _ = run_chunk(w, inp, chunk, B=1, H=2)
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 64, 64), ("f32", 32, 32)])
+@pytest.mark.parametrize("T", [1, 64, 65, 129, 200])
+def test_la_chunk_counts(dtype, d, chunk, T):
+    """Normalized linear attention at one to four chunks, whole and ragged (the
+    next chunk's loads are issued on every chunk, re-reading the last one past
+    the end), with an initial state and normalizer."""
+    w = wl.variant_workload(la.LA_NORMALIZED, dtype, d, d, chunk=chunk, phi=la.LA_PHI_ELU1, seed=79)
+    inp = wl.chunk_inputs(w, B=1, H=2, T=T, S0_std=0.1, z0=True)
+    print("la chunk counts", dtype, d, chunk, T, flush=True)
+    errs, _ = run_chunk(w, inp, chunk, B=1, H=2)
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
 def test_chunk_is_deterministic():
     w = wl.WORKLOADS["gdr_bf16_b4h16t8192d128"]
     inp = wl.chunk_inputs(w, B=1, H=4, T=1000)
