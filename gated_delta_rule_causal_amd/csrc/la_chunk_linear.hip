@@ -826,22 +826,52 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                 G4 sb[NCB];
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
+                // O^T = (Qhat E_I) S0^T + V^T P^T for the NB token blocks I at once
+                // (lane: values 16*wave + 4*lg..+3 of token 16 I + lr): each step
+                // issues NB independent products, and the V^T operand groups,
+                // the same for every block, are read once.  Each accumulator
+                // sums in the order of the single-block form.
 #pragma unroll
-                for (int I = 0; I < NB; ++I) {
-                    // O^T = (Qhat E_I) S0^T + V^T P^T: lane holds values 16*wave + 4*lg..+3
-                    // of token 16 I + lr
-                    f32x4 o = zero4();
-                    if (I == 0) tile_mma_rl_n<NCB>(o, sb, sQ[cur], LDK, NCB, lane);
-                    else tile_mma_rl_scaled<NCB>(o, sb, sQ[cur] + 16 * I * LDK, LDK, sE + I * DK, lane);
-                    const Op *prow = sP + (16 * I + lr) * LDC + 4 * lg;
+                for (int I = 0; I < NB; ++I) ob[I] = zero4();
+                {
+                    const int ko = 4 * lg;
+                    const Op *qr = sQ[cur] + lr * LDK + ko;
 #pragma unroll
-                    for (int t0 = 0; t0 + 32 <= C; t0 += 32)
-                        mma32(o, kt_group<0>(sV[cur], LDV, t0, 16 * wave, lane),
-                              kt_group<0>(sV[cur], LDV, t0 + 16, 16 * wave, lane), ld_group(prow + t0),
-                              ld_group(prow + t0 + 16));
-                    if constexpr (C % 32 == 16)
-                        mma16(o, kt_group<0>(sV[cur], LDV, C - 16, 16 * wave, lane), ld_group(prow + C - 16));
-                    ob[I] = o;
+                    for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            const Op *q = qr + 16 * I * LDK + 16 * s2;
+                            if (I == 0)
+                                mma32(ob[I], sb[s2], sb[s2 + 1], ld_group(q), ld_group(q + 16));
+                            else
+                                mma32(ob[I], sb[s2], sb[s2 + 1], scaled_group(q, sE + I * DK + 16 * s2 + ko),
+                                      scaled_group(q + 16, sE + I * DK + 16 * s2 + 16 + ko));
+                        }
+                    }
+                    if constexpr (NCB % 2 == 1) {
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            const Op *q = qr + 16 * I * LDK + 16 * (NCB - 1);
+                            if (I == 0) mma16(ob[I], sb[NCB - 1], ld_group(q));
+                            else mma16(ob[I], sb[NCB - 1], scaled_group(q, sE + I * DK + 16 * (NCB - 1) + ko));
+                        }
+                    }
+#pragma unroll
+                    for (int t0 = 0; t0 + 32 <= C; t0 += 32) {
+                        const G4 va = kt_group<0>(sV[cur], LDV, t0, 16 * wave, lane);
+                        const G4 vb2 = kt_group<0>(sV[cur], LDV, t0 + 16, 16 * wave, lane);
+#pragma unroll
+                        for (int I = 0; I < NB; ++I) {
+                            const Op *prow = sP + (16 * I + lr) * LDC + 4 * lg;
+                            mma32(ob[I], va, vb2, ld_group(prow + t0), ld_group(prow + t0 + 16));
+                        }
+                    }
+                    if constexpr (C % 32 == 16) {
+                        const G4 va = kt_group<0>(sV[cur], LDV, C - 16, 16 * wave, lane);
+#pragma unroll
+                        for (int I = 0; I < NB; ++I)
+                            mma16(ob[I], va, ld_group(sP + (16 * I + lr) * LDC + 4 * lg + C - 16));
+                    }
                 }
                 // S^T <- S^T diag(D) + K~a^T V, both operands by transposing reads
 #pragma unroll
