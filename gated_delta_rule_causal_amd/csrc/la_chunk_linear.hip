@@ -1108,6 +1108,7 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
 // ------------------------------------------------------------------ dispatch
 
 constexpr int kLinearWaves = 8;   // waves per workgroup
+constexpr int kGlaWaves = 12;     // waves per workgroup of the pipelined gated kernel (three per SIMD)
 
 constexpr int kComputeUnits = 256;
 
@@ -1160,9 +1161,9 @@ static hipError_t launch_linear_t(const ChunkArgs &a) {
         }
     }
     const int64_t blocks = static_cast<int64_t>(p.n_heads) * p.n_vblk * p.n_seg;
-    if constexpr (GATED && GlaLds<DT, DK, DVB, C, kLinearWaves>::FITS) {
-        hipLaunchKernelGGL((gla_pipelined_kernel<PHI, DT, DK, DVB, C, kLinearWaves>), dim3(static_cast<uint32_t>(blocks)),
-                           dim3(kLinearWaves * 64), 0, a.stream, p);
+    if constexpr (GATED && GlaLds<DT, DK, DVB, C, kGlaWaves>::FITS) {
+        hipLaunchKernelGGL((gla_pipelined_kernel<PHI, DT, DK, DVB, C, kGlaWaves>), dim3(static_cast<uint32_t>(blocks)),
+                           dim3(kGlaWaves * 64), 0, a.stream, p);
     } else {
         hipLaunchKernelGGL((linear_chunk_kernel<GATED, PHI, DT, DK, DVB, C, kLinearWaves>),
                            dim3(static_cast<uint32_t>(blocks)), dim3(kLinearWaves * 64), 0, a.stream, p);
