@@ -809,6 +809,14 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
             constexpr unsigned long long kOrder = 0xbe7a95406f3d2c18ull;
             score_tile(static_cast<int>((kOrder >> (8 * wave)) & 15));
             score_tile(static_cast<int>((kOrder >> (8 * wave + 4)) & 15));
+        } else if constexpr (NB == 4 && NW == 12) {
+            // one tile per wave, the rho-scaled ones alone on waves 0-2; waves
+            // 3-6 also take a zero tile (second entry 15: none; tile 15 is only
+            // ever a first entry)
+            constexpr unsigned long long kFirst = 0xb7e94fa50dc8ull, kSecond = 0xfffff6321fffull;
+            score_tile(static_cast<int>((kFirst >> (4 * wave)) & 15));
+            const int t2 = static_cast<int>((kSecond >> (4 * wave)) & 15);
+            if (t2 != 15) score_tile(t2);
         } else {
             for (int tt = wave; tt < NB * NB; tt += NW) score_tile(tt);
         }
