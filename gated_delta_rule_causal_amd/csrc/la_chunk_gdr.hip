@@ -680,7 +680,13 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
                 // step 2: one wave per diagonal block of chunk c+1's inverse; with 16x16
                 // tiles, the other helpers: its Q K^T tiles; HO: S0 Q^T of chunk c
                 if (has_next) {
-                    if (hw < NB) diag_block(hw);
+                    if (hw < NB) {
+                        // the diagonal blocks bound step 2: raised issue priority
+                        // over the waves they share a SIMD with
+                        __builtin_amdgcn_s_setprio(1);
+                        diag_block(hw);
+                        __builtin_amdgcn_s_setprio(0);
+                    }
                     else if constexpr (!S32) score_tiles(nxt, kn, false, WS + NB, NHW - NB);
                 }
                 if (HO && hw >= OJ0) qs_job(cur, hw - OJ0, oqs, oeb);
