@@ -34,6 +34,7 @@
 // block of DVB value channels); wave w keeps the transposed state slice of
 // its 16 value channels in matrix-core accumulators across the sequence.
 #include <algorithm>
+#include <type_traits>
 
 #include "la_chunk_common.hpp"
 
@@ -692,11 +693,13 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
     // step B, every wave: the gate factors of chunk c+1 (lane = token, four
     // channels per pass; the products along a 16-token block are 16-lane DPP
     // row scans)
-    auto gate_pass = [&](int c) {
-        if (c + 1 >= nchunks) return;
+    // A whole chunk takes the variant without the selects for tokens past the
+    // end (FULL: every token of the tile is on).
+    auto gate_pass_n = [&](int c, auto full) {
+        constexpr bool FULL = decltype(full)::value;
         const int nb = (c + 1) & 1, n1 = rows(c + 1);
         const int t = lane, I = t >> 4;
-        const bool in_tile = t < C, on = t < n1;
+        const bool in_tile = t < C, on = FULL ? in_tile : t < n1;
 #pragma unroll
         for (int it = 0; it < GI; ++it) {
             const int cc = 4 * wave + 4 * NW * it;
@@ -777,6 +780,11 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
                 st_group(sKt + t * LDK + cc, Gp::make(fa[0], fa[1], fa[2], fa[3]));
             }
         }
+    };
+    auto gate_pass = [&](int c) {
+        if (c + 1 >= nchunks) return;
+        if (rows(c + 1) == C) gate_pass_n(c, std::true_type{});
+        else gate_pass_n(c, std::false_type{});
     };
     // step C, every wave: the scores of chunk c+1 (16x16 tiles, taken
     // transposed so that a lane writes four consecutive columns of a row)
