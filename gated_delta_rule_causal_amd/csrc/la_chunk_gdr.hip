@@ -347,33 +347,60 @@ __global__ void __launch_bounds__(NW * 64) gdr_chunk_kernel(const ChunkParams p)
             else out(false);   // every column s precedes the row t
         }
     };
-    // diagonal 16x16 block `blk` of T = (I + A)^{-1} by forward substitution,
-    // written over A's block.  One wave per block: lane 4n + p owns rows
-    // 4p..4p+3 of column n, so each step's row-times-column product is four
-    // multiply-adds and a sum over the lane quad (two DPP adds).
+    // diagonal 16x16 block `blk` of T = (I + A)^{-1}, written over A's block,
+    // one wave per block, in 8x8 halves: with A = [[A00, 0], [A10, A11]],
+    // T = [[T00, 0], [-T11 A10 T00, T11]], Thh = (I + Ahh)^{-1}.
     auto diag_block = [&](int blk) {
-        const int n = lane >> 2, pp = lane & 3;
         float *Ab = sA + 16 * blk * LDA + 16 * blk;
-        float x[4];
+        {
+            // T00 and T11 by forward substitution, one per half wave: lane
+            // 32h + 4n + pp owns rows 2pp, 2pp + 1 of column n of half h, so
+            // each step's row-times-column product is two multiply-adds and a
+            // sum over the lane quad (two DPP adds)
+            const int h = lane >> 5, n = (lane >> 2) & 7, pp = lane & 3, o = 8 * h;
+            float x[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = 4 * pp + i == n ? 1.f : 0.f;
-        // every row's four entries are read up front: one LDS latency instead
-        // of one per step of the substitution
-        float4 rows[15];
+            for (int i = 0; i < 2; ++i) x[i] = 2 * pp + i == n ? 1.f : 0.f;
+            // every row's two entries are read up front: one LDS latency instead
+            // of one per step
+            float2 rows[7];
 #pragma unroll
-        for (int t = 1; t < 16; ++t) rows[t - 1] = *reinterpret_cast<const float4 *>(Ab + t * LDA + 4 * pp);
+            for (int t = 1; t < 8; ++t) rows[t - 1] = *reinterpret_cast<const float2 *>(Ab + (o + t) * LDA + o + 2 * pp);
 #pragma unroll
-        for (int t = 1; t < 16; ++t) {
-            const float4 row = rows[t - 1];
-            // A's diagonal and upper part are zero, so the not yet computed
-            // entries (zero) and x[n] = 1 above row t add nothing
-            float part = (row.x * x[0] + row.y * x[1]) + (row.z * x[2] + row.w * x[3]);
-            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0xB1, 0xF, 0xF, true));  // lanes ^1
-            part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x4E, 0xF, 0xF, true));  // lanes ^2
-            if (pp == (t >> 2) && t > n) x[t & 3] = -part;
+            for (int t = 1; t < 8; ++t) {
+                // A's diagonal and upper part are zero, so the not yet computed
+                // entries (zero) and x[n] = 1 above row t add nothing
+                float part = rows[t - 1].x * x[0] + rows[t - 1].y * x[1];
+                part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0xB1, 0xF, 0xF, true));  // lanes ^1
+                part += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(part), 0x4E, 0xF, 0xF, true));  // lanes ^2
+                if (pp == (t >> 1) && t > n) x[t & 1] = -part;
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) Ab[(o + 2 * pp + i) * LDA + o + n] = x[i];
         }
+        // the lower-left 8x8, lane 8r + c owning entry (r, c): Y = A10 T00, then
+        // -T11 Y.  Lanes read what other lanes of the wave wrote just before;
+        // the wave's LDS accesses complete in order, and the empty asm
+        // statements keep the compiler from reordering them.
+        asm volatile("" ::: "memory");
+        const int r = lane >> 3, c = lane & 7;
+        const float *row = Ab + (8 + r) * LDA;
+        const float4 a0 = *reinterpret_cast<const float4 *>(row), a1 = *reinterpret_cast<const float4 *>(row + 4);
+        const float4 u0 = *reinterpret_cast<const float4 *>(row + 8), u1 = *reinterpret_cast<const float4 *>(row + 12);
+        float col[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Ab[(4 * pp + i) * LDA + n] = x[i];
+        for (int b = 0; b < 8; ++b) col[b] = Ab[b * LDA + c];
+        const float y = ((a0.x * col[0] + a0.y * col[1]) + (a0.z * col[2] + a0.w * col[3])) +
+                        ((a1.x * col[4] + a1.y * col[5]) + (a1.z * col[6] + a1.w * col[7]));
+        asm volatile("" ::: "memory");
+        Ab[(8 + r) * LDA + c] = y;
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int b = 0; b < 8; ++b) col[b] = Ab[(8 + b) * LDA + c];
+        const float z = ((u0.x * col[0] + u0.y * col[1]) + (u0.z * col[2] + u0.w * col[3])) +
+                        ((u1.x * col[4] + u1.y * col[5]) + (u1.z * col[6] + u1.w * col[7]));
+        asm volatile("" ::: "memory");
+        Ab[(8 + r) * LDA + c] = -z;
     };
     // off-diagonal blocks of T into buffer `buf`, one block column per helper wave:
     // T_ij = -T_ii sum_{m=j}^{i-1} A_im T_mj (matrix cores in the operand type)
