@@ -16,8 +16,9 @@
 //   S_C = e^{b_C} S0 + U^T diag(e^{b_C - b}) K.
 // Every exponent used is <= 0 (the kernel keeps b in base 2 and evaluates
 // each factor with one hardware exp2).  T = (I + A)^{-1} depends on K, g and beta
-// only; it is formed per chunk from 16x16 blocks: the diagonal blocks by
-// forward substitution, the off-diagonal blocks by
+// only; it is formed per chunk from 16x16 blocks: each diagonal block from its
+// 8x8 diagonal halves (forward substitution) and its lower-left 8x8
+// -T_11 A_10 T_00, the off-diagonal blocks by
 // T_ij = -T_ii sum_{j<=m<i} A_im T_mj, all in float32.
 //
 // Work decomposition: one workgroup per (b, h, block of DVB value channels);
