@@ -90,15 +90,18 @@ struct TilePrefetch {
 // address each lane gives; lds_base must be wave-uniform.  It is issued from
 // inline assembly, so the compiler neither waits for it nor counts it: the
 // issuing wave waits for it (s_waitcnt on the vector-memory counter) before
-// the barrier that hands the tile to its readers.
+// the barrier that hands the tile to its readers.  The load reads M0, which the
+// compiler sets with a scalar move right before the statement; gfx9 needs one
+// wait state between the two, and the compiler does not insert it for inline
+// assembly, so the statement starts with one.
 __device__ __forceinline__ void lds_dma16(const void *src, unsigned lds_base) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
 // The same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
 // (global address = base + offset), so that a caller whose lane offsets do
 // not change between calls keeps them in registers and moves only the base.
 __device__ __forceinline__ void lds_dma16(const void *base, unsigned offset, unsigned lds_base) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base), "{m0}"(lds_base) : "memory");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(offset), "s"(base), "{m0}"(lds_base) : "memory");
 }
 // LDS byte address of a __shared__ object (the low half of its generic address)
 template <class T>
