@@ -13,8 +13,10 @@ Two independent implementations live here:
   pages state alongside the recurrences.  They exist only to pin the
   recurrence (``tests/test_oracle_pins.py``).
 
-Variant codes: 0 normalized linear attention, 1 gated linear attention,
-2 gated delta rule.  phi codes: 0 identity, 1 elu(x)+1.
+Variant codes: 0 normalized linear attention (optionally with a fixed
+per-head decay), 1 gated linear attention, 2 gated delta rule, 3 retention
+(fixed per-head decay, no normalizer), 4 gated delta rule with a per-channel
+decay.  phi codes: 0 identity, 1 elu(x)+1.
 """
 from __future__ import annotations
 
@@ -28,8 +30,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-NORMALIZED, GATED, GATED_DELTA = 0, 1, 2
+NORMALIZED, GATED, GATED_DELTA, RETENTION, KDA = 0, 1, 2, 3, 4
 PHI_IDENTITY, PHI_ELU1 = 0, 1
+
+
+def default_phi(variant: int) -> int:
+    return PHI_ELU1 if variant in (NORMALIZED, GATED) else PHI_IDENTITY
 
 
 def build(force: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
@@ -54,6 +60,20 @@ def _ptr(a):
     if a is None:
         return None
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _check_gate(variant, gate, beta, lead, dk):
+    """Shapes of gate / beta per variant (lead: (B, H, T) or (B, H))."""
+    if variant in (GATED, KDA):
+        assert gate is not None and gate.shape == lead + (dk,)
+    elif variant == GATED_DELTA:
+        assert gate is not None and gate.shape == lead
+    else:
+        assert gate is None or gate.shape == (lead[1],)
+    if variant in (GATED_DELTA, KDA):
+        assert beta is not None and beta.shape == lead
+    else:
+        assert beta is None
 
 
 class OracleLib:
@@ -84,23 +104,20 @@ class OracleLib:
                 phi_kind=None, nthreads=0):
         """Token-by-token forward over whole sequences.
 
-        q, k: (B,H,T,d_k); v: (B,H,T,d_v); gate: (B,H,T,d_k) for GATED,
-        (B,H,T) for GATED_DELTA; beta: (B,H,T) for GATED_DELTA;
-        S0: (B,H,d_v,d_k); z0: (B,H,d_k) (NORMALIZED only).  Returns
+        q, k: (B,H,T,d_k); v: (B,H,T,d_v); gate: (B,H,T,d_k) for GATED
+        and KDA, (B,H,T) for GATED_DELTA, (H,) or None for NORMALIZED and
+        RETENTION (a fixed per-head decay); beta: (B,H,T) for GATED_DELTA
+        and KDA; S0: (B,H,d_v,d_k); z0: (B,H,d_k) (NORMALIZED only).  Returns
         (out, S_T, z_T) as float64; z_T is None unless NORMALIZED.
         """
         if phi_kind is None:
-            phi_kind = PHI_IDENTITY if variant == GATED_DELTA else PHI_ELU1
+            phi_kind = default_phi(variant)
         q, k, v = _f64(q), _f64(k), _f64(v)
         gate, beta, S0, z0 = _f64(gate), _f64(beta), _f64(S0), _f64(z0)
         B, H, T, dk = q.shape
         dv = v.shape[-1]
         assert k.shape == (B, H, T, dk) and v.shape == (B, H, T, dv)
-        if variant == GATED:
-            assert gate is not None and gate.shape == (B, H, T, dk)
-        if variant == GATED_DELTA:
-            assert gate is not None and gate.shape == (B, H, T)
-            assert beta is not None and beta.shape == (B, H, T)
+        _check_gate(variant, gate, beta, (B, H, T), dk)
         if S0 is not None:
             assert S0.shape == (B, H, dv, dk)
         if z0 is not None:
@@ -120,18 +137,19 @@ class OracleLib:
         """One recurrent step for every head, updating S (and z) IN PLACE.
 
         S: (B,H,d_v,d_k) float64 C-contiguous (modified); q, k: (B,H,d_k);
-        v: (B,H,d_v); gate: (B,H,d_k) GATED / (B,H) GATED_DELTA;
-        beta: (B,H); z: (B,H,d_k) float64 (NORMALIZED, modified).
-        Returns out (B,H,d_v).
+        v: (B,H,d_v); gate: (B,H,d_k) GATED and KDA / (B,H) GATED_DELTA /
+        (H,) or None NORMALIZED and RETENTION; beta: (B,H); z: (B,H,d_k)
+        float64 (NORMALIZED, modified).  Returns out (B,H,d_v).
         """
         if phi_kind is None:
-            phi_kind = PHI_IDENTITY if variant == GATED_DELTA else PHI_ELU1
+            phi_kind = default_phi(variant)
         assert S.dtype == np.float64 and S.flags.c_contiguous
         if variant == NORMALIZED:
             assert z is not None and z.dtype == np.float64 and z.flags.c_contiguous
         q, k, v, gate, beta = _f64(q), _f64(k), _f64(v), _f64(gate), _f64(beta)
         B, H, dv, dk = S.shape
         assert q.shape == (B, H, dk) and k.shape == (B, H, dk) and v.shape == (B, H, dv)
+        _check_gate(variant, gate, beta, (B, H), dk)
         out = np.empty((B, H, dv), np.float64)
         rc = self._lib.oracle_decode_step(variant, phi_kind, B, H, dk, dv, _ptr(q), _ptr(k),
                                           _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),

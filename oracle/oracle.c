@@ -33,6 +33,25 @@
  *        equal to page "Module 18 Beyond attention", section 18.2,
  *          S_t = g_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T.
  *
+ *      With a per-head decay gamma_h (gate of shape (H,), shared by the
+ *      batch; NULL means gamma_h = 1) both accumulators decay before the
+ *      write, page "Beyond -- Linear attention and recurrent memory",
+ *      section "Fixed decay versus an input-dependent gate":
+ *          S_t = gamma_h S_{t-1} + phi(k_t) v_t^T
+ *          z_t = gamma_h z_{t-1} + phi(k_t)
+ *   3  retention: the same fixed per-head decay without a normalizer, the
+ *      constant gate of page "Ch. 11 Linear attention and Hyena", section
+ *      11.3 (RetNet bullet):
+ *          S_t = gamma_h S_{t-1} + phi(k_t) v_t^T,   y_t = S_t^T phi(q_t)
+ *      (gate (H,) or NULL = 1; phi identity by default).
+ *   4  gated delta rule with a per-key-channel (diagonal) decay alpha_t,
+ *      the finer-grained gate of page "Beyond -- Linear attention and
+ *      recurrent memory", section "From fixed decay to KDA's gated delta
+ *      write", in the decay-first order of variant 2 (d_v x d_k state):
+ *          S~_t = S_{t-1} diag(alpha_t)
+ *          S_t  = S~_t + beta_t (v_t - S~_t k_t) k_t^T,   o_t = S_t q_t
+ *      (gate alpha (B, H, T, d_k), beta (B, H, T)).
+ *
  * phi codes: 0 identity, 1 elu(x)+1 (page "Beyond -- Linear attention and
  * recurrent memory", section "The big idea": phi(x) = elu(x) + 1).
  *
@@ -41,8 +60,10 @@
  * and 1 keep their state internally in the pages' own d_k x d_v
  * orientation and transpose only when reading S0 / writing S_T.
  *
- * Per-token tensors are (B, H, T, d) row-major.  gate: variant 1 -> gamma
- * (B, H, T, d_k); variant 2 -> g (B, H, T).  beta: variant 2 -> (B, H, T).
+ * Per-token tensors are (B, H, T, d) row-major.  gate: variant 0 and 3 ->
+ * gamma_h (H,) or NULL; variant 1 -> gamma (B, H, T, d_k); variant 2 -> g
+ * (B, H, T); variant 4 -> alpha (B, H, T, d_k).  beta: variants 2 and 4 ->
+ * (B, H, T).
  */
 #include <math.h>
 #include <stdlib.h>
@@ -69,7 +90,7 @@ static void head_forward(int variant, int phi, int T, int dk, int dv,
                          double *out, double *ST, double *zT,
                          double *work /* dk*dv + 3*dk + dv doubles */)
 {
-    double *S = work;             /* variant 0/1: [c][i] (d_k x d_v); variant 2: [i][c] */
+    double *S = work;             /* variant 0/1/3: [c][i] (d_k x d_v); variant 2/4: [i][c] */
     double *z = S + (size_t)dk * dv;
     double *fq = z + dk;
     double *fk = fq + dk;
@@ -79,8 +100,8 @@ static void head_forward(int variant, int phi, int T, int dk, int dv,
     for (int i = 0; i < dv; ++i)
         for (int c = 0; c < dk; ++c) {
             double s = S0 ? S0[(size_t)i * dk + c] : 0.0;
-            if (variant == 2) S[(size_t)i * dk + c] = s;
-            else              S[(size_t)c * dv + i] = s;
+            if (variant == 2 || variant == 4) S[(size_t)i * dk + c] = s;
+            else                              S[(size_t)c * dv + i] = s;
         }
     for (int c = 0; c < dk; ++c) z[c] = z0 ? z0[c] : 0.0;
 
@@ -92,10 +113,12 @@ static void head_forward(int variant, int phi, int T, int dk, int dv,
 
         if (variant == 0) {
             for (int c = 0; c < dk; ++c) { fq[c] = phi_apply(phi, qt[c]); fk[c] = phi_apply(phi, kt[c]); }
-            /* S_t = S_{t-1} + phi(k_t) v_t^T ;  z_t = z_{t-1} + phi(k_t) */
+            /* S_t = gamma_h S_{t-1} + phi(k_t) v_t^T ;  z_t = gamma_h z_{t-1} + phi(k_t)
+               (gamma_h = 1 without a gate) */
+            const double gam = gate ? gate[0] : 1.0;
             for (int c = 0; c < dk; ++c) {
-                for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] += fk[c] * vt[i];
-                z[c] += fk[c];
+                for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] = gam * S[(size_t)c * dv + i] + fk[c] * vt[i];
+                z[c] = gam * z[c] + fk[c];
             }
             /* out_t = phi(q_t)^T S_t / phi(q_t)^T z_t */
             double den = 0.0;
@@ -117,6 +140,42 @@ static void head_forward(int variant, int phi, int T, int dk, int dv,
                 double y = 0.0;
                 for (int c = 0; c < dk; ++c) y += fq[c] * S[(size_t)c * dv + i];
                 ot[i] = y;
+            }
+        } else if (variant == 3) {
+            for (int c = 0; c < dk; ++c) { fq[c] = phi_apply(phi, qt[c]); fk[c] = phi_apply(phi, kt[c]); }
+            /* S_t = gamma_h S_{t-1} + phi(k_t) v_t^T */
+            const double gam = gate ? gate[0] : 1.0;
+            for (int c = 0; c < dk; ++c)
+                for (int i = 0; i < dv; ++i)
+                    S[(size_t)c * dv + i] = gam * S[(size_t)c * dv + i] + fk[c] * vt[i];
+            /* y_t = S_t^T phi(q_t) */
+            for (int i = 0; i < dv; ++i) {
+                double y = 0.0;
+                for (int c = 0; c < dk; ++c) y += fq[c] * S[(size_t)c * dv + i];
+                ot[i] = y;
+            }
+        } else if (variant == 4) {
+            const double *alpha = gate + (size_t)t * dk;
+            const double bw = beta[t];
+            /* S~ = S_{t-1} diag(alpha_t): key channel c of every row decays by alpha_tc */
+            for (int i = 0; i < dv; ++i)
+                for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] *= alpha[c];
+            /* prediction S~ k_t */
+            for (int i = 0; i < dv; ++i) {
+                double acc = 0.0;
+                for (int c = 0; c < dk; ++c) acc += S[(size_t)i * dk + c] * kt[c];
+                pred[i] = acc;
+            }
+            /* S_t = S~ + beta_t (v_t - S~ k_t) k_t^T */
+            for (int i = 0; i < dv; ++i) {
+                const double err = bw * (vt[i] - pred[i]);
+                for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] += err * kt[c];
+            }
+            /* o_t = S_t q_t */
+            for (int i = 0; i < dv; ++i) {
+                double acc = 0.0;
+                for (int c = 0; c < dk; ++c) acc += S[(size_t)i * dk + c] * qt[c];
+                ot[i] = acc;
             }
         } else {
             const double a = gate[t];
@@ -146,7 +205,7 @@ static void head_forward(int variant, int phi, int T, int dk, int dv,
     if (ST)
         for (int i = 0; i < dv; ++i)
             for (int c = 0; c < dk; ++c)
-                ST[(size_t)i * dk + c] = (variant == 2) ? S[(size_t)i * dk + c] : S[(size_t)c * dv + i];
+                ST[(size_t)i * dk + c] = (variant == 2 || variant == 4) ? S[(size_t)i * dk + c] : S[(size_t)c * dv + i];
     if (zT)
         for (int c = 0; c < dk; ++c) zT[c] = z[c];
 }
@@ -155,12 +214,23 @@ static int check_args(int variant, int phi, int B, int H, int T, int dk, int dv,
                       const double *q, const double *k, const double *v,
                       const double *gate, const double *beta, const double *out)
 {
-    if (variant < 0 || variant > 2 || phi < 0 || phi > 1) return 1;
+    if (variant < 0 || variant > 4 || phi < 0 || phi > 1) return 1;
     if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
     if ((size_t)B * H * T > 0 && (!q || !k || !v || !out)) return 1;
     if (variant == 1 && T > 0 && !gate) return 1;
-    if (variant == 2 && T > 0 && (!gate || !beta)) return 1;
+    if ((variant == 2 || variant == 4) && T > 0 && (!gate || !beta)) return 1;
     return 0;
+}
+
+/* The gate values of flat head h = b * H + hh: per token and channel
+   (variants 1, 4), per token (variant 2), or the head's one decay (variants
+   0 and 3, shared by the batch; NULL = no decay). */
+static const double *head_gate(int variant, const double *gate, long h, int H, int T, int dk)
+{
+    if (!gate) return NULL;
+    if (variant == 1 || variant == 4) return gate + (size_t)h * T * dk;
+    if (variant == 2) return gate + (size_t)h * T;
+    return gate + (h % H);
 }
 
 /*
@@ -193,8 +263,8 @@ int oracle_forward(int variant, int phi, int B, int H, int T, int dk, int dv,
             if (!work) continue;
             head_forward(variant, phi, T, dk, dv,
                          q + (size_t)h * T * dk, k + (size_t)h * T * dk, v + (size_t)h * T * dv,
-                         variant == 1 ? gate + (size_t)h * T * dk : (variant == 2 ? gate + (size_t)h * T : NULL),
-                         variant == 2 ? beta + (size_t)h * T : NULL,
+                         head_gate(variant, gate, h, H, T, dk),
+                         (variant == 2 || variant == 4) ? beta + (size_t)h * T : NULL,
                          S0 ? S0 + (size_t)h * dv * dk : NULL,
                          (variant == 0 && z0) ? z0 + (size_t)h * dk : NULL,
                          out + (size_t)h * T * dv,

@@ -154,3 +154,102 @@ def gdr_ut_form(q, k, v, g, beta, S0=None):
     tail = G[T - 1] if T > 0 else np.zeros(0)          # prod_{i=j+1}^{T} g_i
     S_T = gcum[-1] * S0 + U.T @ (tail[:, None] * k) if T > 0 else S0.copy()
     return out, S_T
+
+
+def decay_weights(T, gamma):
+    """W_tj = gamma^(t-j) for j <= t, else 0: the distance-dependent weights
+    of a fixed per-head decay (page "Beyond -- Linear attention and recurrent
+    memory", section "Pitfalls to expect": the parallel form applies the
+    geometric decay gamma^(t-i))."""
+    lag = np.arange(T)[:, None] - np.arange(T)[None, :]
+    return np.where(lag >= 0, float(gamma) ** np.maximum(lag, 0), 0.0)
+
+
+def la_decayed_masked(q, k, v, gamma, S0=None, z0=None, phi=phi_elu1):
+    """Normalized linear attention with a fixed per-head decay, parallel form.
+
+    Page "Beyond -- Linear attention and recurrent memory", section "Fixed
+    decay versus an input-dependent gate": S and z both decay by gamma before
+    each write, so the masked scores carry gamma^(t-j) in numerator and
+    denominator alike.  Unrolling from (S0, z0) (d_k x d_v, d_k) adds
+    gamma^(t+1) phi(q_t)^T S0 and gamma^(t+1) phi(q_t)^T z0 (t counted from 0).
+    Returns out (T, d_v).
+    """
+    Qf, Kf = phi(q), phi(k)
+    T = q.shape[0]
+    scores = decay_weights(T, gamma) * (Qf @ Kf.T)
+    num = scores @ v
+    den = scores.sum(axis=1)
+    lead = float(gamma) ** np.arange(1, T + 1)
+    if S0 is not None:
+        num = num + lead[:, None] * (Qf @ S0)
+    if z0 is not None:
+        den = den + lead * (Qf @ z0)
+    return num / den[:, None]
+
+
+def retention_masked(q, k, v, gamma, S0=None, phi=None):
+    """Constant per-head gate, no normalizer: y = (W o (phi(Q) phi(K)^T)) V with
+    the Toeplitz weights gamma^(t-j) (page "Ch. 11 Linear attention and
+    Hyena", section 11.3, RetNet bullet), plus gamma^(t+1) phi(q_t)^T S0 for an
+    initial state S0 (d_k x d_v).  phi defaults to the identity.
+    Returns out (T, d_v).
+    """
+    f = (lambda x: np.asarray(x, np.float64)) if phi is None else phi
+    Qf, Kf = f(q), f(k)
+    T = q.shape[0]
+    out = (decay_weights(T, gamma) * (Qf @ Kf.T)) @ v
+    if S0 is not None:
+        out = out + (float(gamma) ** np.arange(1, T + 1))[:, None] * (Qf @ S0)
+    return out
+
+
+def kda_product_form(q, k, v, alpha, beta, S0=None):
+    """Gated delta rule with a per-key-channel decay, explicit transition form.
+
+    The decay-first delta write of page "Module 18 Beyond attention", section
+    18.2, with the scalar gate replaced by the diagonal one of page "Beyond --
+    Linear attention and recurrent memory", section "From fixed decay to KDA's
+    gated delta write": S_t = S_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T)
+    + beta_t v_t k_t^T (d_v x d_k state), o_t = S_t q_t.
+    Returns (out (T, d_v), S_T (d_v, d_k)).
+    """
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk)) if S0 is None else np.array(S0, np.float64)
+    I = np.eye(dk)
+    out = np.empty((T, dv))
+    for t in range(T):
+        kt = k[t][:, None]
+        S = S @ np.diag(alpha[t]) @ (I - beta[t] * (kt @ kt.T)) + beta[t] * (v[t][:, None] @ kt.T)
+        out[t] = S @ q[t]
+    return out, S
+
+
+def kda_ut_form(q, k, v, alpha, beta, S0=None):
+    """The per-channel-decay delta rule over the whole sequence as one
+    unit-lower-triangular solve (derived here by unrolling, not printed on
+    the pages).  With D_tjc = prod_{i=j+1}^t alpha_ic and A_c = prod_{i<=t}
+    alpha_ic, pseudo-values u_t = beta_t (v_t - S_{t-1} diag(alpha_t) k_t)
+    give S_t = S0 diag(A_t) + sum_{j<=t} u_j (k_j o D_tj)^T, hence
+      (I + A) U = diag(beta) V - diag(beta) (K o A) S0^T,
+      A_tj = beta_t sum_c k_tc k_jc D_tjc  (j < t),
+      O = (Q o A) S0^T + P U,   P_tj = sum_c q_tc k_jc D_tjc  (j <= t).
+    Returns (out (T, d_v), S_T (d_v, d_k)).
+    """
+    T, dk = k.shape
+    dv = v.shape[1]
+    S0 = np.zeros((dv, dk)) if S0 is None else np.asarray(S0, np.float64)
+    D = gla_decay(alpha)                                # [t, j, c], 0 above the diagonal
+    Acum = np.cumprod(alpha, axis=0)                    # prod_{i<=t} alpha_i
+    KK = np.einsum("tc,tjc,jc->tj", k, D, k)
+    A = np.tril(beta[:, None] * KK, -1)
+    rhs = beta[:, None] * (v - (k * Acum) @ S0.T)
+    U = np.linalg.solve(np.eye(T) + A, rhs)
+    P = np.einsum("tc,tjc,jc->tj", q, D, k)
+    out = (q * Acum) @ S0.T + P @ U
+    if T == 0:
+        return out, S0.copy()
+    tail = D[T - 1]                                     # [j, c] = prod_{i=j+1}^{T} alpha_ic
+    S_T = S0 * Acum[T - 1][None, :] + U.T @ (k * tail)
+    return out, S_T

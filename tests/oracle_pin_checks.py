@@ -16,7 +16,7 @@ import os
 
 import numpy as np
 
-from oracle import GATED, GATED_DELTA, NORMALIZED, PHI_ELU1, PHI_IDENTITY
+from oracle import GATED, GATED_DELTA, KDA, NORMALIZED, PHI_ELU1, PHI_IDENTITY, RETENTION
 from oracle import parallel_forms as pf
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -266,6 +266,166 @@ def check_gdr_matches_ut_form(orc):
     assert _maxdiff(S_T[0, 0], rS) <= TOL
 
 
+# ------------------------------------- fixed per-head decay (normalized, retention)
+
+def check_la_decay_matches_masked(orc):
+    """S and z both decay by gamma_h: the decayed T x T form, per head, at T=64
+    and T=512, with and without an initial state (B = 2 shares the decays)."""
+    for T, dk, dv, seed in ((64, 16, 16, 701), (512, 16, 8, 702)):
+        r = _rng(seed)
+        B, H = 2, 2
+        q, k = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk))
+        v = r.standard_normal((B, H, T, dv))
+        gam = np.array([0.97, 0.8])
+        S0 = r.standard_normal((B, H, dv, dk))
+        z0 = np.abs(r.standard_normal((B, H, dk))) + 1.0
+        for with_state in (False, True):
+            out, S_T, z_T = orc.forward(NORMALIZED, q, k, v, gate=gam, S0=S0 if with_state else None,
+                                        z0=z0 if with_state else None)
+            for b in range(B):
+                for h in range(H):
+                    ref = pf.la_decayed_masked(q[b, h], k[b, h], v[b, h], gam[h],
+                                               S0=S0[b, h].T if with_state else None,
+                                               z0=z0[b, h] if with_state else None)
+                    assert _maxdiff(out[b, h], ref) <= TOL, _maxdiff(out[b, h], ref)
+                    if not with_state:
+                        # unrolled: S_T = sum_j gamma^(T-1-j) v_j phi(k_j)^T, z_T likewise
+                        w = gam[h] ** np.arange(T - 1, -1, -1)
+                        Kf = pf.phi_elu1(k[b, h])
+                        assert _maxdiff(S_T[b, h], (v[b, h] * w[:, None]).T @ Kf) <= TOL * 10
+                        assert _maxdiff(z_T[b, h], w @ Kf) <= TOL * 10
+
+
+def check_la_unit_decay_is_undecayed(orc):
+    """gamma_h = 1 reproduces the undecayed normalized variant exactly."""
+    r = _rng(703)
+    q, k, v = (r.standard_normal((2, 3, 30, 8)) for _ in range(3))
+    a = orc.forward(NORMALIZED, q, k, v)
+    b = orc.forward(NORMALIZED, q, k, v, gate=np.ones(3))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def check_la_decay_equal_keys_give_weighted_mean(orc):
+    """Equal keys: out_t = sum_i gamma^(t-i) v_i / sum_i gamma^(t-i)."""
+    r = _rng(704)
+    T, d, g = 40, 8, 0.85
+    q = r.standard_normal((1, 1, T, d))
+    k = np.broadcast_to(r.standard_normal(d), (1, 1, T, d)).copy()
+    v = r.standard_normal((1, 1, T, d))
+    out, _, _ = orc.forward(NORMALIZED, q, k, v, gate=np.array([g]))
+    for t in (0, 1, 17, T - 1):
+        w = g ** np.arange(t, -1, -1)
+        assert _maxdiff(out[0, 0, t], (w @ v[0, 0, :t + 1]) / w.sum()) <= TOL
+
+
+def check_retention_matches_toeplitz(orc):
+    for phi_kind, phi in ((PHI_IDENTITY, None), (PHI_ELU1, pf.phi_elu1)):
+        r = _rng(705 + phi_kind)
+        B, H, T, dk, dv = 2, 2, 64, 12, 7
+        q, k = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk))
+        v = r.standard_normal((B, H, T, dv))
+        gam = np.array([0.9, 0.6])
+        S0 = r.standard_normal((B, H, dv, dk))
+        out, _, _ = orc.forward(RETENTION, q, k, v, gate=gam, S0=S0, phi_kind=phi_kind)
+        for b in range(B):
+            for h in range(H):
+                ref = pf.retention_masked(q[b, h], k[b, h], v[b, h], gam[h], S0=S0[b, h].T, phi=phi)
+                assert _maxdiff(out[b, h], ref) <= TOL * 10, _maxdiff(out[b, h], ref)
+
+
+def check_retention_is_gla_with_constant_gate(orc):
+    """A per-head constant gamma is gated linear attention with that gate everywhere."""
+    r = _rng(707)
+    B, H, T, dk, dv = 1, 3, 45, 8, 5
+    q, k = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk))
+    v = r.standard_normal((B, H, T, dv))
+    gam = np.array([0.99, 0.5, 0.05])
+    S0 = r.standard_normal((B, H, dv, dk))
+    a, Sa, _ = orc.forward(RETENTION, q, k, v, gate=gam, S0=S0, phi_kind=PHI_ELU1)
+    full = np.broadcast_to(gam[None, :, None, None], (B, H, T, dk)).copy()
+    b, Sb, _ = orc.forward(GATED, q, k, v, gate=full, S0=S0, phi_kind=PHI_ELU1)
+    assert _maxdiff(a, b) <= TOL and _maxdiff(Sa, Sb) <= TOL
+
+
+def check_retention_geometric_sum(orc):
+    """One key and one value written T times: S_T = v phi(k)^T (1 - g^T) / (1 - g)."""
+    r = _rng(708)
+    T, dk, dv, g = 25, 6, 4, 0.7
+    key, val = r.standard_normal(dk), r.standard_normal(dv)
+    k = np.broadcast_to(key, (1, 1, T, dk)).copy()
+    v = np.broadcast_to(val, (1, 1, T, dv)).copy()
+    _, S_T, _ = orc.forward(RETENTION, np.zeros((1, 1, T, dk)), k, v, gate=np.array([g]))
+    assert _maxdiff(S_T[0, 0], np.outer(val, key) * (1 - g ** T) / (1 - g)) <= TOL
+
+
+# ------------------------------------- delta rule with a per-channel decay (KDA)
+
+def _kda_inputs(r, B, H, T, dk, dv, mean=2.0):
+    q = r.standard_normal((B, H, T, dk))
+    k = _unit(r.standard_normal((B, H, T, dk)))
+    v = r.standard_normal((B, H, T, dv))
+    a = _sigmoid(r.normal(mean, 1.0, (B, H, T, dk)))
+    b = _sigmoid(r.normal(0.0, 1.0, (B, H, T)))
+    return q, k, v, a, b
+
+
+def check_kda_matches_product_form(orc):
+    for T, dk, dv, seed in ((64, 16, 16, 801), (40, 12, 5, 802)):
+        r = _rng(seed)
+        q, k, v, a, b = _kda_inputs(r, 1, 2, T, dk, dv)
+        S0 = r.standard_normal((1, 2, dv, dk))
+        out, S_T, _ = orc.forward(KDA, q, k, v, gate=a, beta=b, S0=S0)
+        for h in range(2):
+            ro, rS = pf.kda_product_form(q[0, h], k[0, h], v[0, h], a[0, h], b[0, h], S0[0, h])
+            assert _maxdiff(out[0, h], ro) <= TOL and _maxdiff(S_T[0, h], rS) <= TOL
+
+
+def check_kda_matches_ut_form(orc):
+    r = _rng(803)
+    T, dk, dv = 150, 16, 12
+    q, k, v, a, b = _kda_inputs(r, 1, 1, T, dk, dv, mean=4.0)
+    S0 = r.standard_normal((1, 1, dv, dk))
+    out, S_T, _ = orc.forward(KDA, q, k, v, gate=a, beta=b, S0=S0)
+    ro, rS = pf.kda_ut_form(q[0, 0], k[0, 0], v[0, 0], a[0, 0], b[0, 0], S0[0, 0])
+    assert _maxdiff(out[0, 0], ro) <= TOL and _maxdiff(S_T[0, 0], rS) <= TOL
+
+
+def check_kda_shared_channel_gate_is_gdr(orc):
+    """alpha_t = g_t in every channel: the scalar-gate delta rule."""
+    r = _rng(804)
+    q, k, v, _, b = _kda_inputs(r, 2, 2, 33, 8, 6)
+    g = _sigmoid(r.normal(2.0, 1.0, (2, 2, 33)))
+    S0 = r.standard_normal((2, 2, 6, 8))
+    a = np.broadcast_to(g[..., None], (2, 2, 33, 8)).copy()
+    x = orc.forward(KDA, q, k, v, gate=a, beta=b, S0=S0)
+    y = orc.forward(GATED_DELTA, q, k, v, gate=g, beta=b, S0=S0)
+    assert _maxdiff(x[0], y[0]) <= TOL and _maxdiff(x[1], y[1]) <= TOL
+
+
+def check_kda_unit_beta_recalls_value(orc):
+    """beta = 1, unit keys: S_t k_t = v_t after every write, whatever the decays."""
+    r = _rng(805)
+    T, dk, dv = 20, 16, 8
+    q, k, v, a, _ = _kda_inputs(r, 1, 2, T, dk, dv, mean=0.0)
+    S = np.ascontiguousarray(r.standard_normal((1, 2, dv, dk)))
+    for t in range(T):
+        orc.decode_step(KDA, S, q[:, :, t], k[:, :, t], v[:, :, t], gate=a[:, :, t], beta=np.ones((1, 2)))
+        assert _maxdiff(np.einsum("bhvk,bhk->bhv", S, k[:, :, t]), v[:, :, t]) <= TOL
+
+
+def check_kda_zero_beta_is_channel_decay(orc):
+    """beta = 0: S_T = S0 diag(prod_t alpha_t), o_t = S0 (prod_{i<=t} alpha_i o q_t)."""
+    r = _rng(806)
+    T, dk, dv = 18, 8, 5
+    q, k, v, a, _ = _kda_inputs(r, 1, 1, T, dk, dv)
+    S0 = r.standard_normal((1, 1, dv, dk))
+    out, S_T, _ = orc.forward(KDA, q, k, v, gate=a, beta=np.zeros((1, 1, T)), S0=S0)
+    A = np.cumprod(a[0, 0], axis=0)
+    assert _maxdiff(S_T[0, 0], S0[0, 0] * A[-1][None, :]) <= TOL
+    assert _maxdiff(out[0, 0], (q[0, 0] * A) @ S0[0, 0].T) <= TOL
+
+
 # ------------------------------------------------ state, decode, split calls
 
 def check_state_accounting(orc):
@@ -286,7 +446,7 @@ def check_state_accounting(orc):
         assert z_T is None and S_T.size == c1["state_values_without_normalizer"]
 
 
-def _variant_inputs(r, variant, T, dk, dv, B=1, H=2):
+def _variant_inputs(r, variant, T, dk, dv, B=1, H=2, decay=False):
     q, k = r.standard_normal((B, H, T, dk)), r.standard_normal((B, H, T, dk))
     v = r.standard_normal((B, H, T, dv))
     gate = beta = None
@@ -296,22 +456,34 @@ def _variant_inputs(r, variant, T, dk, dv, B=1, H=2):
         k = _unit(k)
         gate = _sigmoid(r.normal(3.0, 1.0, (B, H, T)))
         beta = _sigmoid(r.normal(0.0, 1.0, (B, H, T)))
+    elif variant == KDA:
+        k = _unit(k)
+        gate = _sigmoid(r.normal(3.0, 1.0, (B, H, T, dk)))
+        beta = _sigmoid(r.normal(0.0, 1.0, (B, H, T)))
+    elif variant == RETENTION or decay:
+        gate = _sigmoid(r.normal(2.0, 1.0, H))
     return q, k, v, gate, beta
 
 
+# (variant, per-head decay) cases of the decode and split-call invariants
+_INVARIANT_CASES = ((NORMALIZED, False), (NORMALIZED, True), (GATED, False), (GATED_DELTA, False),
+                    (RETENTION, True), (KDA, False))
+
+
 def check_decode_chain_equals_forward(orc):
-    for variant in (NORMALIZED, GATED, GATED_DELTA):
-        r = _rng(500 + variant)
+    for variant, decay in _INVARIANT_CASES:
+        r = _rng(500 + variant + 10 * decay)
         T, dk, dv = 17, 8, 6
-        q, k, v, gate, beta = _variant_inputs(r, variant, T, dk, dv)
-        S0 = r.standard_normal((1, 2, dv, dk))
-        z0 = np.abs(r.standard_normal((1, 2, dk))) + 1.0 if variant == NORMALIZED else None
+        q, k, v, gate, beta = _variant_inputs(r, variant, T, dk, dv, B=2, decay=decay)
+        per_head = variant in (NORMALIZED, RETENTION)
+        S0 = r.standard_normal((2, 2, dv, dk))
+        z0 = np.abs(r.standard_normal((2, 2, dk))) + 1.0 if variant == NORMALIZED else None
         out, S_T, z_T = orc.forward(variant, q, k, v, gate=gate, beta=beta, S0=S0, z0=z0)
         S = np.ascontiguousarray(S0.copy())
         z = np.ascontiguousarray(z0.copy()) if z0 is not None else None
         for t in range(T):
-            o = orc.decode_step(variant, S, q[:, :, t], k[:, :, t], v[:, :, t],
-                                gate=None if gate is None else gate[:, :, t],
+            g = gate if (gate is None or per_head) else gate[:, :, t]
+            o = orc.decode_step(variant, S, q[:, :, t], k[:, :, t], v[:, :, t], gate=g,
                                 beta=None if beta is None else beta[:, :, t], z=z)
             assert _maxdiff(o, out[:, :, t]) <= TOL
         assert _maxdiff(S, S_T) <= TOL
@@ -320,11 +492,12 @@ def check_decode_chain_equals_forward(orc):
 
 
 def check_split_call_equals_single_call(orc):
-    for variant in (NORMALIZED, GATED, GATED_DELTA):
-        r = _rng(600 + variant)
+    for variant, decay in _INVARIANT_CASES:
+        r = _rng(600 + variant + 10 * decay)
         T, T1, dk, dv = 45, 19, 8, 8
-        q, k, v, gate, beta = _variant_inputs(r, variant, T, dk, dv)
-        sl = lambda a, s: None if a is None else a[:, :, s]  # noqa: E731
+        q, k, v, gate, beta = _variant_inputs(r, variant, T, dk, dv, decay=decay)
+        per_head = variant in (NORMALIZED, RETENTION)
+        sl = lambda a, s: None if a is None else (a if per_head and a is gate else a[:, :, s])  # noqa: E731
         out, S_T, z_T = orc.forward(variant, q, k, v, gate=gate, beta=beta)
         a = slice(0, T1)
         b = slice(T1, T)

@@ -19,11 +19,11 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 MUTANTS = {
     "phi_missing_plus_one": [("return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x);")],
     "la_normalizer_dropped": [("ot[i] = num / den;", "ot[i] = num;")],
-    "la_normalizer_not_accumulated": [("z[c] += fk[c];", "z[c] = fk[c];")],
+    "la_normalizer_not_accumulated": [("z[c] = gam * z[c] + fk[c];", "z[c] = fk[c];")],
     "la_read_before_update": [
-        ("for (int c = 0; c < dk; ++c) {\n                for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] += fk[c] * vt[i];",
-         "for (int c = 0; c < dk; ++c) {\n                for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] += 0.0;"),
-        ("ot[i] = num / den;", "ot[i] = num / den;\n                for (int c = 0; c < dk; ++c) S[(size_t)c * dv + i] += fk[c] * vt[i];"),
+        ("for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] = gam * S[(size_t)c * dv + i] + fk[c] * vt[i];\n                z[c]",
+         "for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] += 0.0;\n                z[c]"),
+        ("ot[i] = num / den;", "ot[i] = num / den;\n                for (int c = 0; c < dk; ++c) S[(size_t)c * dv + i] = gam * S[(size_t)c * dv + i] + fk[c] * vt[i];"),
     ],
     "gla_gate_on_value_index": [("gt[c] * S[(size_t)c * dv + i]", "gt[i % dk] * S[(size_t)c * dv + i]")],
     "gla_gate_also_decays_new_write": [
@@ -39,8 +39,24 @@ MUTANTS = {
     "gdr_read_transposed": [("o += S[(size_t)i * dk + c] * qt[c];",
                              "o += S[(size_t)(c % dv) * dk + (i % dk)] * qt[c];")],
     "state_written_transposed": [(": S[(size_t)c * dv + i];", ": S[(size_t)(i % dk) * dv + (c % dv)];")],
-    "initial_state_ignored_for_gla": [("if (variant == 2) S[(size_t)i * dk + c] = s;\n            else              S[(size_t)c * dv + i] = s;",
-                                       "if (variant == 2) S[(size_t)i * dk + c] = s;\n            else              S[(size_t)c * dv + i] = (variant == 1) ? 0.0 : s;")],
+    # fixed per-head decay: the page's own pitfall, decaying only one accumulator
+    "la_decay_state_only": [("z[c] = gam * z[c] + fk[c];", "z[c] = z[c] + fk[c];")],
+    "la_decay_normalizer_only": [
+        ("for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] = gam * S[(size_t)c * dv + i] + fk[c] * vt[i];\n                z[c]",
+         "for (int i = 0; i < dv; ++i) S[(size_t)c * dv + i] = S[(size_t)c * dv + i] + fk[c] * vt[i];\n                z[c]")],
+    "decay_indexed_by_flat_head": [("return gate + (h % H);", "return gate + (h % (H > 1 ? H : 1) == h ? h : h % H) + (h >= H);")],
+    "retention_decays_new_write": [
+        ("S[(size_t)c * dv + i] = gam * S[(size_t)c * dv + i] + fk[c] * vt[i];\n            /* y_t",
+         "S[(size_t)c * dv + i] = gam * (S[(size_t)c * dv + i] + fk[c] * vt[i]);\n            /* y_t")],
+    "kda_decay_on_value_rows": [("for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] *= alpha[c];",
+                                 "for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] *= alpha[i % dk];")],
+    "kda_predict_from_undecayed_state": [
+        ("for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] *= alpha[c];", ""),
+        ("for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] += err * kt[c];",
+         "for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] = alpha[c] * S[(size_t)i * dk + c] + err * kt[c];")],
+    "kda_beta_dropped": [("const double err = bw * (vt[i] - pred[i]);", "const double err = (vt[i] - pred[i]);")],
+    "initial_state_ignored_for_gla": [("else                              S[(size_t)c * dv + i] = s;",
+                                       "else                              S[(size_t)c * dv + i] = (variant == 1) ? 0.0 : s;")],
 }
 
 CHILD = r"""
