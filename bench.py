@@ -142,6 +142,52 @@ def time_launches(fn, steps, warmup, stream):
     return wall, sum(ms) / len(ms), ms
 
 
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_peaks(stream, copy_bytes=1 << 30, reps=5):
+    """On-box peaks: a hand-written streaming copy of copy_bytes (read once,
+    written once; GB/s counts both) and a matrix-core-only bf16 loop
+    (libla_probe.so), each timed with HIP events on `stream`."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "gated_delta_rule_causal_amd", "libla_probe.so"))
+    lib.la_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.la_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.la_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.la_probe_mfma_flops.restype = ctypes.c_double
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    src = torch.ones(copy_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+
+    def copy():
+        assert lib.la_probe_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), copy_bytes, sp) == 0
+
+    _, copy_ms, _ = time_launches(copy, reps, 2, stream)
+    assert bool(torch.equal(src[:1024], dst[:1024]))
+    del src, dst
+    blocks, iters = 256 * 8, 2000
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        assert lib.la_probe_mfma(ctypes.c_void_p(buf.data_ptr()), blocks, iters, sp) == 0
+
+    _, mfma_ms, _ = time_launches(mfma, reps, 2, stream)
+    return {"hbm_copy_gbs": 2 * copy_bytes / (copy_ms * 1e-3) / 1e9, "copy_bytes": copy_bytes,
+            "copy_ms": copy_ms,
+            "bf16_mfma_tflops": lib.la_probe_mfma_flops(blocks, iters) / (mfma_ms * 1e-3) / 1e12,
+            "mfma_ms": mfma_ms}
+
+
 def cpu_baseline(w, inp, seconds_target=15.0):
     """The float64 oracle on a sample of the workload's heads (full T)."""
     import numpy as np
@@ -163,7 +209,7 @@ def cpu_baseline(w, inp, seconds_target=15.0):
     dt = time.perf_counter() - t0
     head_tokens_per_s = n_take * w.T / dt
     return {"value": head_tokens_per_s / w.H, "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of %d heads (b*H+h = 0..%d), full T=%d, float64 token recurrence, %.1f s; "
                       "tokens/s counts a token as all H=%d heads" % (n_take, nh, n_take - 1, w.T, dt, w.H)}
 
@@ -178,7 +224,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=CHUNK_WORKLOAD,
                     help="chunked-forward workload to time (default: the gated delta rule headline)")
     ap.add_argument("--copy-bytes", type=int, default=0,
-                    help="also run one device-to-device copy of this many bytes (counter calibration)")
+                    help="also run one probe copy of this many bytes (counter calibration)")
+    ap.add_argument("--no-probes", action="store_true", help="skip the on-box peak probes")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -250,13 +297,29 @@ def main(argv=None):
     dwall, dms, _ = time_launches(decode_step, args.decode_steps, 10, stream)
     dbytes = decode_bytes(wd.B, wd.H, wd.d_k, wd.d_v)
     dgbs = dbytes / (dms * 1e-3) / 1e9
+    del S, pool
 
+    # control: the same step over B=512 (537 MB of state, twice the 256 MB
+    # Infinity Cache), so that the cache cannot hold the state between steps
+    Bc = 2 * wd.B
+    Sc = to_dev(wl.decode_state(wd, B=Bc))
+    poolc = [{k: to_dev(v) for k, v in wl.decode_step_inputs(wd, s, B=Bc).items()} for s in range(4)]
+    oc = torch.empty((Bc, wd.H, wd.d_v), dtype=torch.bfloat16, device="cuda")
+    itc = [0]
+
+    def decode_step_control():
+        x = poolc[itc[0] % len(poolc)]
+        itc[0] += 1
+        la.la_decode_step(x["q"], x["k"], x["v"], Sc, variant=wd.variant, gate=x["gate"], beta=x["beta"], out=oc)
+
+    _, dmsc, _ = time_launches(decode_step_control, max(20, args.decode_steps // 4), 5, stream)
+    dbytesc = decode_bytes(Bc, wd.H, wd.d_k, wd.d_v)
+    del Sc, poolc
+
+    peaks = None if args.no_probes else measured_peaks(stream)
     if args.copy_bytes > 0:
-        # an elementwise kernel that reads and writes exactly copy_bytes each
-        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
+        # one probe copy of a known size, for calibrating the traffic counters
+        measured_peaks(stream, copy_bytes=args.copy_bytes, reps=1)
 
     result = {
         "metric": METRIC,
@@ -282,8 +345,16 @@ def main(argv=None):
         "decode": {"workload": DECODE_WORKLOAD, "kernel": "decode_kernel", "steps": args.decode_steps,
                    "avg_launch_ms": dms, "tokens_per_s": wd.B * args.decode_steps / dwall,
                    "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                "frac": dgbs / HBM_PEAK_GBS, "algorithmic_bytes": dbytes}},
+                                "frac": dgbs / HBM_PEAK_GBS, "algorithmic_bytes": dbytes},
+                   "control_b512": {"avg_launch_ms": dmsc, "algorithmic_bytes": dbytesc,
+                                    "achieved_gbs": dbytesc / (dmsc * 1e-3) / 1e9,
+                                    "frac": dbytesc / (dmsc * 1e-3) / 1e9 / HBM_PEAK_GBS}},
     }
+    if peaks is not None:
+        peaks["chunk_hbm_frac_of_measured"] = gbs / peaks["hbm_copy_gbs"]
+        peaks["chunk_mfma_frac_of_measured"] = tflops / peaks["bf16_mfma_tflops"] if w.dtype == "bf16" else None
+        peaks["decode_hbm_frac_of_measured"] = dgbs / peaks["hbm_copy_gbs"]
+        result["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(result), flush=True)

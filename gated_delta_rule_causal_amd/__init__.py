@@ -40,13 +40,50 @@ def make_desc(variant: int, dtype: int, B: int, H: int, T: int, d_k: int, d_v: i
 def _ptr(t):
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor):
-        raise TypeError("expected a torch.Tensor or None")
-    if not t.is_cuda:
-        raise ValueError("tensors must live in GPU memory")
-    if not t.is_contiguous():
-        raise ValueError("tensors must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(name, t, shape, dtype, device):
+    """The C library cannot see tensor sizes: every tensor is checked here for
+    the exact shape, element type and device include/la.h documents."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch.Tensor or None" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s: dtype %s, expected %s" % (name, t.dtype, dtype))
+    if t.device != device:
+        raise ValueError("%s: on %s, expected %s (q's device)" % (name, t.device, device))
+    if not t.is_contiguous():
+        raise ValueError("%s: must be contiguous" % name)
+
+
+def _check_qkv(q, k, v, lead):
+    """q, k, v: same dtype (float32 or bfloat16) and device, q on the GPU;
+    returns (dtype code, d_k, d_v)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("%s: expected a torch.Tensor" % name)
+    if q.dtype not in _DTYPES:
+        raise TypeError("q/k/v must be float32 or bfloat16")
+    if q.dim() != len(lead) + 1:
+        raise ValueError("q: expected %d dimensions, got %d" % (len(lead) + 1, q.dim()))
+    d_k = q.shape[-1]
+    if v.dim() != q.dim():
+        raise ValueError("v: expected %d dimensions, got %d" % (q.dim(), v.dim()))
+    d_v = v.shape[-1]
+    _check("q", q, tuple(q.shape), q.dtype, q.device)
+    _check("k", k, tuple(q.shape), q.dtype, q.device)
+    _check("v", v, tuple(q.shape[:-1]) + (d_v,), q.dtype, q.device)
+    return _DTYPES[q.dtype], d_k, d_v
+
+
+def _require_gpu(q):
+    # after the shape checks, so that those are testable without a GPU
+    if not q.is_cuda:
+        raise ValueError("q: tensors must live in GPU memory")
 
 
 def _stream(stream):
@@ -84,21 +121,31 @@ def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, ch
     needed.  Returns (out, S_T, z_T).
     """
     lib = load()
-    if q.dtype not in _DTYPES:
-        raise TypeError("q/k/v must be float32 or bfloat16")
-    B, H, T, d_k = q.shape
-    d_v = v.shape[-1]
-    desc = make_desc(variant, _DTYPES[q.dtype], B, H, T, d_k, d_v, chunk, phi)
+    dt, d_k, d_v = _check_qkv(q, k, v, "BHT")
+    B, H, T = q.shape[:3]
+    dev, f32 = q.device, torch.float32
+    _check("gate", gate, (B, H, T, d_k) if variant == LA_GATED else (B, H, T), f32, dev)
+    _check("beta", beta, (B, H, T), f32, dev)
+    _check("S0", S0, (B, H, d_v, d_k), f32, dev)
+    _check("z0", z0, (B, H, d_k), f32, dev)
+    _check("out", out, (B, H, T, d_v), q.dtype, dev)
+    _check("S_T", S_T, (B, H, d_v, d_k), f32, dev)
+    _check("z_T", z_T, (B, H, d_k), f32, dev)
+    _require_gpu(q)
+    desc = make_desc(variant, dt, B, H, T, d_k, d_v, chunk, phi)
     if out is None:
-        out = torch.empty((B, H, T, d_v), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, H, T, d_v), dtype=q.dtype, device=dev)
     if return_state and S_T is None:
-        S_T = torch.empty((B, H, d_v, d_k), dtype=torch.float32, device=q.device)
+        S_T = torch.empty((B, H, d_v, d_k), dtype=f32, device=dev)
     if return_state and variant == LA_NORMALIZED and z_T is None:
-        z_T = torch.empty((B, H, d_k), dtype=torch.float32, device=q.device)
+        z_T = torch.empty((B, H, d_k), dtype=f32, device=dev)
     ws_bytes = int(lib.la_chunk_fwd_workspace(ctypes.byref(desc)))
     ws = workspace
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or ws.device != dev or not ws.is_contiguous():
+            raise ValueError("workspace: a contiguous tensor on q's device")
     if ws is None and ws_bytes:
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_given = 0 if ws is None else ws.numel() * ws.element_size()
     check(lib.la_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                            _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_T), _ptr(z_T), _ptr(ws),
@@ -114,13 +161,20 @@ def la_decode_step(q, k, v, S, *, variant, gate=None, beta=None, z=None, phi=Non
     float32; gate / beta / z as include/la.h describes.  Returns out (B,H,d_v).
     """
     lib = load()
-    if q.dtype not in _DTYPES:
-        raise TypeError("q/k/v must be float32 or bfloat16")
-    B, H, d_k = q.shape
-    d_v = v.shape[-1]
-    desc = make_desc(variant, _DTYPES[q.dtype], B, H, 1, d_k, d_v, 0, phi)
+    dt, d_k, d_v = _check_qkv(q, k, v, "BH")
+    B, H = q.shape[:2]
+    dev, f32 = q.device, torch.float32
+    if S is None:
+        raise ValueError("S: the state is required")
+    _check("gate", gate, (B, H, d_k) if variant == LA_GATED else (B, H), f32, dev)
+    _check("beta", beta, (B, H), f32, dev)
+    _check("S", S, (B, H, d_v, d_k), f32, dev)
+    _check("z", z, (B, H, d_k), f32, dev)
+    _check("out", out, (B, H, d_v), q.dtype, dev)
+    _require_gpu(q)
+    desc = make_desc(variant, dt, B, H, 1, d_k, d_v, 0, phi)
     if out is None:
-        out = torch.empty((B, H, d_v), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, H, d_v), dtype=q.dtype, device=dev)
     check(lib.la_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                              _ptr(beta), _ptr(S), _ptr(z), _ptr(out), _stream(stream)))
     return out

@@ -34,6 +34,9 @@ COMMON_FLAGS = [
 ]
 
 SOURCES = ["la_api.cpp", "la_decode.hip", "la_chunk_linear.hip", "la_chunk_gdr.hip"]
+# peak probes (a streaming copy, a matrix-core loop), a library of their own
+PROBE_SOURCES = ["la_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libla_probe.so")
 
 
 def _compile(src: str) -> str:
@@ -51,18 +54,23 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
         raise RuntimeError("hipcc not found (set HIPCC)")
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    jobs = jobs or min(len(SOURCES) + len(PROBE_SOURCES), max(1, (os.cpu_count() or 2)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
+    if verbose:
+        print("built", LIB, "and", PROBE_LIB)
+    return LIB
+
+
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-    os.replace(tmp, LIB)
-    if verbose:
-        print("built", LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 def main(argv=None):

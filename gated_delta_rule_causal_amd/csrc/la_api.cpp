@@ -59,8 +59,8 @@ la_status check_desc(const la_desc *d, bool chunked) {
         return fail(LA_EUNSUPPORTED, "head sizes d_k=%d, d_v=%d: supported are 16, 32, 64, 128", d->d_k, d->d_v);
     if (chunked) {
         if (d->chunk < 0) return fail(LA_EINVAL, "chunk=%d must be >= 0", d->chunk);
-        if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64)
-            return fail(LA_EUNSUPPORTED, "chunk=%d: supported are 0 (= 64), 16, 32, 64", d->chunk);
+        if (d->chunk != 0 && d->chunk != 16 && d->chunk != 32 && d->chunk != 64 && d->chunk != 128)
+            return fail(LA_EUNSUPPORTED, "chunk=%d: supported are 0 (= 64), 16, 32, 64, 128", d->chunk);
     }
     // element counts must stay far from 64-bit overflow
     const double elems = static_cast<double>(d->B) * d->H * (chunked ? (d->T > 0 ? d->T : 1) : 1) *

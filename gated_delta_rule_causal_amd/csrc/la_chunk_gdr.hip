@@ -788,6 +788,9 @@ static hipError_t gdr_chunk(const ChunkArgs &a) {
         case 16: return gdr_dvb<DT, DK, 16>(a);
         case 32: return gdr_dvb<DT, DK, 32>(a);
         case 64: return gdr_dvb<DT, DK, 64>(a);
+        // 128-token tiles of this kernel exceed the LDS of a compute unit; the
+        // result does not depend on the chunk length, so they run as 64
+        case 128: return gdr_dvb<DT, DK, 64>(a);
     }
     return hipErrorInvalidValue;
 }

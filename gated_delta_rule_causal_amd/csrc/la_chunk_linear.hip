@@ -142,6 +142,91 @@ __device__ __forceinline__ void mul_bcast15_row2_4(const float (&y)[4], float (&
     asm(LA_DPP4("row_bcast:15 row_mask:0x4 bank_mask:0xf") : LA_DPP4_OPS(x, y));
 }
 
+// Suffix products along each 16-lane row: lane i of a row gets x_i * ... *
+// x_15 (four DPP row shifts to the left; a lane whose source lies past the
+// row end keeps x), for one channel or four at once.
+__device__ __forceinline__ float row_suffix_mul(float x) {
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shl:1 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shl:2 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shl:4 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    asm("s_nop 1\n\tv_mul_f32_dpp %0, %0, %0 row_shl:8 row_mask:0xf bank_mask:0xf" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ void row_suffix_mul4(float (&x)[4]) {
+    asm(LA_DPP4("row_shl:1 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4("row_shl:2 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4("row_shl:4 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4("row_shl:8 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+}
+// the next lane's value within its 16-lane row, 1 at the row end: with
+// x = row_suffix_mul(g), the exclusive suffix product g_{i+1} * ... * g_15
+__device__ __forceinline__ float row_next_or_one(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.f), __float_as_int(x), 0x101, 0xF, 0xF, false));
+}
+
+// Below this product of one channel's gates over a 16-token block the fast
+// diagonal factorization (key operand phi(k_j) / R_j) would leave the float32
+// range; such a chunk takes gla_diag_exact for its diagonal score tiles and
+// forms its key operands from suffix products instead.
+constexpr float kGlaWeakBlock = 0x1p-64f;
+
+// Exact diagonal 16x16 score tile of gated linear attention, for token block
+// I of a chunk (n valid tokens, rows of q, k and the gates DK elements apart
+// from the chunk's first token):
+//   P_tj = sum_c phi(q_tc) phi(k_jc) prod_{j < i <= t} gamma_ic   (j <= t),
+// zero above the diagonal and for tokens past n.  Every decay factor is a
+// running product of the gates themselves and never exceeds 1, so the tile
+// is exact (to float32 rounding) for any gates in (0, 1] (page "Ch. 11 Linear
+// attention and Hyena", 11.3 and the solution to Exercise 11.5, which state
+// the gate range).  Lane (j, cq): key token j of the block and one group of
+// channels; its running key factors kd_c = phi(k_jc) prod_{j < i <= t}
+// gamma_ic advance one query token t per step, and the row sum over the
+// channel groups comes from two lane exchanges.  The inputs are re-read from
+// global memory (they are in the cache: the chunk was just staged).
+template <int PHI, class IO, int DK, class Op>
+__device__ __forceinline__ void gla_diag_exact(const IO *q0, const IO *k0, const float *g0, int n, int I, Op *P,
+                                               int ldc, int lane) {
+    constexpr int NQ = DK / 8 < 4 ? DK / 8 : 4;   // channel groups over the lanes of a token
+    constexpr int CPL = DK / NQ;                   // channels per lane, a multiple of 8
+    const int j = lane & 15, cq = lane >> 4;
+    const bool act = cq < NQ;
+    const int c0 = (act ? cq : 0) * CPL;
+    const int rj = 16 * I + j;
+    const bool jon = act && rj < n;
+    float kd[CPL];
+#pragma unroll
+    for (int cg = 0; cg < CPL; cg += 8) {
+        float x[8];
+        load8(k0 + static_cast<size_t>(min(rj, n - 1)) * DK + c0 + cg, x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kd[cg + i] = jon ? apply_phi<PHI>(x[i]) : 0.f;
+    }
+#pragma unroll 1
+    for (int t = 0; t < 16; ++t) {
+        const int rt = 16 * I + t;
+        const size_t row = static_cast<size_t>(min(rt, n - 1)) * DK + c0;
+        const bool ton = rt < n, adv = t > j;
+        float s = 0.f;
+#pragma unroll
+        for (int cg = 0; cg < CPL; cg += 8) {
+            // one channel group's loads at a time: the routine shares the
+            // register budget of the kernel it is inlined into
+            asm volatile("" ::: "memory");
+            float qv[8], gv[8];
+            load8(q0 + row + cg, qv);
+            load8(g0 + row + cg, gv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                kd[cg + i] *= adv ? gv[i] : 1.f;
+                s += (ton ? apply_phi<PHI>(qv[i]) : 0.f) * kd[cg + i];
+            }
+        }
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        if (cq == 0) from_f32(P[t * ldc + j], t >= j ? s : 0.f);
+    }
+}
+
 // pair index of an off-diagonal key block J <= I - 2 (blocks strictly between exist)
 __host__ __device__ constexpr int rho_index(int I, int J) { return (I - 2) * (I - 1) / 2 + J; }
 
@@ -187,6 +272,7 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     __shared__ __align__(16) Op sV[C * LDV];                 // this block's values, [t][v]
     __shared__ __align__(16) unsigned char sPG[L::PG_BYTES]; // gates (f32), then P
     __shared__ __align__(16) float sF[L::F_FLOATS];
+    __shared__ int sWeak;   // gated: this chunk takes the exact diagonal tiles
     Op *sP = reinterpret_cast<Op *>(sPG);
     float *sG = reinterpret_cast<float *>(sPG);
     float *sE = sF;                       // gated: prod of the chunk's gates before block I, [NB][DK]
@@ -305,6 +391,7 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
         // or with phi applied (normalized); gates as float32 with padded tokens
         // set to 1 (no decay).
         pv.store(sV, LDV, tid);
+        if (GATED && tid == 0) sWeak = 0;
         if constexpr (!GATED) {
 #pragma unroll
             for (int i = 0; i < pq.PER; ++i) {
@@ -379,6 +466,18 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                     run[i] = row_scan_mul(g[i]);   // R_t = prod_{16I <= s <= t} g_s
                     rinv[i] = __builtin_amdgcn_rcpf(run[i]);
                 }
+                // strong decay somewhere in these channels (a block product below
+                // kGlaWeakBlock; R_t only falls along a block): k~ from the
+                // exclusive suffix products of the gates, which never exceed 1,
+                // and the chunk's diagonal tiles by gla_diag_exact
+                const bool weak = __builtin_amdgcn_ballot_w64(run[0] < kGlaWeakBlock || run[1] < kGlaWeakBlock ||
+                                                              run[2] < kGlaWeakBlock || run[3] < kGlaWeakBlock) != 0;
+                float sx[4] = {0.f, 0.f, 0.f, 0.f};
+                if (weak) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sx[i] = row_next_or_one(row_suffix_mul(g[i]));
+                    if (lane == 0) sWeak = 1;
+                }
                 float tot[NB][4];   // whole-block products (uniform)
 #pragma unroll
                 for (int J = 0; J < NB; ++J)
@@ -429,8 +528,8 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                         if (J > I) after *= tot[J][i];
                     }
                     fq[i] = on ? apply_phi<PHI>(q[i]) * run[i] : 0.f;
-                    fd[i] = on ? apply_phi<PHI>(k[i]) * rinv[i] : 0.f;
-                    fk[i] = fd[i] * tb;
+                    fd[i] = on && !weak ? apply_phi<PHI>(k[i]) * rinv[i] : 0.f;
+                    fk[i] = weak ? (on ? apply_phi<PHI>(k[i]) * sx[i] : 0.f) : fd[i] * tb;
                     fa[i] = fk[i] * after;
                 }
                 if (in_tile) {
@@ -446,11 +545,17 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
         // ---- intra-chunk scores P (16x16 tiles, block-lower-triangular)
         // Each tile is taken transposed (keys x queries), so that a lane holds
         // four consecutive columns j of one row t and writes them at once.
+        const bool weak_chunk = GATED && __builtin_amdgcn_readfirstlane(sWeak) != 0;
         for (int tt = wave; tt < NB * NB; tt += NW) {
             const int I = tt / NB, J = tt % NB;
             const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
             if (J > I) {
                 st_group(sP + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
+                continue;
+            }
+            if (GATED && J == I && weak_chunk) {
+                gla_diag_exact<PHI, IO, DK>(qh + static_cast<size_t>(c0) * DK, kh + static_cast<size_t>(c0) * DK,
+                                            gh + static_cast<size_t>(c0) * DK, n, I, sP + 16 * I * LDC + 16 * I, LDC, lane);
                 continue;
             }
             f32x4 acc = zero4();
@@ -613,6 +718,7 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
     constexpr bool GDMA = L::GDMA;
     constexpr int GLD = L::GLD;
     __shared__ __align__(16) float sG[GDMA ? C * GLD : 4];   // gates of the chunk being prepared
+    __shared__ int sWeak;   // chunk c+1 takes the exact diagonal tiles
     float *sE = sF, *sD = sF + NB * DK, *sRho = sF + (NB + 1) * DK, *sTot = sRho + L::NRHO * DK;
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -719,6 +825,18 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
             row_scan_mul4(run);   // R_t = prod_{16I <= s <= t} g_s
 #pragma unroll
             for (int i = 0; i < 4; ++i) rinv[i] = __builtin_amdgcn_rcpf(run[i]);
+            // strong decay in these channels (a block product below
+            // kGlaWeakBlock): k~ from exclusive suffix products of the gates
+            // (never above 1) and exact diagonal tiles for the chunk
+            const bool weak = __builtin_amdgcn_ballot_w64(run[0] < kGlaWeakBlock || run[1] < kGlaWeakBlock ||
+                                                          run[2] < kGlaWeakBlock || run[3] < kGlaWeakBlock) != 0;
+            float sx[4] = {g[0], g[1], g[2], g[3]};
+            if (weak) {
+                row_suffix_mul4(sx);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sx[i] = row_next_or_one(sx[i]);
+                if (lane == 0) sWeak = 1;
+            }
             {
                 // per-chunk factors, from a scan across the block ends: after
                 // two DPP row broadcasts lane t holds P_t = prod_{s <= t} g_s, so
@@ -767,10 +885,10 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // tokens past the end: zero operands (selects, not branches)
-                const float rq = on ? run[i] : 0.f, rk = on ? rinv[i] : 0.f;
+                const float rq = on ? run[i] : 0.f, rk = on && !weak ? rinv[i] : 0.f;
                 fq[i] = apply_phi<PHI>(q[i]) * rq;
                 fd[i] = apply_phi<PHI>(k[i]) * rk;
-                fk[i] = fd[i] * tb[i];
+                fk[i] = weak ? apply_phi<PHI>(k[i]) * (on ? sx[i] : 0.f) : fd[i] * tb[i];
                 fa[i] = fk[i] * after[i];
             }
             if (in_tile) {
@@ -791,11 +909,17 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
     auto scores = [&](int c) {
         if (c + 1 >= nchunks) return;
         const int nb = (c + 1) & 1;
+        const bool weak = __builtin_amdgcn_readfirstlane(sWeak) != 0;
         auto score_tile = [&](int tt) {   // tile (I, J) = (tt / NB, tt % NB)
             const int I = tt / NB, J = tt % NB;
             const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
             if (J > I) {
                 st_group(sP + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
+                return;
+            }
+            if (J == I && weak) {
+                const size_t o = static_cast<size_t>((c + 1) * C) * DK;
+                gla_diag_exact<PHI, IO, DK>(qh + o, kh + o, gh + o, rows(c + 1), I, sP + 16 * I * LDC + 16 * I, LDC, lane);
                 return;
             }
             f32x4 acc = zero4();
@@ -935,6 +1059,7 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
             pq.store(sQ[nb], LDK, htid);
             pk.store(sK, LDK, htid);
             pv.store(sV[nb], LDV, htid);
+            if (htid == 0) sWeak = 0;   // last read in the previous step C
             // GDMA: chunk c+1's gate tile (sG was last read in the previous
             // step B), issued after the stores above, whose waits for the
             // staged registers would otherwise cover these loads too
@@ -1174,6 +1299,15 @@ static hipError_t launch_linear_t(const ChunkArgs &a) {
             const int64_t sblocks = static_cast<int64_t>(p.n_heads) * p.n_seg * (a.d_v / DVB);
             hipLaunchKernelGGL((la_segment_state_kernel<DT, DK, DVB, C>), dim3(static_cast<uint32_t>(sblocks)), dim3(256), 0,
                                a.stream, p, static_cast<float *>(a.workspace));
+        } else if (a.T > 0 && p.n_vblk > 1 && a.z0 && a.z_T == a.z0) {
+            // one pass, several value blocks per head, z_T in place of z0: every
+            // value block's workgroup reads z0 but only block 0 writes z_T, and a
+            // workgroup may start after block 0 has finished, so the blocks read
+            // a copy of z0 staged in the workspace
+            const size_t zbytes = static_cast<size_t>(p.n_heads) * a.d_k * sizeof(float);
+            hipError_t e = hipMemcpyAsync(a.workspace, a.z0, zbytes, hipMemcpyDeviceToDevice, a.stream);
+            if (e != hipSuccess) return e;
+            p.z0 = static_cast<const float *>(a.workspace);
         }
     }
     const int64_t blocks = static_cast<int64_t>(p.n_heads) * p.n_vblk * p.n_seg;
@@ -1201,6 +1335,9 @@ static hipError_t linear_chunk(const ChunkArgs &a) {
         case 16: return launch_linear_t<GATED, PHI, DT, DK, DVB, 16>(a);
         case 32: return launch_linear_t<GATED, PHI, DT, DK, DVB, fit_chunk<GATED, DT, DK, DVB, 32>()>(a);
         case 64: return launch_linear_t<GATED, PHI, DT, DK, DVB, fit_chunk<GATED, DT, DK, DVB, 64>()>(a);
+        // 128-token tiles of these kernels exceed the LDS of a compute unit;
+        // the result does not depend on the chunk length
+        case 128: return launch_linear_t<GATED, PHI, DT, DK, DVB, fit_chunk<GATED, DT, DK, DVB, 64>()>(a);
     }
     return hipErrorInvalidValue;
 }
@@ -1235,9 +1372,13 @@ static hipError_t linear_variant(const ChunkArgs &a) {
 // Workspace of the chunked forward: the segment slots of the normalized
 // variant (none for the other variants).
 size_t chunk_workspace_bytes(const ChunkArgs &a) {
+    if (a.variant != LA_NORMALIZED || a.T <= 0) return 0;
     const int64_t n = linear_max_segments(a);
-    if (n < 2) return 0;
-    return static_cast<size_t>(a.B) * a.H * n * (static_cast<size_t>(a.d_v) * a.d_k + a.d_k) * sizeof(float);
+    const size_t heads = static_cast<size_t>(a.B) * a.H;
+    // segment slots, or (one pass) a staged copy of z0 for z_T aliasing it
+    const size_t zstage = heads * a.d_k * sizeof(float);
+    if (n < 2) return zstage;
+    return std::max(zstage, heads * n * (static_cast<size_t>(a.d_v) * a.d_k + a.d_k) * sizeof(float));
 }
 
 hipError_t launch_chunk_linear(const ChunkArgs &a) {

@@ -48,11 +48,9 @@
  *     failure returns LA_EHIP.
  *   - Documented preconditions that are NOT checked (values live on the
  *     device): gate entries in (0, 1]; beta in [0, 1]; keys of
- *     LA_GATED_DELTA of unit length; z0 >= 0 for LA_NORMALIZED; for
- *     LA_GATED the product of one channel's gates over any 16 consecutive
- *     tokens of a chunk is at least 1e-30 (the chunked forward factors the
- *     decay through per-16-token reference points; past that range float32
- *     cannot hold the factors).
+ *     LA_GATED_DELTA of unit length; z0 >= 0 for LA_NORMALIZED.  Any gate in
+ *     (0, 1] is handled, however strong the decay: decay factors are only
+ *     ever formed as products or exponentials that do not exceed 1.
  */
 #ifndef LA_H
 #define LA_H
@@ -88,8 +86,10 @@ typedef enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1 } la_phi;
  *   T        tokens per sequence, >= 0 (ignored by la_decode_step).
  *   d_k      key/query head size; d_v value head size.  Supported:
  *            d_k in {16, 32, 64, 128}, d_v in {16, 32, 64, 128}.
- *   chunk    chunk length of la_chunk_fwd: 0 (= 64), 16, 32 or 64.  The
- *            result does not depend on it beyond floating-point rounding.
+ *   chunk    chunk length of la_chunk_fwd: 0 (= 64), 16, 32, 64 or 128.
+ *            The result does not depend on it beyond floating-point
+ *            rounding; a length whose tiles do not fit a compute unit's LDS
+ *            runs as the largest one that does (128 runs as 64).
  */
 typedef struct {
     int32_t variant;
@@ -102,12 +102,14 @@ typedef struct {
 
 /*
  * Bytes of device workspace la_chunk_fwd needs for `desc` (0 when none).
- * Only LA_NORMALIZED uses one, when its heads alone cannot occupy the GPU:
- * its state is a plain sum over the tokens, so the sequence then runs as
+ * Only LA_NORMALIZED with T > 0 uses one.  When its heads alone cannot occupy
+ * the GPU its state is a plain sum over the tokens, so the sequence runs as
  * concurrent segments whose state increments are staged in the workspace
- * (one d_v x d_k + d_k float32 slot per head and segment).  The size depends
- * on B, H, T, d_k and d_v only.  Returns 0 for an invalid descriptor as
- * well; la_chunk_fwd reports it.
+ * (one d_v x d_k + d_k float32 slot per head and segment); otherwise the
+ * workspace holds a copy of z0 (B*H*d_k float32) when z_T is z0, since the
+ * workgroups of a head's value blocks all read z0 and one writes z_T.  The
+ * size depends on the descriptor only.  Returns 0 for an invalid descriptor
+ * as well; la_chunk_fwd reports it.
  */
 size_t la_chunk_fwd_workspace(const la_desc *desc);
 

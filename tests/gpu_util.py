@@ -1,4 +1,8 @@
-"""Helpers of the GPU parity tests: host -> device transfer and the parity metric."""
+"""Helpers of the GPU parity tests: host -> device transfer, the parity
+metric, and the record of achieved errors."""
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -43,3 +47,16 @@ def parity_error(x, ref, lead=2):
     rm = np.abs(ref).reshape(n, -1).max(axis=1)
     rm = np.where(rm > 0, rm, 1.0)
     return float(np.max(xd / rm))
+
+
+def record(case, errs, dtype):
+    """Append the achieved errors of one parity case (a dict tensor -> error)
+    to the JSON-lines file named by LA_PARITY_LOG, when it is set, so that the
+    margin to the tolerance is visible and not only pass/fail."""
+    path = os.environ.get("LA_PARITY_LOG")
+    if not path:
+        return
+    row = {"case": case, "dtype": dtype, "tol": TOL[dtype]}
+    row.update({k: float(v) for k, v in errs.items()})
+    with open(path, "a") as f:
+        f.write(json.dumps(row) + "\n")

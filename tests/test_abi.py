@@ -103,7 +103,8 @@ CHUNK_CASES = [
     ("zero_dk", D(d_k=0), {}, la.LA_EINVAL, "d_k"),
     ("unsupported_dk", D(d_k=48), {}, la.LA_EUNSUPPORTED, "head sizes"),
     ("unsupported_dv", D(d_v=256), {}, la.LA_EUNSUPPORTED, "head sizes"),
-    ("unsupported_chunk", D(chunk=128), {}, la.LA_EUNSUPPORTED, "chunk"),
+    ("unsupported_chunk", D(chunk=256), {}, la.LA_EUNSUPPORTED, "chunk"),
+    ("unsupported_chunk_48", D(chunk=48), {}, la.LA_EUNSUPPORTED, "chunk"),
     ("negative_chunk", D(chunk=-16), {}, la.LA_EINVAL, "chunk"),
     ("missing_q", D(), {"q": None}, la.LA_EINVAL, "required"),
     ("missing_out", D(), {"out": None}, la.LA_EINVAL, "required"),
@@ -152,14 +153,15 @@ def test_workspace_query_of_invalid_desc_is_zero(lib):
 def test_workspace_sizes(lib):
     # Only the normalized variant uses a workspace: one slot of d_v*d_k + d_k
     # floats per head and segment, when the heads (value blocks of up to 64
-    # channels) give fewer workgroups than the 256 compute units.  The segment
-    # count is bounded by 256 / workgroups and by the 16-token chunks over two.
+    # channels) give fewer workgroups than the 256 compute units (the segment
+    # count is bounded by 256 / workgroups and by the 16-token chunks over
+    # two); otherwise a staged copy of z0, d_k floats per head.
     slot = lambda dk, dv: (dv * dk + dk) * 4  # noqa: E731
     assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=4, H=8, T=2048)) == 32 * 8 * slot(64, 64)
     assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=1, H=1, T=100, d_k=16, d_v=16)) == 3 * slot(16, 16)
-    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=16, H=16, T=2048)) == 0   # 256 heads
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=16, H=16, T=2048)) == 256 * 64 * 4   # 256 heads
     assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=0)) == 0
-    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=31)) == 0                 # one 16-token chunk pair at most
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=31)) == 6 * 64 * 4   # one 16-token chunk pair at most
     assert la.la_chunk_fwd_workspace(D(la.LA_GATED, T=2048)) == 0
     assert la.la_chunk_fwd_workspace(D(la.LA_GATED_DELTA, T=2048)) == 0
 
@@ -187,5 +189,72 @@ def test_empty_problem_is_a_no_op(lib):
 def test_binding_rejects_host_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 16)
-    with pytest.raises(ValueError):
+    with pytest.raises(ValueError, match="GPU memory"):
         la.la_chunk_fwd(x, x, x, variant=la.LA_NORMALIZED)
+    with pytest.raises(ValueError, match="GPU memory"):
+        la.la_decode_step(x[:, :, 0], x[:, :, 0], x[:, :, 0], torch.zeros(1, 1, 16, 16),
+                          variant=la.LA_NORMALIZED, z=torch.zeros(1, 1, 16))
+
+
+# The C library cannot see tensor sizes, so the binding checks every tensor's
+# shape, dtype and device before any call; these checks run before the
+# device check, so host tensors exercise them here.
+def _chunk_args(variant, dtype="float32", B=2, H=3, T=10, dk=16, dv=8):
+    import torch
+    dt = getattr(torch, dtype)
+    a = dict(q=torch.zeros(B, H, T, dk, dtype=dt), k=torch.zeros(B, H, T, dk, dtype=dt),
+             v=torch.zeros(B, H, T, dv, dtype=dt))
+    if variant == la.LA_GATED:
+        a["gate"] = torch.ones(B, H, T, dk)
+    if variant == la.LA_GATED_DELTA:
+        a["gate"], a["beta"] = torch.ones(B, H, T), torch.ones(B, H, T)
+    return a
+
+
+CHUNK_BINDING_CASES = [
+    ("k_shape", la.LA_GATED_DELTA, {"k": (2, 3, 10, 32)}, "k: shape"),
+    ("v_rows", la.LA_GATED_DELTA, {"v": (2, 3, 9, 8)}, "v: shape"),
+    ("k_dtype", la.LA_GATED_DELTA, {"k": "bfloat16"}, "k: dtype"),
+    ("gate_shape", la.LA_GATED, {"gate": (2, 3, 10)}, "gate: shape"),
+    ("gate_dtype", la.LA_GATED_DELTA, {"gate": "bfloat16"}, "gate: dtype"),
+    ("beta_shape", la.LA_GATED_DELTA, {"beta": (2, 3, 11)}, "beta: shape"),
+    ("S0_transposed", la.LA_GATED_DELTA, {"S0": (2, 3, 16, 8)}, "S0: shape"),
+    ("S0_bf16", la.LA_GATED_DELTA, {"S0": ((2, 3, 8, 16), "bfloat16")}, "S0: dtype"),
+    ("z0_shape", la.LA_NORMALIZED, {"z0": (2, 3, 8)}, "z0: shape"),
+    ("out_dtype", la.LA_NORMALIZED, {"out": ((2, 3, 10, 8), "bfloat16")}, "out: dtype"),
+    ("S_T_shape", la.LA_GATED, {"S_T": (2, 3, 8, 8)}, "S_T: shape"),
+    ("z_T_shape", la.LA_NORMALIZED, {"z_T": (3, 16)}, "z_T: shape"),
+]
+
+
+@pytest.mark.parametrize("name,variant,bad,msg", CHUNK_BINDING_CASES, ids=[c[0] for c in CHUNK_BINDING_CASES])
+def test_binding_rejects_mismatched_chunk_args(name, variant, bad, msg):
+    import torch
+    a = _chunk_args(variant)
+    for key, spec in bad.items():
+        if isinstance(spec, str):
+            a[key] = a[key].to(getattr(torch, spec))
+        else:
+            shape, dt = spec if isinstance(spec[1], str) else (spec, "float32")
+            a[key] = torch.zeros(shape, dtype=getattr(torch, dt))
+    q, k, v = a.pop("q"), a.pop("k"), a.pop("v")
+    with pytest.raises(ValueError, match=msg):
+        la.la_chunk_fwd(q, k, v, variant=variant, **a)
+
+
+def test_binding_rejects_mismatched_decode_args():
+    import torch
+    q = k = torch.zeros(2, 3, 16)
+    v = torch.zeros(2, 3, 8)
+    with pytest.raises(ValueError, match="S: shape"):
+        la.la_decode_step(q, k, v, torch.zeros(2, 3, 16, 8), variant=la.LA_GATED_DELTA,
+                          gate=torch.ones(2, 3), beta=torch.ones(2, 3))
+    with pytest.raises(ValueError, match="S: dtype"):
+        la.la_decode_step(q, k, v, torch.zeros(2, 3, 8, 16, dtype=torch.bfloat16), variant=la.LA_GATED_DELTA,
+                          gate=torch.ones(2, 3), beta=torch.ones(2, 3))
+    with pytest.raises(ValueError, match="gate: shape"):
+        la.la_decode_step(q, k, v, torch.zeros(2, 3, 8, 16), variant=la.LA_GATED_DELTA,
+                          gate=torch.ones(2, 3, 16), beta=torch.ones(2, 3))
+    with pytest.raises(ValueError, match="v: shape"):
+        la.la_decode_step(q, k, torch.zeros(2, 4, 8), torch.zeros(2, 3, 8, 16), variant=la.LA_GATED_DELTA,
+                          gate=torch.ones(2, 3), beta=torch.ones(2, 3))

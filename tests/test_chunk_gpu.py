@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_causal_amd as la
 import oracle
 import workloads as wl
-from gpu_util import TOL, dev, host64, parity_error
+from gpu_util import TOL, dev, host64, parity_error, record
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +46,7 @@ SWEEP = []
 for name in VARIANTS:
     for dtype in ("f32", "bf16"):
         for dk, dv in ((16, 16), (32, 64), (64, 32), (128, 128), (64, 16)):
-            for chunk in (16, 32, 64):
+            for chunk in (16, 32, 64, 128):
                 SWEEP.append((name, dtype, dk, dv, chunk))
 
 
@@ -59,21 +59,68 @@ def test_chunk_matches_oracle(name, dtype, dk, dv, chunk):
     inp = wl.chunk_inputs(w, B=2, H=2, T=T, S0_std=0.1, z0=True)
     print("chunk parity", name, dtype, dk, dv, chunk, "T", T, flush=True)
     errs, _ = run_chunk(w, inp, chunk, B=2, H=2)
+    record("sweep-%s-%s-dk%d-dv%d-c%d" % (name, dtype, dk, dv, chunk), errs, dtype)
     assert max(errs.values()) <= TOL[dtype], errs
 
 
 @pytest.mark.parametrize("wname", ["la_f32_b1h2t64d16", "la_bf16_b4h8t2048d64",
                                    "gla_bf16_b8h16t4096d128", "gdr_bf16_b4h16t8192d128"])
 def test_chunk_workload_full_shape(wname):
-    """The specified workloads at full size: every head runs on the GPU; the oracle
-    checks all heads of the small workloads and a spread sample of the large ones."""
+    """The specified workloads at full size, every head on the GPU and in the
+    oracle (the oracle runs the largest, 64 heads x 8192 tokens, in seconds)."""
     w = wl.WORKLOADS[wname]
     inp = wl.chunk_inputs(w)
-    nh = w.B * w.H
-    sample = None if nh <= 32 else sorted({0, 1, nh // 3, nh // 2, nh - 2, nh - 1, 17, 5 * nh // 7})
-    print("chunk workload", wname, "sample", sample, flush=True)
-    errs, _ = run_chunk(w, inp, w.chunk, sample=sample)
+    print("chunk workload", wname, "all heads", flush=True)
+    errs, _ = run_chunk(w, inp, w.chunk)
+    record("workload-" + wname, errs, w.dtype)
     assert max(errs.values()) <= TOL[w.dtype], errs
+
+
+# Strong decay (page "Ch. 11 Linear attention and Hyena", 11.3: any gate in
+# (0, 1]): random gates sigmoid(N(-3, 1)) (about 0.05), constant gates down to
+# 0.001 (a 16-token block product of 1e-48, below float32's range), and mild
+# gates with one channel at 1e-3.  Ragged lengths of one to four chunks.
+def _strong_gates(inp, kind):
+    g = inp["gate"].data
+    if isinstance(kind, float):
+        g[...] = kind
+    elif kind == "mixed":
+        g[..., 5] = 1e-3
+    return inp
+
+
+GLA_STRONG = [(n, dt, d, c) for (n, dt, d, c) in (("gla", "bf16", 128, 64), ("gla", "bf16", 64, 32),
+                                                  ("gla_id", "bf16", 64, 64), ("gla", "f32", 64, 64),
+                                                  ("gla", "f32", 128, 64), ("gla", "f32", 32, 16))]
+
+
+@pytest.mark.parametrize("T", [16, 65, 200])
+@pytest.mark.parametrize("kind", ["sig-3", 0.5, 0.05, 0.005, 0.001, "mixed"])
+@pytest.mark.parametrize("name,dtype,d,chunk", GLA_STRONG, ids=["-".join(map(str, c)) for c in GLA_STRONG])
+def test_gla_strong_decay(name, dtype, d, chunk, kind, T):
+    variant, phi = VARIANTS[name]
+    w = wl.variant_workload(variant, dtype, d, d, chunk=chunk, phi=phi, seed=83,
+                            gate_mean=-3.0 if kind == "sig-3" else 3.0)
+    inp = _strong_gates(wl.chunk_inputs(w, B=1, H=2, T=T, S0_std=0.1), kind)
+    print("gla strong decay", name, dtype, d, chunk, kind, T, flush=True)
+    errs, (out, S_T, _) = run_chunk(w, inp, chunk, B=1, H=2)
+    record("gla-strong-%s-%s-d%d-c%d-%s-T%d" % (name, dtype, d, chunk, kind, T), errs, dtype)
+    assert torch.isfinite(out).all() and torch.isfinite(S_T).all()
+    assert max(errs.values()) <= TOL[dtype], errs
+
+
+@pytest.mark.parametrize("T", [65, 200])
+@pytest.mark.parametrize("kind", ["sig-2", 0.005])
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("bf16", 128, 32), ("f32", 64, 64)])
+def test_gdr_strong_decay(dtype, d, chunk, kind, T):
+    w = wl.variant_workload(la.LA_GATED_DELTA, dtype, d, d, chunk=chunk, seed=89,
+                            gate_mean=-2.0 if kind == "sig-2" else 4.0)
+    inp = _strong_gates(wl.chunk_inputs(w, B=1, H=2, T=T, S0_std=0.1), kind)
+    print("gdr strong decay", dtype, d, chunk, kind, T, flush=True)
+    errs, (out, S_T, _) = run_chunk(w, inp, chunk, B=1, H=2)
+    record("gdr-strong-%s-d%d-c%d-%s-T%d" % (dtype, d, chunk, kind, T), errs, dtype)
+    assert torch.isfinite(out).all() and torch.isfinite(S_T).all()
+    assert max(errs.values()) <= TOL[dtype], errs
 
 
 @pytest.mark.parametrize("name", list(VARIANTS))
@@ -83,7 +130,7 @@ def test_chunk_size_independence(name):
     inp = wl.chunk_inputs(w, B=1, H=3, T=150, S0_std=0.1, z0=True)
     d = {k: dev(v) for k, v in inp.items()}
     res = []
-    for chunk in (16, 32, 64):
+    for chunk in (16, 32, 64, 128):
         out, S_T, _ = la.la_chunk_fwd(d["q"], d["k"], d["v"], variant=variant, gate=d.get("gate"),
                                       beta=d.get("beta"), S0=d.get("S0"), z0=d.get("z0"), chunk=chunk, phi=phi)
         res.append((host64(out), host64(S_T)))
@@ -149,6 +196,8 @@ def test_in_place_state_and_empty_sequence(name):
     la.la_chunk_fwd(d["q"], d["k"], d["v"], variant=variant, gate=d.get("gate"), beta=d.get("beta"),
                     S0=S, z0=z, S_T=S, z_T=z, phi=phi)
     assert torch.equal(S, ref[1])
+    if z is not None:
+        assert torch.equal(z, ref[2])
     # T = 0: the final state is the initial state
     e = lambda t: None if t is None else t[:, :, :0].contiguous()  # noqa: E731
     o0, S0o, z0o = la.la_chunk_fwd(e(d["q"]), e(d["k"]), e(d["v"]), variant=variant, gate=e(d.get("gate")),
@@ -156,6 +205,26 @@ def test_in_place_state_and_empty_sequence(name):
     assert o0.numel() == 0 and torch.equal(S0o, d["S0"])
     if z0o is not None:
         assert torch.equal(z0o, d["z0"])
+
+
+@pytest.mark.parametrize("T", [40, 1000])
+def test_la_in_place_one_pass_many_value_blocks(T):
+    """Normalized variant in one pass with several value blocks per head (B=1,
+    H=2, d=64 gives four 16-channel blocks; T=40 is too short to segment), z_T
+    and S_T in place of z0 and S0: every block reads z0, one writes z_T."""
+    w = wl.variant_workload(la.LA_NORMALIZED, "f32", 64, 64, chunk=16, phi=la.LA_PHI_ELU1, seed=61)
+    inp = wl.chunk_inputs(w, B=1, H=2, T=T, S0_std=0.1, z0=True)
+    d = {k: dev(v) for k, v in inp.items()}
+    ref = la.la_chunk_fwd(d["q"], d["k"], d["v"], variant=w.variant, S0=d["S0"], z0=d["z0"], chunk=16)
+    S, z = d["S0"].clone(), d["z0"].clone()
+    out, _, _ = la.la_chunk_fwd(d["q"], d["k"], d["v"], variant=w.variant, S0=S, z0=z, S_T=S, z_T=z, chunk=16)
+    assert torch.equal(out, ref[0]) and torch.equal(S, ref[1]) and torch.equal(z, ref[2])
+    ro, rS, rz = oracle.forward(w.variant, inp["q"].f64(), inp["k"].f64(), inp["v"].f64(),
+                                S0=inp["S0"].f64(), z0=inp["z0"].f64())
+    errs = {"out": parity_error(host64(out), ro), "S_T": parity_error(host64(S), rS),
+            "z_T": parity_error(host64(z), rz)}
+    record("la-in-place-one-pass-T%d" % T, errs, "f32")
+    assert max(errs.values()) <= TOL["f32"], errs
 
 
 @pytest.mark.parametrize("B,H,T,d,chunk", [(1, 1, 64 * 20 + 7, 64, 64), (2, 3, 16 * 9, 32, 16),

@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_causal_amd as la
 import oracle
 import workloads as wl
-from gpu_util import TOL, dev, host64, parity_error
+from gpu_util import TOL, dev, host64, parity_error, record
 
 pytestmark = pytest.mark.gpu
 
@@ -53,17 +53,20 @@ def test_decode_matches_oracle(variant, phi, dtype, dk, dv):
     w = wl.variant_workload(variant, dtype, dk, dv, S0_std=0.1, phi=phi, seed=17)
     print("decode parity", variant, phi, dtype, dk, dv, flush=True)
     eo, es, ez = run_decode(w, steps=6, B=2, H=5)
+    record("decode-%d-%d-%s-dk%d-dv%d" % (variant, phi, dtype, dk, dv), {"o": eo, "S": es, "z": ez}, dtype)
     tol = TOL[dtype]
     assert eo <= tol and es <= tol and ez <= tol, (eo, es, ez)
 
 
 def test_decode_gdr_full_shape_1000_steps():
     """The B=256, H=16, d=128 decode sequence: 1000 in-place steps on every head,
-    compared on a sample of heads at every step and on their final state."""
+    compared at every step and on the final state over every 37th head (111
+    heads, every residue modulo 8, so every XCD's share of the launch)."""
     w = wl.WORKLOADS["gdr_decode_b256h16d128"]
-    sample = [0, 1, 15, 16, 1023, 2048, 3001, w.B * w.H - 1]
+    sample = list(range(0, w.B * w.H, 37)) + [w.B * w.H - 1]
     print("decode full shape", w.name, "steps", w.T, flush=True)
     eo, es, _ = run_decode(w, steps=w.T, B=w.B, H=w.H, sample=sample)
+    record("workload-" + w.name, {"o": eo, "S": es}, w.dtype)
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype], (eo, es)
 
 

@@ -215,8 +215,12 @@ def decode_step_inputs(w: Workload, step: int, seed: int | None = None, *,
 
 
 def variant_workload(variant: int, dtype: str, d_k: int, d_v: int, chunk: int = 64,
-                     seed: int = 11, S0_std: float = 0.0, phi: int = -1) -> Workload:
-    """An ad-hoc workload of the same recipe (used for parity sweeps)."""
-    gate_mean = {NORMALIZED: 0.0, GATED: 3.0, GATED_DELTA: 4.0}[variant]
+                     seed: int = 11, S0_std: float = 0.0, phi: int = -1,
+                     gate_mean: float | None = None) -> Workload:
+    """An ad-hoc workload of the same recipe (used for parity sweeps); the
+    gate pre-activation mean defaults to the specified workloads' (a lower
+    mean gives stronger decay)."""
+    if gate_mean is None:
+        gate_mean = {NORMALIZED: 0.0, GATED: 3.0, GATED_DELTA: 4.0}[variant]
     return Workload("custom", variant, dtype, 1, 1, 1, d_k, d_v, chunk,
                     max(d_k, 1) ** -0.5, gate_mean=gate_mean, S0_std=S0_std, seed=seed, phi=phi)
