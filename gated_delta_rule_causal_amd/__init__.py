@@ -19,7 +19,7 @@ from ._lib import (LA_BF16, LA_EHIP, LA_EINVAL, LA_EUNSUPPORTED, LA_F32, LA_GATE
                    LA_GATED_DELTA, LA_NORMALIZED, LA_OK, LA_PHI_ELU1, LA_PHI_IDENTITY,
                    LaDesc, LaError, check, load)
 
-__all__ = ["la_chunk_fwd", "la_decode_step", "la_chunk_fwd_workspace", "la_status_str",
+__all__ = ["la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step", "la_chunk_fwd_workspace", "la_status_str",
            "la_last_error", "la_abi_version", "make_desc", "LaDesc", "LaError",
            "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_F32", "LA_BF16",
            "LA_PHI_IDENTITY", "LA_PHI_ELU1"]
@@ -150,6 +150,33 @@ def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, ch
     check(lib.la_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                            _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_T), _ptr(z_T), _ptr(ws),
                            ws_given, _stream(stream)))
+    return out, S_T, z_T
+
+
+def la_chunk_fwd_noalloc(q, k, v, *, variant, out, gate=None, beta=None, S0=None, z0=None, chunk=0,
+                         phi=None, S_T=None, z_T=None, stream=None):
+    """la_chunk_fwd with the scratch from the library's own device array (C:
+    ``la_chunk_fwd_noalloc``), for callers that cannot allocate: nothing is
+    allocated here either, so ``out`` (and S_T / z_T when wanted) must be
+    passed.  Calls on one GPU share the array and must not overlap in time.
+    Returns (out, S_T, z_T)."""
+    lib = load()
+    dt, d_k, d_v = _check_qkv(q, k, v, "BHT")
+    B, H, T = q.shape[:3]
+    dev, f32 = q.device, torch.float32
+    if out is None:
+        raise ValueError("out: required (this entry point allocates nothing)")
+    _check("gate", gate, (B, H, T, d_k) if variant == LA_GATED else (B, H, T), f32, dev)
+    _check("beta", beta, (B, H, T), f32, dev)
+    _check("S0", S0, (B, H, d_v, d_k), f32, dev)
+    _check("z0", z0, (B, H, d_k), f32, dev)
+    _check("out", out, (B, H, T, d_v), q.dtype, dev)
+    _check("S_T", S_T, (B, H, d_v, d_k), f32, dev)
+    _check("z_T", z_T, (B, H, d_k), f32, dev)
+    _require_gpu(q)
+    desc = make_desc(variant, dt, B, H, T, d_k, d_v, chunk, phi)
+    check(lib.la_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                                   _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_T), _ptr(z_T), _stream(stream)))
     return out, S_T, z_T
 
 

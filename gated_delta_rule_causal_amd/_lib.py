@@ -21,8 +21,9 @@ LA_F32, LA_BF16 = 0, 1
 LA_PHI_IDENTITY, LA_PHI_ELU1 = 0, 1
 LA_ABI_VERSION = 1
 
-EXPORTED = ("la_chunk_fwd_workspace", "la_chunk_fwd", "la_decode_step",
+EXPORTED = ("la_chunk_fwd_workspace", "la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step",
             "la_status_str", "la_last_error", "la_abi_version")
+LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class LaDesc(ctypes.Structure):
@@ -49,6 +50,8 @@ def load(path: str = LIB_PATH):
     lib.la_chunk_fwd_workspace.restype = sz
     lib.la_chunk_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp, vp, sz, vp]
     lib.la_chunk_fwd.restype = ctypes.c_int
+    lib.la_chunk_fwd_noalloc.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp, vp]
+    lib.la_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]

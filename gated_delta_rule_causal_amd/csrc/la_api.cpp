@@ -8,7 +8,15 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "la_internal.hpp"
+
+// Library-held scratch of la_chunk_fwd_noalloc: one array per GPU (each GPU
+// holds its own copy at its own address), kept until the process ends.  In
+// host code `scratch` only names the symbol; its device address comes from
+// hipGetSymbolAddress, per device, in scratch_on_current_device().
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -84,6 +92,28 @@ la_status check_role(const la_desc *d, const float *gate, const float *beta, con
     return LA_OK;
 }
 
+// Device address of `scratch` on the current device, resolved once per device
+// (with that device current) and kept; nullptr if HIP reports an error.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_on_current_device(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -111,10 +141,26 @@ size_t la_chunk_fwd_workspace(const la_desc *d) {
     return la::chunk_workspace_bytes(a);
 }
 
+static la_status chunk_fwd(const la_desc *d, const void *q, const void *k, const void *v, const float *gate,
+                           const float *beta, const float *S0, const float *z0, void *out, float *S_T, float *z_T,
+                           void *workspace, size_t workspace_bytes, void *stream, bool use_scratch);
+
 la_status la_chunk_fwd(const la_desc *d, const void *q, const void *k, const void *v,
                        const float *gate, const float *beta, const float *S0, const float *z0,
                        void *out, float *S_T, float *z_T, void *workspace, size_t workspace_bytes,
                        void *stream) {
+    return chunk_fwd(d, q, k, v, gate, beta, S0, z0, out, S_T, z_T, workspace, workspace_bytes, stream, false);
+}
+
+la_status la_chunk_fwd_noalloc(const la_desc *d, const void *q, const void *k, const void *v,
+                               const float *gate, const float *beta, const float *S0, const float *z0,
+                               void *out, float *S_T, float *z_T, void *stream) {
+    return chunk_fwd(d, q, k, v, gate, beta, S0, z0, out, S_T, z_T, nullptr, 0, stream, true);
+}
+
+static la_status chunk_fwd(const la_desc *d, const void *q, const void *k, const void *v, const float *gate,
+                           const float *beta, const float *S0, const float *z0, void *out, float *S_T, float *z_T,
+                           void *workspace, size_t workspace_bytes, void *stream, bool use_scratch) {
     g_last_error[0] = '\0';
     la_status st = check_desc(d, true);
     if (st != LA_OK) return st;
@@ -139,8 +185,13 @@ la_status la_chunk_fwd(const la_desc *d, const void *q, const void *k, const voi
     a.B = d->B; a.H = d->H; a.T = d->T; a.d_k = d->d_k; a.d_v = d->d_v;
     a.chunk = d->chunk ? d->chunk : 64;
     const size_t need_ws = la::chunk_workspace_bytes(a);
-    if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+    if (use_scratch) {
+        if (need_ws > LA_NOALLOC_SCRATCH_BYTES)
+            return fail(LA_EINVAL, "needs %zu bytes of scratch; la_chunk_fwd_noalloc holds %zu (use la_chunk_fwd)",
+                        need_ws, (size_t)LA_NOALLOC_SCRATCH_BYTES);
+    } else if (need_ws > 0 && (!workspace || workspace_bytes < need_ws)) {
         return fail(LA_EINVAL, "workspace of %zu bytes required, %zu given", need_ws, workspace ? workspace_bytes : 0);
+    }
 
     const size_t dk = d->d_k, dv = d->d_v;
     const Range r_q = range("q", q, tok * dk * esz), r_k = range("k", k, tok * dk * esz);
@@ -166,6 +217,11 @@ la_status la_chunk_fwd(const la_desc *d, const void *q, const void *k, const voi
             if (&o2 != &o && overlaps(o, o2)) return fail(LA_EINVAL, "%s overlaps %s", o.name, o2.name);
     }
     if (heads == 0) return LA_OK;
+    if (use_scratch && need_ws > 0) {
+        hipError_t e = scratch_on_current_device(&workspace);
+        if (e != hipSuccess) return fail(LA_EHIP, "scratch address: %s", hipGetErrorString(e));
+        workspace_bytes = LA_NOALLOC_SCRATCH_BYTES;
+    }
 
     a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.S0 = S0; a.z0 = z0;
     a.out = out; a.S_T = S_T; a.z_T = z_T; a.workspace = workspace; a.workspace_bytes = workspace_bytes;

@@ -31,7 +31,8 @@
  * CONVENTIONS (all entry points)
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
  *     library never allocates, frees or retains memory, and keeps no global
- *     state.  Calls are thread-safe.
+ *     state except the scratch array of la_chunk_fwd_noalloc.  Calls are
+ *     thread-safe (la_chunk_fwd_noalloc: see its note on overlapping calls).
  *   - Tensors are dense, row-major (C order), 16-byte aligned.
  *   - Per-token tensors are (B, H, T, d).  The state S of every variant is
  *     (B, H, d_v, d_k) float32 (row = value channel, column = key channel);
@@ -151,6 +152,28 @@ la_status la_chunk_fwd(const la_desc *desc,
                        void *out, float *S_T, float *z_T,
                        void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/*
+ * la_chunk_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace: the scratch la_chunk_fwd would need comes from a
+ * device array the library holds, LA_NOALLOC_SCRATCH_BYTES on each GPU it
+ * runs on, kept until the process ends.  The entry point itself allocates
+ * nothing (no hipMalloc, no allocating library call); the caller passes every
+ * input and output as for la_chunk_fwd.  A call whose la_chunk_fwd_workspace()
+ * exceeds LA_NOALLOC_SCRATCH_BYTES is rejected with LA_EINVAL before any HIP
+ * call.  Every call on one GPU shares that GPU's array (its contents on entry
+ * do not matter), so calls that overlap in time on one GPU race: serialize
+ * them, e.g. on one stream.  Otherwise the same arguments, checks and results
+ * as la_chunk_fwd.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+la_status la_chunk_fwd_noalloc(const la_desc *desc,
+                               const void *q, const void *k, const void *v,
+                               const float *gate, const float *beta,
+                               const float *S0, const float *z0,
+                               void *out, float *S_T, float *z_T,
+                               void *stream);
 
 /*
  * One recurrent decode step for every (b, h): reads one token, updates the

@@ -258,3 +258,24 @@ def test_binding_rejects_mismatched_decode_args():
     with pytest.raises(ValueError, match="v: shape"):
         la.la_decode_step(q, k, torch.zeros(2, 4, 8), torch.zeros(2, 3, 8, 16), variant=la.LA_GATED_DELTA,
                           gate=torch.ones(2, 3), beta=torch.ones(2, 3))
+
+
+def test_noalloc_rejects_requests_beyond_its_scratch(lib):
+    # 131072 heads of d_k = 128 in one pass would stage 64 MiB of z0, twice the
+    # library's array: rejected before any HIP call
+    d = D(la.LA_NORMALIZED, B=1024, H=128, T=64, d_k=128, d_v=128)
+    assert la.la_chunk_fwd_workspace(d) > _lib.LA_NOALLOC_SCRATCH_BYTES
+    assert lib.la_chunk_fwd_noalloc(ctypes.byref(d), fake(0), fake(1), fake(2), None, None, None, None,
+                                    fake(3), None, None, None) == la.LA_EINVAL
+    assert "scratch" in la.la_last_error()
+    # the argument checks are those of la_chunk_fwd
+    d2 = D(la.LA_GATED_DELTA)
+    assert lib.la_chunk_fwd_noalloc(ctypes.byref(d2), fake(0), fake(1), fake(2), None, None, None, None,
+                                    fake(3), None, None, None) == la.LA_EINVAL
+    assert "gate" in la.la_last_error()
+
+
+def test_noalloc_header_size_matches_binding():
+    text = open(HEADER).read()
+    m = re.search(r"#define LA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.LA_NOALLOC_SCRATCH_BYTES
