@@ -17,18 +17,28 @@ import torch
 
 from ._lib import (LA_BF16, LA_EHIP, LA_EINVAL, LA_EUNSUPPORTED, LA_F32, LA_GATED,  # noqa: F401
                    LA_GATED_DELTA, LA_NORMALIZED, LA_OK, LA_PHI_ELU1, LA_PHI_IDENTITY,
-                   LaDesc, LaError, check, load)
+                   LA_RETENTION, LaDesc, LaError, check, load)
 
 __all__ = ["la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step", "la_chunk_fwd_workspace", "la_status_str",
            "la_last_error", "la_abi_version", "make_desc", "LaDesc", "LaError",
-           "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_F32", "LA_BF16",
+           "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_RETENTION", "LA_F32", "LA_BF16",
            "LA_PHI_IDENTITY", "LA_PHI_ELU1"]
 
 _DTYPES = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}
 
 
 def _default_phi(variant: int) -> int:
-    return LA_PHI_IDENTITY if variant == LA_GATED_DELTA else LA_PHI_ELU1
+    return LA_PHI_ELU1 if variant in (LA_NORMALIZED, LA_GATED) else LA_PHI_IDENTITY
+
+
+def _gate_shape(variant, lead, d_k):
+    """Shape of the gate argument: (H,) fixed per-head decay (normalized,
+    retention); per token (delta rule); per token and key channel (gated)."""
+    if variant in (LA_NORMALIZED, LA_RETENTION):
+        return (lead[1],)
+    if variant == LA_GATED_DELTA:
+        return tuple(lead)
+    return tuple(lead) + (d_k,)
 
 
 def make_desc(variant: int, dtype: int, B: int, H: int, T: int, d_k: int, d_v: int,
@@ -124,7 +134,7 @@ def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, ch
     dt, d_k, d_v = _check_qkv(q, k, v, "BHT")
     B, H, T = q.shape[:3]
     dev, f32 = q.device, torch.float32
-    _check("gate", gate, (B, H, T, d_k) if variant == LA_GATED else (B, H, T), f32, dev)
+    _check("gate", gate, _gate_shape(variant, (B, H, T), d_k), f32, dev)
     _check("beta", beta, (B, H, T), f32, dev)
     _check("S0", S0, (B, H, d_v, d_k), f32, dev)
     _check("z0", z0, (B, H, d_k), f32, dev)
@@ -166,7 +176,7 @@ def la_chunk_fwd_noalloc(q, k, v, *, variant, out, gate=None, beta=None, S0=None
     dev, f32 = q.device, torch.float32
     if out is None:
         raise ValueError("out: required (this entry point allocates nothing)")
-    _check("gate", gate, (B, H, T, d_k) if variant == LA_GATED else (B, H, T), f32, dev)
+    _check("gate", gate, _gate_shape(variant, (B, H, T), d_k), f32, dev)
     _check("beta", beta, (B, H, T), f32, dev)
     _check("S0", S0, (B, H, d_v, d_k), f32, dev)
     _check("z0", z0, (B, H, d_k), f32, dev)
@@ -193,7 +203,7 @@ def la_decode_step(q, k, v, S, *, variant, gate=None, beta=None, z=None, phi=Non
     dev, f32 = q.device, torch.float32
     if S is None:
         raise ValueError("S: the state is required")
-    _check("gate", gate, (B, H, d_k) if variant == LA_GATED else (B, H), f32, dev)
+    _check("gate", gate, _gate_shape(variant, (B, H), d_k), f32, dev)
     _check("beta", beta, (B, H), f32, dev)
     _check("S", S, (B, H, d_v, d_k), f32, dev)
     _check("z", z, (B, H, d_k), f32, dev)

@@ -16,10 +16,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libla.so")
 
 LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP = 0, 1, 2, 3
-LA_NORMALIZED, LA_GATED, LA_GATED_DELTA = 0, 1, 2
+LA_NORMALIZED, LA_GATED, LA_GATED_DELTA, LA_RETENTION = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
 LA_PHI_IDENTITY, LA_PHI_ELU1 = 0, 1
-LA_ABI_VERSION = 1
+LA_ABI_VERSION = 2
 
 EXPORTED = ("la_chunk_fwd_workspace", "la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step",
             "la_status_str", "la_last_error", "la_abi_version")

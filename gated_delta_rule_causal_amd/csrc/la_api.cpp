@@ -52,7 +52,7 @@ bool misaligned(const void *p, uintptr_t a) { return p && (reinterpret_cast<uint
 // Checks shared by both entry points.  n_tok = tokens per head that the call reads.
 la_status check_desc(const la_desc *d, bool chunked) {
     if (!d) return fail(LA_EINVAL, "desc is NULL");
-    if (d->variant < LA_NORMALIZED || d->variant > LA_GATED_DELTA)
+    if (d->variant < LA_NORMALIZED || d->variant > LA_RETENTION)
         return fail(LA_EINVAL, "variant %d is not a la_variant", d->variant);
     if (d->dtype != LA_F32 && d->dtype != LA_BF16) return fail(LA_EINVAL, "dtype %d is not a la_dtype", d->dtype);
     if (d->phi != LA_PHI_IDENTITY && d->phi != LA_PHI_ELU1) return fail(LA_EINVAL, "phi %d is not a la_phi", d->phi);
@@ -77,20 +77,38 @@ la_status check_desc(const la_desc *d, bool chunked) {
     return LA_OK;
 }
 
+// How a variant's gate is laid out: one decay per head (H,), optional;
+// one per token (B,H,T) / (B,H); one per token and key channel.
+enum GateKind { GATE_PER_HEAD, GATE_PER_TOKEN, GATE_PER_CHANNEL };
+GateKind gate_kind(int variant) {
+    if (variant == LA_NORMALIZED || variant == LA_RETENTION) return GATE_PER_HEAD;
+    if (variant == LA_GATED_DELTA) return GATE_PER_TOKEN;
+    return GATE_PER_CHANNEL;
+}
+bool has_beta(int variant) { return variant == LA_GATED_DELTA; }
+
 la_status check_role(const la_desc *d, const float *gate, const float *beta, const float *z_in,
                      const float *z_out, bool need_data) {
-    if (d->variant == LA_NORMALIZED) {
-        if (gate) return fail(LA_EINVAL, "gate must be NULL for LA_NORMALIZED");
-        if (beta) return fail(LA_EINVAL, "beta must be NULL for LA_NORMALIZED");
-    } else {
-        if (z_in || z_out) return fail(LA_EINVAL, "z must be NULL unless the variant is LA_NORMALIZED");
-        if (need_data && !gate) return fail(LA_EINVAL, "gate is required for this variant");
-        if (d->variant == LA_GATED && beta) return fail(LA_EINVAL, "beta must be NULL for LA_GATED");
-        if (d->variant == LA_GATED_DELTA && need_data && !beta)
-            return fail(LA_EINVAL, "beta is required for LA_GATED_DELTA");
-    }
+    if (d->variant != LA_NORMALIZED && (z_in || z_out))
+        return fail(LA_EINVAL, "z must be NULL unless the variant is LA_NORMALIZED");
+    if (gate_kind(d->variant) != GATE_PER_HEAD && need_data && !gate)
+        return fail(LA_EINVAL, "gate is required for this variant");
+    if (!has_beta(d->variant) && beta) return fail(LA_EINVAL, "beta must be NULL for this variant");
+    if (has_beta(d->variant) && need_data && !beta) return fail(LA_EINVAL, "beta is required for LA_GATED_DELTA");
     return LA_OK;
 }
+
+// Bytes of the gate argument: `per` tokens per head (T, or 1 for decode).
+size_t gate_bytes(const la_desc *d, size_t heads, size_t per) {
+    switch (gate_kind(d->variant)) {
+        case GATE_PER_HEAD: return static_cast<size_t>(d->H) * 4;
+        case GATE_PER_TOKEN: return heads * per * 4;
+        default: return heads * per * static_cast<size_t>(d->d_k) * 4;
+    }
+}
+// Alignment of the gate argument: scalars per head or token are read one at
+// a time, per-channel gates as 16-byte vectors.
+uintptr_t gate_align(int variant) { return gate_kind(variant) == GATE_PER_CHANNEL ? 16 : 4; }
 
 // Device address of `scratch` on the current device, resolved once per device
 // (with that device current) and kept; nullptr if HIP reports an error.
@@ -175,8 +193,8 @@ static la_status chunk_fwd(const la_desc *d, const void *q, const void *k, const
     const void *ptrs[] = {q, k, v, gate, beta, S0, z0, out, S_T, z_T, workspace};
     const char *names[] = {"q", "k", "v", "gate", "beta", "S0", "z0", "out", "S_T", "z_T", "workspace"};
     for (int i = 0; i < 11; ++i) {
-        // per-token gate / beta of the gated delta rule are read with scalar loads
-        uintptr_t al = (i == 3 && d->variant == LA_GATED_DELTA) || i == 4 ? 4 : 16;
+        // scalar gates (per head or per token) and beta are read with scalar loads
+        uintptr_t al = i == 3 ? gate_align(d->variant) : i == 4 ? 4 : 16;
         if (misaligned(ptrs[i], al)) return fail(LA_EINVAL, "%s is not %d-byte aligned", names[i], (int)al);
     }
 
@@ -196,7 +214,7 @@ static la_status chunk_fwd(const la_desc *d, const void *q, const void *k, const
     const size_t dk = d->d_k, dv = d->d_v;
     const Range r_q = range("q", q, tok * dk * esz), r_k = range("k", k, tok * dk * esz);
     const Range r_v = range("v", v, tok * dv * esz);
-    const Range r_g = range("gate", gate, d->variant == LA_GATED ? tok * dk * 4 : tok * 4);
+    const Range r_g = range("gate", gate, gate_bytes(d, heads, static_cast<size_t>(d->T)));
     const Range r_b = range("beta", beta, tok * 4);
     const Range r_s0 = range("S0", S0, heads * dv * dk * 4), r_z0 = range("z0", z0, heads * dk * 4);
     const Range r_o = range("out", out, tok * dv * esz);
@@ -248,14 +266,14 @@ la_status la_decode_step(const la_desc *d, const void *q, const void *k, const v
     const void *ptrs[] = {q, k, v, gate, beta, S, z, out};
     const char *names[] = {"q", "k", "v", "gate", "beta", "S", "z", "out"};
     for (int i = 0; i < 8; ++i) {
-        uintptr_t al = (i == 3 && d->variant == LA_GATED_DELTA) || i == 4 ? 4 : 16;
+        uintptr_t al = i == 3 ? gate_align(d->variant) : i == 4 ? 4 : 16;
         if (i == 7) al = esz;  // one output element per state row
         if (misaligned(ptrs[i], al)) return fail(LA_EINVAL, "%s is not %d-byte aligned", names[i], (int)al);
     }
     const size_t dk = d->d_k, dv = d->d_v;
     const Range r_q = range("q", q, heads * dk * esz), r_k = range("k", k, heads * dk * esz);
     const Range r_v = range("v", v, heads * dv * esz);
-    const Range r_g = range("gate", gate, d->variant == LA_GATED ? heads * dk * 4 : heads * 4);
+    const Range r_g = range("gate", gate, gate_bytes(d, heads, 1));
     const Range r_b = range("beta", beta, heads * 4);
     const Range r_s = range("S", S, heads * dv * dk * 4), r_z = range("z", z, heads * dk * 4);
     const Range r_o = range("out", out, heads * dv * esz);

@@ -20,6 +20,11 @@ struct ChunkParams {
     // slot s >= 1: the state increment of segment s - 1)
     int seg_len = 0, n_seg = 1;
     const float *seg_state = nullptr;
+    // normalized / retention: heads per batch entry (the per-head decay of
+    // head bh is gate[bh % H]; gate NULL = no decay) and whether the
+    // normalizer is carried (normalized) or not (retention)
+    int H = 1;
+    int normalize = 1;
 };
 
 // Copy rows [0, n) of a D-wide row-major global tile (row stride `lds`

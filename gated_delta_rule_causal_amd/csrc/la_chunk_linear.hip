@@ -7,7 +7,16 @@
 //   P   = M o (phiQ phiK^T)                       (M: j <= t, a token sees itself)
 //   O   = (phiQ S0^T + P V) / (phiQ z0 + P 1)
 //   S_C = S0 + V^T phiK,   z_C = z0 + phiK^T 1.
-// The denominator uses the same rounded P as the numerator.
+// The denominator uses the same rounded P as the numerator.  With a fixed
+// per-head decay gamma (same page, section "Fixed decay versus an
+// input-dependent gate": S and z both decay before each write) every term
+// carries the power of gamma that unrolling the recurrence gives, for tokens
+// t, j = 0 .. n-1 of the chunk:
+//   P_tj *= gamma^(t-j),  the S0 / z0 terms of token t *= gamma^(t+1),
+//   S_C = gamma^n S0 + sum_j gamma^(n-1-j) v_j phi(k_j)^T  (z_C likewise);
+// every power is at most 1 and comes from a per-chunk table gamma^0..gamma^C.
+// Retention (page "Ch. 11 Linear attention and Hyena", 11.3, RetNet bullet)
+// is the same path without the normalizer.
 //
 // Gated (page "Ch. 11 Linear attention and Hyena", 11.3 and the solution to
 // Exercise 11.5): per-channel gates gamma_t, decay between tokens j <= t of
@@ -243,7 +252,7 @@ struct LinearLds {
     static constexpr int P_BYTES = C * LDC * (int)sizeof(Op);
     static constexpr int G_BYTES = GATED ? C * LDG * 4 : 0;
     static constexpr int PG_BYTES = P_BYTES > G_BYTES ? P_BYTES : G_BYTES;
-    static constexpr int F_FLOATS = GATED ? (NB + 1 + NRHO) * DK : DK + C;
+    static constexpr int F_FLOATS = GATED ? (NB + 1 + NRHO) * DK : DK + C + C + 4;   // normalized: z, den, gamma^0..C
     static constexpr int KT_ELEMS = GATED ? C * LDK : 8;   // gated: state-update key operand
     static constexpr int BYTES = (GATED ? 3 : 2) * C * LDK * (int)sizeof(Op) + KT_ELEMS * (int)sizeof(Op) +
                                  C * LDV * (int)sizeof(Op) + PG_BYTES + F_FLOATS * 4;
@@ -280,6 +289,7 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     float *sRho = sF + (NB + 1) * DK;     // gated: prod of the blocks strictly between J and I, [NRHO][DK]
     float *sZ = sF;                       // normalized: running z, [DK]
     float *sDen = sF + DK;                // normalized: denominators, [C]
+    float *sPow = sF + DK + C;            // not gated: gamma^k of the per-head decay, k = 0 .. C
 
     // the wave index is uniform: role branches compile to scalar branches
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -301,6 +311,15 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
     IO *oh = static_cast<IO *>(p.out) + tok0 * p.d_v;
     const float *gh = GATED ? p.gate + tok0 * DK : nullptr;
 
+    // not gated: log2 of the head's fixed decay (0 without one: every power is
+    // 1, and `decay` is false so that the undecayed path skips the factors)
+    const float l2g = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(
+                   int, !GATED && p.gate ? __builtin_amdgcn_logf(p.gate[bh % p.H]) : 0.f)));
+    const bool decay = !GATED && l2g != 0.f;
+    if constexpr (!GATED) {
+        for (int e = tid; e <= C; e += NTHR) sPow[e] = __builtin_amdgcn_exp2f(static_cast<float>(e) * l2g);
+    }
     f32x4 st[NCB];
     const size_t srow = (static_cast<size_t>(bh) * p.d_v + (wave < WS ? vch : 0)) * DK;
     const size_t slot = static_cast<size_t>(p.d_v) * DK + DK;   // floats per seg_state slot
@@ -328,13 +347,19 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                     v[j][cb] = *reinterpret_cast<const float4 *>(col + min(s0 + j, seg) * slot + 16 * cb);
 #pragma unroll
             for (int j = 0; j < SB; ++j)
-                if (s0 + j <= seg)
+                if (s0 + j <= seg) {
+                    // slot s0 + j reaches this segment's start after (seg - s0 - j)
+                    // whole segments of decay
+                    const float w = decay ? __builtin_amdgcn_exp2f(static_cast<float>((seg - s0 - j) * p.seg_len) * l2g)
+                                          : 1.f;
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) st[cb] += f32x4{v[j][cb].x, v[j][cb].y, v[j][cb].z, v[j][cb].w};
+                    for (int cb = 0; cb < NCB; ++cb)
+                        st[cb] += w * f32x4{v[j][cb].x, v[j][cb].y, v[j][cb].z, v[j][cb].w};
+                }
         }
     }
     if constexpr (!GATED) {
-        for (int c = tid; c < DK; c += NTHR) {
+        for (int c = tid; c < DK && p.normalize; c += NTHR) {
             float z = 0.f;
             if (p.n_seg > 1) {
                 const float *zc = segs + static_cast<size_t>(p.d_v) * DK + c;
@@ -344,7 +369,9 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                     for (int j = 0; j < 8; ++j) v[j] = zc[min(s0 + j, seg) * slot];
 #pragma unroll
                     for (int j = 0; j < 8; ++j)
-                        if (s0 + j <= seg) z += v[j];
+                        if (s0 + j <= seg)
+                            z += (decay ? __builtin_amdgcn_exp2f(static_cast<float>((seg - s0 - j) * p.seg_len) * l2g) : 1.f) *
+                                 v[j];
                 }
             } else if (p.z0) {
                 z = p.z0[static_cast<size_t>(bh) * DK + c];
@@ -569,30 +596,42 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                                            sQ + 16 * I * LDK, LDK, lane);
             } else {
                 tile_mma_ll<DK>(acc, sK + 16 * J * LDK, LDK, sQ + 16 * I * LDK, LDK, lane);
+                // fixed decay: P_tj *= gamma^(t - j)
+                if (decay) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] *= sPow[max(t - j0 - i, 0)];
+                }
             }
             st_group(sP + t * LDC + j0, Gp::make(j0 <= t ? acc[0] : 0.f, j0 + 1 <= t ? acc[1] : 0.f,
                                                  j0 + 2 <= t ? acc[2] : 0.f, j0 + 3 <= t ? acc[3] : 0.f));
         }
         __syncthreads();
 
-        if constexpr (!GATED) {
-            // ---- denominators phi(q_t).z0 + sum_j P_tj (the rounded P of the
-            // numerator); 8 lanes per token
+        if (!GATED && p.normalize) {
+            // ---- denominators gamma^(t+1) phi(q_t).z0 + sum_j P_tj (the rounded
+            // P of the numerator); 8 lanes per token
             for (int e = tid; e < 8 * C; e += NTHR) {
                 const int t = e >> 3, part = e & 7;
-                float d = 0.f;
-                for (int c = part; c < DK; c += 8) d += to_f32(sQ[t * LDK + c]) * sZ[c];
-                for (int j = part; j <= t; j += 8) d += to_f32(sP[t * LDC + j]);
-                d = group_sum<8>(d);
+                float dz = 0.f, dp = 0.f;
+                for (int c = part; c < DK; c += 8) dz += to_f32(sQ[t * LDK + c]) * sZ[c];
+                for (int j = part; j <= t; j += 8) dp += to_f32(sP[t * LDC + j]);
+                const float d = group_sum<8>((decay ? sPow[t + 1] * dz : dz) + dp);
                 if (part == 0) sDen[t] = d;
             }
             __syncthreads();
-            // z_C = z0 + phiK^T 1 (after every denominator has read z0)
+            // z_C = gamma^n z0 + sum_t gamma^(n-1-t) phi(k_t) (after every
+            // denominator has read z0)
             for (int c = tid; c < DK; c += NTHR) {
                 float s = 0.f;
+                if (decay) {
 #pragma unroll 8
-                for (int t = 0; t < C; ++t) s += to_f32(sK[t * LDK + c]);
-                sZ[c] += s;
+                    for (int t = 0; t < n; ++t) s += sPow[n - 1 - t] * to_f32(sK[t * LDK + c]);
+                    sZ[c] = sPow[n] * sZ[c] + s;
+                } else {
+#pragma unroll 8
+                    for (int t = 0; t < C; ++t) s += to_f32(sK[t * LDK + c]);   // rows past n are zero
+                    sZ[c] += s;
+                }
             }
         }
 
@@ -611,6 +650,12 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                     else tile_mma_rl_scaled<NCB>(o, sb, sQ + 16 * I * LDK, LDK, sE + I * DK, lane);
                 } else {
                     tile_mma_rl_n<NCB>(o, sb, sQ + 16 * I * LDK, LDK, NCB, lane);
+                    // fixed decay: the entering state reaches token t after t + 1 steps
+                    if (decay) {
+                        const float lead = sPow[16 * I + lr + 1];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[i] *= lead;
+                    }
                 }
                 // + V^T P^T: V^T by transposing reads of the value tile
                 const Op *prow = sP + (16 * I + lr) * LDC + 4 * lg;
@@ -619,18 +664,36 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                     mma32(o, kt_group<0>(sV, LDV, t0, 16 * wave, lane), kt_group<0>(sV, LDV, t0 + 16, 16 * wave, lane),
                           ld_group(prow + t0), ld_group(prow + t0 + 16));
                 if constexpr (C % 32 == 16) mma16(o, kt_group<0>(sV, LDV, C - 16, 16 * wave, lane), ld_group(prow + C - 16));
-                if constexpr (!GATED) {
+                if (!GATED && p.normalize) {
                     const float inv = 1.f / sDen[16 * I + lr];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) o[i] *= inv;
                 }
                 ob[I] = o;
             }
+            // V^T operand groups of the state update (the same for every key
+            // block); not gated: token t's value scaled by gamma^(n-1-t)
+            G4 vg[NB];
+#pragma unroll
+            for (int s2 = 0; s2 < NB; ++s2) {
+                vg[s2] = kt_group<0>(sV, LDV, 16 * s2, 16 * wave, lane);
+                if (decay) {
+                    float x[4];
+                    Gp::unpack(vg[s2], x);
+                    const int t0 = 16 * s2 + 4 * lg;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[i] *= sPow[max(n - 1 - t0 - i, 0)];
+                    vg[s2] = Gp::make(x[0], x[1], x[2], x[3]);
+                }
+            }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 if constexpr (GATED) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) st[cb][i] *= sD[16 * cb + 4 * lg + i];
+                } else if (decay) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st[cb][i] *= sPow[n];
                 }
                 // S^T += K^T V (gated: the scaled key operand): both from the
                 // token-major tiles by transposing reads
@@ -638,11 +701,9 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
 #pragma unroll
                 for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
                     mma32(st[cb], kt_group<0>(kt, LDK, 16 * s2, 16 * cb, lane),
-                          kt_group<0>(kt, LDK, 16 * s2 + 16, 16 * cb, lane), kt_group<0>(sV, LDV, 16 * s2, 16 * wave, lane),
-                          kt_group<0>(sV, LDV, 16 * s2 + 16, 16 * wave, lane));
+                          kt_group<0>(kt, LDK, 16 * s2 + 16, 16 * cb, lane), vg[s2], vg[s2 + 1]);
                 if constexpr (NB % 2 == 1)
-                    mma16(st[cb], kt_group<0>(kt, LDK, 16 * (NB - 1), 16 * cb, lane),
-                          kt_group<0>(sV, LDV, 16 * (NB - 1), 16 * wave, lane));
+                    mma16(st[cb], kt_group<0>(kt, LDK, 16 * (NB - 1), 16 * cb, lane), vg[NB - 1]);
             }
         }
         __syncthreads();
@@ -657,7 +718,7 @@ __global__ void __launch_bounds__(NW * 64) linear_chunk_kernel(const ChunkParams
                 make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
     }
     if constexpr (!GATED) {
-        if (p.z_T && vb == 0 && last_seg)
+        if (p.normalize && p.z_T && vb == 0 && last_seg)
             for (int c = tid; c < DK; c += NTHR) p.z_T[static_cast<size_t>(bh) * DK + c] = sZ[c];
     }
 }
@@ -1090,19 +1151,21 @@ __global__ void __launch_bounds__(NW * 64) gla_pipelined_kernel(const ChunkParam
 }
 
 // ------------------------------------------------------------------ segments
-// Normalized variant only: its state is a plain sum over the tokens
-// (S_C = S0 + V^T phiK, z_C = z0 + phiK^T 1), so the sequence can be cut into
-// segments that run concurrently, each entering with the initial state plus
-// the increments of the segments before it.  la_segment_state_kernel fills
-// the slots of ChunkParams::seg_state: slot 0 of a head is (S0, z0) (zeros
-// when absent), slot s >= 1 the increment of segment s - 1,
-//   dS = V^T phiK  (value rows x key columns),   dz = phiK^T 1,
-// over that segment's tokens, with phiK rounded to the operand type as the
-// chunk kernel rounds it.  Copying S0 here also lets S_T alias S0: every read
-// of S0 is done before the chunk kernel starts.  One workgroup per (head,
-// slot, DVA-channel value block), four waves; the (value, key) 16x16 tiles of
-// the block are dealt to the waves round robin.
-template <class DT, int DK, int DVA, int C>
+// Normalized and retention variants: their state is a plain sum over the
+// tokens (S_C = S0 + V^T phiK, z_C = z0 + phiK^T 1; with a fixed decay each
+// term decayed to the end), so the sequence can be cut into segments that run
+// concurrently, each entering with the initial state plus the increments of
+// the segments before it, decayed by gamma^L per whole segment of L tokens
+// in between.  la_segment_state_kernel fills the slots of
+// ChunkParams::seg_state: slot 0 of a head is (S0, z0) (zeros when absent),
+// slot s >= 1 the increment of segment s - 1,
+//   dS = sum_t gamma^(L_s-1-t) v_t phi(k_t)^T,   dz = sum_t gamma^(L_s-1-t) phi(k_t),
+// over that segment's L_s tokens t, with the scaled phi(k_t) rounded to the
+// operand type before both sums.  Copying S0 here also lets S_T alias S0:
+// every read of S0 is done before the chunk kernel starts.  One workgroup per
+// (head, slot, DVA-channel value block), four waves; the (value, key) 16x16
+// tiles of the block are dealt to the waves round robin.
+template <int PHI, class DT, int DK, int DVA, int C>
 __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams p, float *ws) {
     typedef typename DT::storage IO;
     typedef typename OpOf<DT>::type Op;
@@ -1133,6 +1196,7 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
     }
     const int tb = (s - 1) * p.seg_len;
     const int Tn = min(p.seg_len, p.T - tb);
+    const float l2g = p.gate ? __builtin_amdgcn_logf(p.gate[bh % p.H]) : 0.f;   // fixed decay, 0 = none
     const IO *kh = static_cast<const IO *>(p.k) + (static_cast<size_t>(bh) * p.T + tb) * DK;
     const IO *vh = static_cast<const IO *>(p.v) + (static_cast<size_t>(bh) * p.T + tb) * p.d_v + DVA * vb;
     // the rows of the next two chunks are loaded into registers (two sets,
@@ -1172,10 +1236,12 @@ __global__ void __launch_bounds__(256) la_segment_state_kernel(const ChunkParams
             if (k.TOTAL % 256 != 0 && e >= k.TOTAL) continue;
             const int t = e / k.VPR, c = (e % k.VPR) * k.VE;
             const bool ok = ((k.valid >> i) & 1u) && t < n;
+            // token c0 + t decays over the Tn - 1 - (c0 + t) tokens after it
+            const float w = l2g != 0.f ? __builtin_amdgcn_exp2f(static_cast<float>(Tn - 1 - c0 - t) * l2g) : 1.f;
             float x[8];
             unpack(k.r[i], x);
 #pragma unroll
-            for (int j = 0; j < k.VE; ++j) x[j] = ok ? phi_elu1(x[j]) : 0.f;
+            for (int j = 0; j < k.VE; ++j) x[j] = ok ? apply_phi<PHI>(x[j]) * w : 0.f;
 #pragma unroll
             for (int j = 0; j < k.VE; j += 4) {
                 const typename Gp::type g = Gp::make(x[j], x[j + 1], x[j + 2], x[j + 3]);
@@ -1261,7 +1327,7 @@ constexpr int kComputeUnits = 256;
 // long (chunks are at least 16 tokens).  max_segments bounds the count for
 // any chunk length; it sizes the workspace.
 static int64_t linear_max_segments(const ChunkArgs &a) {
-    if (a.variant != LA_NORMALIZED || a.T <= 0) return 1;
+    if ((a.variant != LA_NORMALIZED && a.variant != LA_RETENTION) || a.T <= 0) return 1;
     const int64_t wgs = static_cast<int64_t>(a.B) * a.H * (a.d_v / std::min(a.d_v, 64));
     if (wgs <= 0 || wgs >= kComputeUnits) return 1;
     return std::max<int64_t>(1, std::min<int64_t>((kComputeUnits + wgs - 1) / wgs, (a.T + 15) / 16 / 2));
@@ -1289,6 +1355,8 @@ static hipError_t launch_linear_t(const ChunkArgs &a) {
     p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.beta = nullptr; p.S0 = a.S0; p.z0 = a.z0;
     p.out = a.out; p.S_T = a.S_T; p.z_T = a.z_T;
     p.T = a.T; p.d_v = a.d_v; p.n_vblk = a.d_v / DVB; p.n_heads = a.B * a.H;
+    p.H = a.H;
+    p.normalize = a.variant == LA_NORMALIZED;
     if constexpr (!GATED) {
         const int per = linear_segment_chunks(a, C);
         const int nchunks = (a.T + C - 1) / C;
@@ -1297,9 +1365,9 @@ static hipError_t launch_linear_t(const ChunkArgs &a) {
             p.n_seg = (nchunks + per - 1) / per;
             p.seg_state = static_cast<const float *>(a.workspace);
             const int64_t sblocks = static_cast<int64_t>(p.n_heads) * p.n_seg * (a.d_v / DVB);
-            hipLaunchKernelGGL((la_segment_state_kernel<DT, DK, DVB, C>), dim3(static_cast<uint32_t>(sblocks)), dim3(256), 0,
+            hipLaunchKernelGGL((la_segment_state_kernel<PHI, DT, DK, DVB, C>), dim3(static_cast<uint32_t>(sblocks)), dim3(256), 0,
                                a.stream, p, static_cast<float *>(a.workspace));
-        } else if (a.T > 0 && p.n_vblk > 1 && a.z0 && a.z_T == a.z0) {
+        } else if (p.normalize && a.T > 0 && p.n_vblk > 1 && a.z0 && a.z_T == a.z0) {
             // one pass, several value blocks per head, z_T in place of z0: every
             // value block's workgroup reads z0 but only block 0 writes z_T, and a
             // workgroup may start after block 0 has finished, so the blocks read
@@ -1364,7 +1432,11 @@ static hipError_t linear_dk(const ChunkArgs &a) {
 
 template <class DT>
 static hipError_t linear_variant(const ChunkArgs &a) {
-    if (a.variant == LA_NORMALIZED) return linear_dk<false, LA_PHI_ELU1, DT>(a);
+    // normalized and retention share the ungated kernels (the normalizer is a
+    // runtime switch; the normalized variant always uses elu+1)
+    if (a.variant == LA_NORMALIZED || (a.variant == LA_RETENTION && a.phi == LA_PHI_ELU1))
+        return linear_dk<false, LA_PHI_ELU1, DT>(a);
+    if (a.variant == LA_RETENTION) return linear_dk<false, LA_PHI_IDENTITY, DT>(a);
     if (a.phi == LA_PHI_ELU1) return linear_dk<true, LA_PHI_ELU1, DT>(a);
     return linear_dk<true, LA_PHI_IDENTITY, DT>(a);
 }
@@ -1372,11 +1444,11 @@ static hipError_t linear_variant(const ChunkArgs &a) {
 // Workspace of the chunked forward: the segment slots of the normalized
 // variant (none for the other variants).
 size_t chunk_workspace_bytes(const ChunkArgs &a) {
-    if (a.variant != LA_NORMALIZED || a.T <= 0) return 0;
+    if ((a.variant != LA_NORMALIZED && a.variant != LA_RETENTION) || a.T <= 0) return 0;
     const int64_t n = linear_max_segments(a);
     const size_t heads = static_cast<size_t>(a.B) * a.H;
-    // segment slots, or (one pass) a staged copy of z0 for z_T aliasing it
-    const size_t zstage = heads * a.d_k * sizeof(float);
+    // segment slots, or (normalized, one pass) a staged copy of z0 for z_T aliasing it
+    const size_t zstage = a.variant == LA_NORMALIZED ? heads * a.d_k * sizeof(float) : 0;
     if (n < 2) return zstage;
     return std::max(zstage, heads * n * (static_cast<size_t>(a.d_v) * a.d_k + a.d_k) * sizeof(float));
 }

@@ -20,9 +20,13 @@
 //   gated linear attention (page "Ch. 11 Linear attention and Hyena", 11.3):
 //     r = S_i.(gamma o phi(q)),  S_i <- S_i o gamma + v_i phi(k),
 //     o_i = r + v_i (phi(k).phi(q))                 (= S_new,i . phi(q))
-//   normalized (page "Beyond -- Linear attention and recurrent memory"):
-//     r = S_i.phi(q),  S_i <- S_i + v_i phi(k),  z <- z + phi(k),
-//     o_i = (r + v_i (phi(k).phi(q))) / (z_old.phi(q) + phi(k).phi(q))
+//   normalized (page "Beyond -- Linear attention and recurrent memory"),
+//   with the head's fixed decay gamma (1 without one; section "Fixed decay
+//   versus an input-dependent gate"):
+//     r = gamma S_i.phi(q),  S_i <- gamma S_i + v_i phi(k),  z <- gamma z + phi(k),
+//     o_i = (r + v_i (phi(k).phi(q))) / (gamma z_old.phi(q) + phi(k).phi(q))
+//   retention (page "Ch. 11 Linear attention and Hyena", 11.3, RetNet bullet):
+//     the same without z: o_i = r + v_i (phi(k).phi(q))
 #include "la_internal.hpp"
 
 namespace la {
@@ -34,7 +38,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const typename DT::storage *__restrict__ q, const typename DT::storage *__restrict__ k,
     const typename DT::storage *__restrict__ v, const float *__restrict__ gate,
     const float *__restrict__ beta, float *__restrict__ S, float *__restrict__ z,
-    typename DT::storage *__restrict__ out, int64_t n_heads) {
+    typename DT::storage *__restrict__ out, int64_t n_heads, int H) {
     constexpr int G = DK / 8;                                // lanes per state row
     constexpr int GROUPS = kDecodeThreads / G;               // row groups per workgroup
     constexpr int HPW = GROUPS >= DV ? GROUPS / DV : 1;      // heads per workgroup
@@ -103,14 +107,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 for (int c = 0; c < 8; ++c) s[r][c] = s[r][c] * gm[c] + vv[r] * fk[c];
                 vv[r] = rq + vv[r] * kq;
             }
-        } else {
-            float zz[8];
-            load8(z + h * DK + c0, zz);
-            float zq = 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) zq += zz[c] * fq[c];
-            zq = group_sum<G>(zq);
-            const float inv_den = 1.f / (zq + kq);
+        } else if constexpr (VAR == LA_RETENTION) {
+            const float gm = gate ? gate[h % H] : 1.f;
 #pragma unroll
             for (int r = 0; r < RPG; ++r) {
                 float rq = 0.f;
@@ -118,15 +116,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
                 for (int c = 0; c < 8; ++c) rq += s[r][c] * fq[c];
                 rq = group_sum<G>(rq);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) s[r][c] = s[r][c] + vv[r] * fk[c];
-                vv[r] = (rq + vv[r] * kq) * inv_den;
+                for (int c = 0; c < 8; ++c) s[r][c] = gm * s[r][c] + vv[r] * fk[c];
+                vv[r] = gm * rq + vv[r] * kq;
+            }
+        } else {
+            const float gm = gate ? gate[h % H] : 1.f;
+            float zz[8];
+            load8(z + h * DK + c0, zz);
+            float zq = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) zq += zz[c] * fq[c];
+            zq = group_sum<G>(zq);
+            const float inv_den = 1.f / (gm * zq + kq);
+#pragma unroll
+            for (int r = 0; r < RPG; ++r) {
+                float rq = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) rq += s[r][c] * fq[c];
+                rq = group_sum<G>(rq);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) s[r][c] = gm * s[r][c] + vv[r] * fk[c];
+                vv[r] = (gm * rq + vv[r] * kq) * inv_den;
             }
             // every group of the head has read z; only then may row 0's group overwrite it
             __syncthreads();
             if (active && row0 == 0) {
                 float4 *zp = reinterpret_cast<float4 *>(z + h * DK + c0);
-                zp[0] = make_float4(zz[0] + fk[0], zz[1] + fk[1], zz[2] + fk[2], zz[3] + fk[3]);
-                zp[1] = make_float4(zz[4] + fk[4], zz[5] + fk[5], zz[6] + fk[6], zz[7] + fk[7]);
+                zp[0] = make_float4(gm * zz[0] + fk[0], gm * zz[1] + fk[1], gm * zz[2] + fk[2], gm * zz[3] + fk[3]);
+                zp[1] = make_float4(gm * zz[4] + fk[4], gm * zz[5] + fk[5], gm * zz[6] + fk[6], gm * zz[7] + fk[7]);
             }
         }
     }
@@ -154,7 +171,7 @@ static hipError_t launch_decode_t(const DecodeArgs &a) {
     hipLaunchKernelGGL((decode_kernel<VAR, DT, DK, DV, PHI>), dim3(static_cast<uint32_t>(blocks)),
                        dim3(kDecodeThreads), 0, a.stream, static_cast<const T *>(a.q),
                        static_cast<const T *>(a.k), static_cast<const T *>(a.v), a.gate, a.beta,
-                       a.S, a.z, static_cast<T *>(a.out), n_heads);
+                       a.S, a.z, static_cast<T *>(a.out), n_heads, a.H);
     return hipGetLastError();
 }
 
@@ -184,6 +201,10 @@ template <class DT>
 static hipError_t decode_variant(const DecodeArgs &a) {
     if (a.variant == LA_NORMALIZED) return decode_dk<LA_NORMALIZED, DT, LA_PHI_ELU1>(a);
     if (a.variant == LA_GATED_DELTA) return decode_dk<LA_GATED_DELTA, DT, LA_PHI_IDENTITY>(a);
+    if (a.variant == LA_RETENTION) {
+        if (a.phi == LA_PHI_ELU1) return decode_dk<LA_RETENTION, DT, LA_PHI_ELU1>(a);
+        return decode_dk<LA_RETENTION, DT, LA_PHI_IDENTITY>(a);
+    }
     if (a.phi == LA_PHI_ELU1) return decode_dk<LA_GATED, DT, LA_PHI_ELU1>(a);
     return decode_dk<LA_GATED, DT, LA_PHI_IDENTITY>(a);
 }

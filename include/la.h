@@ -23,6 +23,16 @@
  *                   o_t = S_t q_t.
  *                   Page "Module 18 Beyond attention", section 18.2; page
  *                   "Linear Attention", gated-delta-rule formulation.
+ *   LA_RETENTION    linear attention with a fixed per-head decay gamma_h and
+ *                   no normalizer (the constant gate):
+ *                   S_t = gamma_h S_{t-1} + v_t phi(k_t)^T,  o_t = S_t phi(q_t).
+ *                   Page "Ch. 11 Linear attention and Hyena", section 11.3
+ *                   (RetNet bullet).
+ *
+ * LA_NORMALIZED optionally takes the same fixed per-head decay, applied to
+ * both accumulators (page "Beyond -- Linear attention and recurrent memory",
+ * section "Fixed decay versus an input-dependent gate"):
+ *   S_t = gamma_h S_{t-1} + v_t phi(k_t)^T,  z_t = gamma_h z_{t-1} + phi(k_t).
  *
  * Every token is "update first, then read": a token attends to itself
  * (page "Beyond -- Linear attention and recurrent memory", section
@@ -63,7 +73,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 typedef enum {
     LA_OK = 0,
@@ -72,7 +82,7 @@ typedef enum {
     LA_EHIP = 3           /* the HIP runtime reported an error at launch */
 } la_status;
 
-typedef enum { LA_NORMALIZED = 0, LA_GATED = 1, LA_GATED_DELTA = 2 } la_variant;
+typedef enum { LA_NORMALIZED = 0, LA_GATED = 1, LA_GATED_DELTA = 2, LA_RETENTION = 3 } la_variant;
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 typedef enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1 } la_phi;
 
@@ -81,8 +91,8 @@ typedef enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1 } la_phi;
  *   variant  la_variant.
  *   dtype    la_dtype of q, k, v, out.
  *   phi      feature map on q and k.  LA_NORMALIZED requires LA_PHI_ELU1 (the
- *            normalizer needs positive features); LA_GATED accepts either;
- *            LA_GATED_DELTA requires LA_PHI_IDENTITY.
+ *            normalizer needs positive features); LA_GATED and LA_RETENTION
+ *            accept either; LA_GATED_DELTA requires LA_PHI_IDENTITY.
  *   B, H     batch size and heads, >= 0.
  *   T        tokens per sequence, >= 0 (ignored by la_decode_step).
  *   d_k      key/query head size; d_v value head size.  Supported:
@@ -127,8 +137,10 @@ size_t la_chunk_fwd_workspace(const la_desc *desc);
  *
  *   q     (B,H,T,d_k) dtype.            k (B,H,T,d_k) dtype.
  *   v     (B,H,T,d_v) dtype.
- *   gate  LA_GATED: gamma (B,H,T,d_k) f32; LA_GATED_DELTA: g (B,H,T) f32;
- *         LA_NORMALIZED: must be NULL.
+ *   gate  LA_GATED: gamma (B,H,T,d_k) f32, 16-byte aligned;
+ *         LA_GATED_DELTA: g (B,H,T) f32;
+ *         LA_NORMALIZED, LA_RETENTION: the fixed decay gamma_h (H,) f32,
+ *         shared by the batch, or NULL for none (gamma_h = 1).
  *   beta  LA_GATED_DELTA: (B,H,T) f32; otherwise must be NULL.
  *   S0    initial state (B,H,d_v,d_k) f32, or NULL for zeros.
  *   z0    LA_NORMALIZED: initial normalizer (B,H,d_k) f32 or NULL for
@@ -183,7 +195,7 @@ la_status la_chunk_fwd_noalloc(const la_desc *desc,
  *
  *   q, k  (B,H,d_k) dtype.   v (B,H,d_v) dtype.
  *   gate  LA_GATED: gamma (B,H,d_k) f32; LA_GATED_DELTA: g (B,H) f32;
- *         LA_NORMALIZED: must be NULL.
+ *         LA_NORMALIZED, LA_RETENTION: gamma_h (H,) f32 or NULL.
  *   beta  LA_GATED_DELTA: (B,H) f32; otherwise must be NULL.
  *   S     (B,H,d_v,d_k) f32, read and overwritten with the new state.
  *   z     LA_NORMALIZED: (B,H,d_k) f32, read and overwritten; otherwise NULL.

@@ -110,7 +110,13 @@ CHUNK_CASES = [
     ("missing_out", D(), {"out": None}, la.LA_EINVAL, "required"),
     ("missing_gate", D(), {"gate": None}, la.LA_EINVAL, "gate"),
     ("missing_beta", D(), {"beta": None}, la.LA_EINVAL, "beta"),
-    ("gate_on_normalized", D(la.LA_NORMALIZED), {"gate": fake(5)}, la.LA_EINVAL, "gate"),
+    ("beta_on_normalized", D(la.LA_NORMALIZED), {"beta": fake(6)}, la.LA_EINVAL, "beta"),
+    ("beta_on_retention", D(la.LA_RETENTION), {"beta": fake(6)}, la.LA_EINVAL, "beta"),
+    ("z0_on_retention", D(la.LA_RETENTION), {"z0": fake(7)}, la.LA_EINVAL, "z"),
+    ("misaligned_head_gate", D(la.LA_NORMALIZED), {"gate": fake(5, 2)}, la.LA_EINVAL, "aligned"),
+    ("head_gate_overlaps_out", D(la.LA_RETENTION), {"gate": fake(3, 64), "ws": fake(9), "ws_bytes": 1 << 24},
+     la.LA_EINVAL, "overlaps"),
+    ("bad_variant_5", D(variant=5), {}, la.LA_EINVAL, "variant"),
     ("beta_on_gated", D(la.LA_GATED), {"beta": fake(6)}, la.LA_EINVAL, "beta"),
     ("z0_on_delta", D(), {"z0": fake(7)}, la.LA_EINVAL, "z"),
     ("z_T_on_gated", D(la.LA_GATED), {"z_T": fake(7)}, la.LA_EINVAL, "z"),
@@ -137,6 +143,8 @@ DECODE_CASES = [
     ("out_overlaps_state", D(), {"out": fake(4, 128)}, la.LA_EINVAL, "overlaps"),
     ("z_on_gated", D(la.LA_GATED), {"z": fake(7)}, la.LA_EINVAL, "z"),
     ("unsupported_dk", D(d_k=8), {}, la.LA_EUNSUPPORTED, "head sizes"),
+    ("z_on_retention", D(la.LA_RETENTION), {"z": fake(7)}, la.LA_EINVAL, "z"),
+    ("misaligned_head_gate", D(la.LA_RETENTION), {"gate": fake(5, 1)}, la.LA_EINVAL, "aligned"),
 ]
 
 
@@ -151,7 +159,7 @@ def test_workspace_query_of_invalid_desc_is_zero(lib):
 
 
 def test_workspace_sizes(lib):
-    # Only the normalized variant uses a workspace: one slot of d_v*d_k + d_k
+    # Only the normalized and retention variants use a workspace: one slot of d_v*d_k + d_k
     # floats per head and segment, when the heads (value blocks of up to 64
     # channels) give fewer workgroups than the 256 compute units (the segment
     # count is bounded by 256 / workgroups and by the 16-token chunks over
@@ -164,6 +172,9 @@ def test_workspace_sizes(lib):
     assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=31)) == 6 * 64 * 4   # one 16-token chunk pair at most
     assert la.la_chunk_fwd_workspace(D(la.LA_GATED, T=2048)) == 0
     assert la.la_chunk_fwd_workspace(D(la.LA_GATED_DELTA, T=2048)) == 0
+    # retention: the same segment slots, no z0 staging
+    assert la.la_chunk_fwd_workspace(D(la.LA_RETENTION, B=4, H=8, T=2048)) == 32 * 8 * slot(64, 64)
+    assert la.la_chunk_fwd_workspace(D(la.LA_RETENTION, B=16, H=16, T=2048)) == 0
 
 
 def test_missing_workspace_is_rejected(lib):

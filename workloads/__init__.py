@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-NORMALIZED, GATED, GATED_DELTA = 0, 1, 2
+NORMALIZED, GATED, GATED_DELTA, RETENTION, KDA = 0, 1, 2, 3, 4
 PHI_IDENTITY, PHI_ELU1 = 0, 1
 
 
@@ -113,7 +113,7 @@ class Workload:
     def phi_kind(self) -> int:
         if self.phi >= 0:
             return self.phi
-        return PHI_IDENTITY if self.variant == GATED_DELTA else PHI_ELU1
+        return PHI_ELU1 if self.variant in (NORMALIZED, GATED) else PHI_IDENTITY
 
 
 WORKLOADS = {
@@ -138,12 +138,15 @@ WORKLOAD_ORDER = list(WORKLOADS)
 
 def chunk_inputs(w: Workload, seed: int | None = None, *, T: int | None = None,
                  B: int | None = None, H: int | None = None,
-                 S0_std: float | None = None, z0: bool = False) -> dict:
+                 S0_std: float | None = None, z0: bool = False, head_decay: bool = False) -> dict:
     """Inputs of one whole-sequence forward call, as HostTensors.
 
     Keys: q, k, v, and as the variant needs: gate, beta; S0 / z0 when an
     initial state is requested (S0_std > 0, z0=True for the normalized
-    variant).  Shapes may be overridden (B, H, T) for smaller test cases.
+    variant).  The retention variant, and the normalized one with
+    head_decay, take a fixed decay per head, gate (H,) = sigmoid(N(gate_mean,
+    1)), drawn in the gate slot.  Shapes may be overridden (B, H, T) for
+    smaller test cases.
     """
     seed = w.seed if seed is None else seed
     B = w.B if B is None else B
@@ -159,10 +162,13 @@ def chunk_inputs(w: Workload, seed: int | None = None, *, T: int | None = None,
     if w.variant == GATED_DELTA:
         k = _unit_rows(k)
     out["q"], out["k"], out["v"] = _store(q, w.dtype), _store(k, w.dtype), _store(v, w.dtype)
-    if w.variant == GATED:
+    if w.variant in (GATED, KDA):
         out["gate"] = _store(_sigmoid(_normal(rng, (B, H, T, dk), 1.0, w.gate_mean)), "f32")
     elif w.variant == GATED_DELTA:
         out["gate"] = _store(_sigmoid(_normal(rng, (B, H, T), 1.0, w.gate_mean)), "f32")
+    elif w.variant == RETENTION or (w.variant == NORMALIZED and head_decay):
+        out["gate"] = _store(_sigmoid(_normal(rng, (H,), 1.0, w.gate_mean)), "f32")
+    if w.variant in (GATED_DELTA, KDA):
         out["beta"] = _store(_sigmoid(_normal(rng, (B, H, T), 1.0, w.beta_mean)), "f32")
     if S0_std > 0:
         out["S0"] = _store(_normal(rng, (B, H, dv, dk), S0_std), "f32")
@@ -203,15 +209,26 @@ def decode_step_inputs(w: Workload, step: int, seed: int | None = None, *,
     k = _normal(rng, (B, H, dk), w.qkv_scale)
     v = _normal(rng, (B, H, dv), w.qkv_scale)
     out = {}
-    if w.variant == GATED_DELTA:
+    if w.variant in (GATED_DELTA, KDA):
         k = _unit_rows(k)
     out["q"], out["k"], out["v"] = _store(q, w.dtype), _store(k, w.dtype), _store(v, w.dtype)
-    if w.variant == GATED:
+    if w.variant in (GATED, KDA):
         out["gate"] = _store(_sigmoid(_normal(rng, (B, H, dk), 1.0, w.gate_mean)), "f32")
     elif w.variant == GATED_DELTA:
         out["gate"] = _store(_sigmoid(_normal(rng, (B, H), 1.0, w.gate_mean)), "f32")
+    if w.variant in (GATED_DELTA, KDA):
         out["beta"] = _store(_sigmoid(_normal(rng, (B, H), 1.0, w.beta_mean)), "f32")
     return out
+
+
+def head_decays(w: Workload, seed: int | None = None, *, H=None) -> HostTensor:
+    """A fixed decay per head, (H,) = sigmoid(N(gate_mean, 1)) f32, for decode
+    sequences of the retention and (decayed) normalized variants: the same
+    every step, drawn from default_rng([seed, 2**30 + 2])."""
+    seed = w.seed if seed is None else seed
+    H = w.H if H is None else H
+    rng = np.random.default_rng([seed, (1 << 30) + 2])
+    return _store(_sigmoid(_normal(rng, (H,), 1.0, w.gate_mean)), "f32")
 
 
 def variant_workload(variant: int, dtype: str, d_k: int, d_v: int, chunk: int = 64,
@@ -221,6 +238,6 @@ def variant_workload(variant: int, dtype: str, d_k: int, d_v: int, chunk: int = 
     gate pre-activation mean defaults to the specified workloads' (a lower
     mean gives stronger decay)."""
     if gate_mean is None:
-        gate_mean = {NORMALIZED: 0.0, GATED: 3.0, GATED_DELTA: 4.0}[variant]
+        gate_mean = {NORMALIZED: 3.0, GATED: 3.0, GATED_DELTA: 4.0, RETENTION: 3.0, KDA: 3.0}[variant]
     return Workload("custom", variant, dtype, 1, 1, 1, d_k, d_v, chunk,
                     max(d_k, 1) ** -0.5, gate_mean=gate_mean, S0_std=S0_std, seed=seed, phi=phi)
