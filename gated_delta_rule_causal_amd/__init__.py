@@ -19,7 +19,7 @@ from ._lib import (LA_BF16, LA_EHIP, LA_EINVAL, LA_EUNSUPPORTED, LA_F32, LA_GATE
                    LA_GATED_DELTA, LA_NORMALIZED, LA_OK, LA_PHI_ELU1, LA_PHI_IDENTITY,
                    LA_RETENTION, LaDesc, LaError, check, load)
 
-__all__ = ["la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step", "la_chunk_fwd_workspace", "la_status_str",
+__all__ = ["la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step", "la_verify", "la_commit", "la_chunk_fwd_workspace", "la_status_str",
            "la_last_error", "la_abi_version", "make_desc", "LaDesc", "LaError",
            "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_RETENTION", "LA_F32", "LA_BF16",
            "LA_PHI_IDENTITY", "LA_PHI_ELU1"]
@@ -215,3 +215,46 @@ def la_decode_step(q, k, v, S, *, variant, gate=None, beta=None, z=None, phi=Non
     check(lib.la_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                              _ptr(beta), _ptr(S), _ptr(z), _ptr(out), _stream(stream)))
     return out
+
+
+def la_verify(q, k, v, S, *, variant, gate=None, beta=None, z=None, phi=None, out=None, stream=None):
+    """Outputs of T draft tokens from the checkpoint S (and z), which is left
+    untouched (C: ``la_verify``).  q, k (B,H,T,d_k), v (B,H,T,d_v); gate and
+    beta per token as in la_chunk_fwd.  Returns out (B,H,T,d_v)."""
+    lib = load()
+    dt, d_k, d_v = _check_qkv(q, k, v, "BHT")
+    B, H, T = q.shape[:3]
+    dev, f32 = q.device, torch.float32
+    if S is None:
+        raise ValueError("S: the checkpoint is required")
+    _check("gate", gate, _gate_shape(variant, (B, H, T), d_k), f32, dev)
+    _check("beta", beta, (B, H, T), f32, dev)
+    _check("S", S, (B, H, d_v, d_k), f32, dev)
+    _check("z", z, (B, H, d_k), f32, dev)
+    _check("out", out, (B, H, T, d_v), q.dtype, dev)
+    _require_gpu(q)
+    desc = make_desc(variant, dt, B, H, T, d_k, d_v, 0, phi)
+    if out is None:
+        out = torch.empty((B, H, T, d_v), dtype=q.dtype, device=dev)
+    check(lib.la_verify(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(S),
+                        _ptr(z), _ptr(out), _stream(stream)))
+    return out
+
+
+def la_commit(k, v, S, accepted, *, variant, gate=None, beta=None, z=None, phi=None, stream=None):
+    """Apply the first accepted[b] of T draft tokens to S (and z) in place
+    (C: ``la_commit``).  k (B,H,T,d_k), v (B,H,T,d_v); accepted (B,) int32 on
+    the device."""
+    lib = load()
+    dt, d_k, d_v = _check_qkv(k, k, v, "BHT")
+    B, H, T = k.shape[:3]
+    dev, f32 = k.device, torch.float32
+    _check("gate", gate, _gate_shape(variant, (B, H, T), d_k), f32, dev)
+    _check("beta", beta, (B, H, T), f32, dev)
+    _check("S", S, (B, H, d_v, d_k), f32, dev)
+    _check("z", z, (B, H, d_k), f32, dev)
+    _check("accepted", accepted, (B,), torch.int32, dev)
+    _require_gpu(k)
+    desc = make_desc(variant, dt, B, H, T, d_k, d_v, 0, phi)
+    check(lib.la_commit(ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta), _ptr(accepted), _ptr(S),
+                        _ptr(z), _stream(stream)))

@@ -22,7 +22,7 @@ LA_PHI_IDENTITY, LA_PHI_ELU1 = 0, 1
 LA_ABI_VERSION = 2
 
 EXPORTED = ("la_chunk_fwd_workspace", "la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step",
-            "la_status_str", "la_last_error", "la_abi_version")
+            "la_verify", "la_commit", "la_status_str", "la_last_error", "la_abi_version")
 LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -54,6 +54,10 @@ def load(path: str = LIB_PATH):
     lib.la_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
     lib.la_decode_step.restype = ctypes.c_int
+    lib.la_verify.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, vp]
+    lib.la_verify.restype = ctypes.c_int
+    lib.la_commit.argtypes = [dp, vp, vp, fp, fp, vp, fp, fp, vp]
+    lib.la_commit.restype = ctypes.c_int
     lib.la_status_str.argtypes = [ctypes.c_int]
     lib.la_status_str.restype = ctypes.c_char_p
     lib.la_last_error.argtypes = []

@@ -297,4 +297,82 @@ la_status la_decode_step(const la_desc *d, const void *q, const void *k, const v
     return LA_OK;
 }
 
+// Shared checks of la_verify and la_commit: T draft tokens per sequence,
+// tensors laid out as the chunked forward's with T tokens; `commit` calls
+// take `accepted` and write S (and z) in place, verify calls write `out`.
+static la_status multi_token(const la_desc *d, const void *q, const void *k, const void *v, const float *gate,
+                             const float *beta, float *S, float *z, void *out, const int32_t *accepted, void *stream,
+                             bool commit) {
+    g_last_error[0] = '\0';
+    la_status st = check_desc(d, false);
+    if (st != LA_OK) return st;
+    if (d->T < 0) return fail(LA_EINVAL, "T=%d must be >= 0", d->T);
+    const size_t heads = static_cast<size_t>(d->B) * d->H;
+    const size_t tok = heads * static_cast<size_t>(d->T);
+    const bool need_data = tok > 0;
+    st = check_role(d, gate, beta, z, z, need_data);
+    if (st != LA_OK) return st;
+    if (need_data && (!k || !v || !S)) return fail(LA_EINVAL, "k, v and S are required");
+    if (need_data && !commit && (!q || !out)) return fail(LA_EINVAL, "q and out are required to verify");
+    if (need_data && commit && !accepted) return fail(LA_EINVAL, "accepted is required to commit");
+    if (need_data && d->variant == LA_NORMALIZED && !z) return fail(LA_EINVAL, "z is required for LA_NORMALIZED");
+    if (commit && out) return fail(LA_EINVAL, "out must be NULL for la_commit");
+    if (!commit && accepted) return fail(LA_EINVAL, "accepted must be NULL for la_verify");
+
+    const size_t esz = d->dtype == LA_BF16 ? 2 : 4;
+    const void *ptrs[] = {q, k, v, gate, beta, S, z, out, accepted};
+    const char *names[] = {"q", "k", "v", "gate", "beta", "S", "z", "out", "accepted"};
+    for (int i = 0; i < 9; ++i) {
+        uintptr_t al = i == 3 ? gate_align(d->variant) : (i == 4 || i == 8) ? 4 : 16;
+        if (i == 7) al = esz;   // one output element per state row
+        if (misaligned(ptrs[i], al)) return fail(LA_EINVAL, "%s is not %d-byte aligned", names[i], (int)al);
+    }
+    const size_t dk = d->d_k, dv = d->d_v;
+    const Range r_q = range("q", q, tok * dk * esz), r_k = range("k", k, tok * dk * esz);
+    const Range r_v = range("v", v, tok * dv * esz);
+    const Range r_g = range("gate", gate, gate_bytes(d, heads, static_cast<size_t>(d->T)));
+    const Range r_b = range("beta", beta, tok * 4);
+    const Range r_a = range("accepted", accepted, static_cast<size_t>(d->B) * 4);
+    const Range r_s = range("S", S, heads * dv * dk * 4), r_z = range("z", z, heads * dk * 4);
+    const Range r_o = range("out", out, tok * dv * esz);
+    const Range inputs[] = {r_q, r_k, r_v, r_g, r_b, r_a};
+    // verify only reads the state; commit writes it; out is written by verify
+    const Range written[] = {r_o, commit ? r_s : Range{"S", 0, 0}, commit ? r_z : Range{"z", 0, 0}};
+    const Range read_state[] = {r_s, r_z};
+    for (const Range &o : written) {
+        for (const Range &i : inputs)
+            if (overlaps(o, i)) return fail(LA_EINVAL, "%s overlaps %s", o.name, i.name);
+        for (const Range &o2 : written)
+            if (&o2 != &o && overlaps(o, o2)) return fail(LA_EINVAL, "%s overlaps %s", o.name, o2.name);
+        if (!commit)
+            for (const Range &s2 : read_state)
+                if (overlaps(o, s2)) return fail(LA_EINVAL, "%s overlaps %s", o.name, s2.name);
+    }
+    if (overlaps(r_s, r_z)) return fail(LA_EINVAL, "S overlaps z");
+    if (!need_data) return LA_OK;
+
+    la::DecodeArgs a = {};
+    a.variant = d->variant; a.dtype = d->dtype; a.phi = d->phi;
+    a.B = d->B; a.H = d->H; a.d_k = d->d_k; a.d_v = d->d_v;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta; a.S = S; a.z = z; a.out = out;
+    a.stream = static_cast<hipStream_t>(stream);
+    a.mode = commit ? la::DECODE_COMMIT : la::DECODE_VERIFY;
+    a.T = d->T;
+    a.accepted = accepted;
+    hipError_t e = la::launch_decode(a);
+    if (e != hipSuccess) return fail(LA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return LA_OK;
+}
+
+la_status la_verify(const la_desc *d, const void *q, const void *k, const void *v, const float *gate,
+                    const float *beta, const float *S, const float *z, void *out, void *stream) {
+    return multi_token(d, q, k, v, gate, beta, const_cast<float *>(S), const_cast<float *>(z), out, nullptr, stream,
+                       false);
+}
+
+la_status la_commit(const la_desc *d, const void *k, const void *v, const float *gate, const float *beta,
+                    const int32_t *accepted, float *S, float *z, void *stream) {
+    return multi_token(d, nullptr, k, v, gate, beta, S, z, nullptr, accepted, stream, true);
+}
+
 }  // extern "C"

@@ -158,6 +158,166 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
 }
 
+// ------------------------------------------------------------------ multi-token
+// Speculative decoding by checkpoint plus input replay (page "Beyond --
+// Linear attention and recurrent memory", section "What we don't cover",
+// recurrent-state commit and rollback): a fixed state has no token rows to
+// truncate, so draft tokens are verified from the checkpointed state without
+// changing it, and the accepted prefix is then replayed into it.
+//   COMMIT = false (verify): T tokens from S (and z), outputs of every token,
+//            S and z untouched;
+//   COMMIT = true (commit):  the first accepted[b] tokens of sequence b
+//            (clamped to [0, T]) applied to S (and z) in place, no outputs.
+// The state rows stay in registers for all the tokens, so either call reads
+// the state once (commit writes it once); the per-token arithmetic is the
+// step of decode_kernel above.  The normalizer z is kept per lane in
+// registers (every row group of a head updates its own copy identically) and
+// written after a barrier, once every group has read it.
+template <int VAR, class DT, int DK, int DV, int PHI, bool COMMIT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(
+    const typename DT::storage *__restrict__ q, const typename DT::storage *__restrict__ k,
+    const typename DT::storage *__restrict__ v, const float *__restrict__ gate,
+    const float *__restrict__ beta, float *__restrict__ S, float *__restrict__ z,
+    typename DT::storage *__restrict__ out, const int32_t *__restrict__ accepted, int64_t n_heads, int H, int T) {
+    constexpr int G = DK / 8;
+    constexpr int GROUPS = kDecodeThreads / G;
+    constexpr int HPW = GROUPS >= DV ? GROUPS / DV : 1;
+    constexpr int GPH = GROUPS / HPW;
+    constexpr int RPG = DV / GPH;
+    static_assert(DK % 8 == 0 && G <= 64 && RPG >= 1 && RPG * GPH == DV, "decode tiling");
+
+    const int tid = threadIdx.x;
+    const int grp = tid / G;
+    const int c0 = (tid % G) * 8;
+    const int64_t head = static_cast<int64_t>(blockIdx.x) * HPW + grp / GPH;
+    const int row0 = grp % GPH;
+    const bool active = head < n_heads;
+    const int64_t h = active ? head : 0;
+    // tokens to apply: all T to verify; the sequence's accepted count to commit
+    const int n = COMMIT ? min(max(accepted[h / H], 0), T) : T;
+
+    float s[RPG][8];
+#pragma unroll
+    for (int r = 0; r < RPG; ++r) load8(S + (h * DV + row0 + r * GPH) * DK + c0, s[r]);
+    float zz[8];
+    if constexpr (VAR == LA_NORMALIZED) load8(z + h * DK + c0, zz);
+    const float gh = (VAR == LA_NORMALIZED || VAR == LA_RETENTION) && gate ? gate[h % H] : 1.f;
+
+    for (int t = 0; t < n; ++t) {
+        const int64_t tok = h * T + t;
+        float kk[8], qq[8], vv[RPG];
+        load8(k + tok * DK + c0, kk);
+        if constexpr (!COMMIT) load8(q + tok * DK + c0, qq);
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) vv[r] = load1(v + tok * DV + row0 + r * GPH);
+
+        if constexpr (VAR == LA_GATED_DELTA) {
+            const float g = gate[tok], b = beta[tok];
+            float kq = 0.f;
+            if constexpr (!COMMIT) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) kq += kk[c] * qq[c];
+                kq = group_sum<G>(kq);
+            }
+#pragma unroll
+            for (int r = 0; r < RPG; ++r) {
+                float p = 0.f, rq = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    p += s[r][c] * kk[c];
+                    if constexpr (!COMMIT) rq += s[r][c] * qq[c];
+                }
+                p = group_sum<G>(p);
+                if constexpr (!COMMIT) rq = group_sum<G>(rq);
+                const float u = b * (vv[r] - g * p);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) s[r][c] = g * s[r][c] + u * kk[c];
+                vv[r] = g * rq + u * kq;
+            }
+        } else {
+            float fk[8], fq[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                fk[c] = apply_phi<PHI>(kk[c]);
+                fq[c] = COMMIT ? 0.f : apply_phi<PHI>(qq[c]);
+            }
+            float kq = 0.f;
+            if constexpr (!COMMIT) {
+#pragma unroll
+                for (int c = 0; c < 8; ++c) kq += fk[c] * fq[c];
+                kq = group_sum<G>(kq);
+            }
+            if constexpr (VAR == LA_GATED) {
+                float gm[8];
+                load8(gate + tok * DK + c0, gm);
+#pragma unroll
+                for (int r = 0; r < RPG; ++r) {
+                    float rq = 0.f;
+                    if constexpr (!COMMIT) {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) rq += s[r][c] * gm[c] * fq[c];
+                        rq = group_sum<G>(rq);
+                    }
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) s[r][c] = s[r][c] * gm[c] + vv[r] * fk[c];
+                    vv[r] = rq + vv[r] * kq;
+                }
+            } else {
+                float inv_den = 1.f;
+                if constexpr (VAR == LA_NORMALIZED && !COMMIT) {
+                    float zq = 0.f;
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) zq += zz[c] * fq[c];
+                    zq = group_sum<G>(zq);
+                    inv_den = 1.f / (gh * zq + kq);
+                }
+#pragma unroll
+                for (int r = 0; r < RPG; ++r) {
+                    float rq = 0.f;
+                    if constexpr (!COMMIT) {
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) rq += s[r][c] * fq[c];
+                        rq = group_sum<G>(rq);
+                    }
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) s[r][c] = gh * s[r][c] + vv[r] * fk[c];
+                    vv[r] = (gh * rq + vv[r] * kq) * inv_den;
+                }
+                if constexpr (VAR == LA_NORMALIZED) {
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) zz[c] = gh * zz[c] + fk[c];
+                }
+            }
+        }
+        if constexpr (!COMMIT) {
+            if (active && c0 == 0) {
+#pragma unroll
+                for (int r = 0; r < RPG; ++r) store1(out + tok * DV + row0 + r * GPH, vv[r]);
+            }
+        }
+    }
+
+    if constexpr (COMMIT) {
+        // every group of the head has read z (at the start); only then may row
+        // 0's group overwrite it
+        if constexpr (VAR == LA_NORMALIZED) __syncthreads();
+        if (!active || n == 0) return;
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) {
+            f32x4_t *sp = reinterpret_cast<f32x4_t *>(S + (h * DV + row0 + r * GPH) * DK + c0);
+            __builtin_nontemporal_store(f32x4_t{s[r][0], s[r][1], s[r][2], s[r][3]}, sp);
+            __builtin_nontemporal_store(f32x4_t{s[r][4], s[r][5], s[r][6], s[r][7]}, sp + 1);
+        }
+        if constexpr (VAR == LA_NORMALIZED) {
+            if (row0 == 0) {
+                float4 *zp = reinterpret_cast<float4 *>(z + h * DK + c0);
+                zp[0] = make_float4(zz[0], zz[1], zz[2], zz[3]);
+                zp[1] = make_float4(zz[4], zz[5], zz[6], zz[7]);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------ dispatch
 
 template <int VAR, class DT, int DK, int DV, int PHI>
@@ -168,10 +328,18 @@ static hipError_t launch_decode_t(const DecodeArgs &a) {
     const int64_t n_heads = static_cast<int64_t>(a.B) * a.H;
     const int64_t blocks = (n_heads + HPW - 1) / HPW;
     typedef typename DT::storage T;
-    hipLaunchKernelGGL((decode_kernel<VAR, DT, DK, DV, PHI>), dim3(static_cast<uint32_t>(blocks)),
-                       dim3(kDecodeThreads), 0, a.stream, static_cast<const T *>(a.q),
-                       static_cast<const T *>(a.k), static_cast<const T *>(a.v), a.gate, a.beta,
-                       a.S, a.z, static_cast<T *>(a.out), n_heads, a.H);
+    const dim3 grid(static_cast<uint32_t>(blocks)), block(kDecodeThreads);
+    const T *q = static_cast<const T *>(a.q), *k = static_cast<const T *>(a.k), *v = static_cast<const T *>(a.v);
+    T *out = static_cast<T *>(a.out);
+    if (a.mode == DECODE_STEP)
+        hipLaunchKernelGGL((decode_kernel<VAR, DT, DK, DV, PHI>), grid, block, 0, a.stream, q, k, v, a.gate, a.beta,
+                           a.S, a.z, out, n_heads, a.H);
+    else if (a.mode == DECODE_VERIFY)
+        hipLaunchKernelGGL((decode_multi_kernel<VAR, DT, DK, DV, PHI, false>), grid, block, 0, a.stream, q, k, v,
+                           a.gate, a.beta, a.S, a.z, out, a.accepted, n_heads, a.H, a.T);
+    else
+        hipLaunchKernelGGL((decode_multi_kernel<VAR, DT, DK, DV, PHI, true>), grid, block, 0, a.stream, q, k, v,
+                           a.gate, a.beta, a.S, a.z, out, a.accepted, n_heads, a.H, a.T);
     return hipGetLastError();
 }
 

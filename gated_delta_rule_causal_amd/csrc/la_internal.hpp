@@ -9,6 +9,8 @@
 
 namespace la {
 
+enum DecodeMode { DECODE_STEP = 0, DECODE_VERIFY = 1, DECODE_COMMIT = 2 };
+
 struct DecodeArgs {
     int variant, dtype, phi;
     int B, H, d_k, d_v;
@@ -17,6 +19,9 @@ struct DecodeArgs {
     float *S, *z;
     void *out;
     hipStream_t stream;
+    int mode = DECODE_STEP;
+    int T = 1;                          // tokens per sequence (verify / commit)
+    const int32_t *accepted = nullptr;  // commit: tokens kept per sequence (B,)
 };
 
 struct ChunkArgs {

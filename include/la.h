@@ -207,6 +207,41 @@ la_status la_decode_step(const la_desc *desc,
                          float *S, float *z, void *out,
                          void *stream);
 
+/*
+ * Speculative decoding by checkpoint plus input replay (page "Beyond --
+ * Linear attention and recurrent memory", section "What we don't cover":
+ * a fixed state has no token rows to truncate after rejected drafts).
+ *
+ * la_verify runs T draft tokens per sequence (desc->T) from the checkpointed
+ * state S (and z) and writes the output of every token, leaving S and z
+ * untouched: the same outputs as T consecutive la_decode_step calls.
+ *   q, k  (B,H,T,d_k) dtype.   v (B,H,T,d_v) dtype.
+ *   gate  LA_GATED: (B,H,T,d_k) f32; LA_GATED_DELTA: (B,H,T) f32;
+ *         LA_NORMALIZED, LA_RETENTION: gamma_h (H,) f32 or NULL.
+ *   beta  LA_GATED_DELTA: (B,H,T) f32; otherwise NULL.
+ *   S, z  the checkpoint, (B,H,d_v,d_k) and (LA_NORMALIZED) (B,H,d_k) f32,
+ *         read only.
+ *   out   (B,H,T,d_v) dtype, written; overlaps nothing else.
+ *
+ * la_commit then applies the first accepted[b] tokens of each sequence b to
+ * S (and z) in place, replaying the same inputs (q is not needed): the state
+ * that accepted[b] la_decode_step calls would have left.  accepted is (B,)
+ * int32 in device memory; values are clamped to [0, T] (0 leaves the
+ * sequence's state as it is).  Both calls read the state once; la_commit
+ * writes it once.  Argument checks and errors as la_decode_step.
+ */
+la_status la_verify(const la_desc *desc,
+                    const void *q, const void *k, const void *v,
+                    const float *gate, const float *beta,
+                    const float *S, const float *z, void *out,
+                    void *stream);
+la_status la_commit(const la_desc *desc,
+                    const void *k, const void *v,
+                    const float *gate, const float *beta,
+                    const int32_t *accepted,
+                    float *S, float *z,
+                    void *stream);
+
 /* Static description of a status code. */
 const char *la_status_str(la_status status);
 

@@ -290,3 +290,43 @@ def test_noalloc_header_size_matches_binding():
     text = open(HEADER).read()
     m = re.search(r"#define LA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == _lib.LA_NOALLOC_SCRATCH_BYTES
+
+
+def call_verify(lib, desc, **kw):
+    args = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(5), beta=fake(6), S=fake(4), z=None, out=fake(3))
+    args.update(kw)
+    return lib.la_verify(ctypes.byref(desc), args["q"], args["k"], args["v"], args["gate"], args["beta"],
+                         args["S"], args["z"], args["out"], None)
+
+
+def call_commit(lib, desc, **kw):
+    args = dict(k=fake(1), v=fake(2), gate=fake(5), beta=fake(6), accepted=fake(8), S=fake(4), z=None)
+    args.update(kw)
+    return lib.la_commit(ctypes.byref(desc), args["k"], args["v"], args["gate"], args["beta"], args["accepted"],
+                         args["S"], args["z"], None)
+
+
+MULTI_CASES = [
+    ("verify", "missing_out", D(T=4), {"out": None}, "q and out"),
+    ("verify", "missing_q", D(T=4), {"q": None}, "q and out"),
+    ("verify", "out_overlaps_state", D(T=4), {"out": fake(4, 256)}, "overlaps"),
+    ("verify", "normalized_needs_z", D(la.LA_NORMALIZED, T=4), {"gate": None, "beta": None}, "z is required"),
+    ("verify", "negative_T", D(T=-1), {}, "T="),
+    ("commit", "missing_accepted", D(T=4), {"accepted": None}, "accepted"),
+    ("commit", "misaligned_accepted", D(T=4), {"accepted": fake(8, 2)}, "aligned"),
+    ("commit", "state_overlaps_k", D(T=4), {"S": fake(1, 64)}, "overlaps"),
+    ("commit", "accepted_overlaps_state", D(T=4), {"accepted": fake(4, 16)}, "overlaps"),
+    ("commit", "missing_beta", D(T=4), {"beta": None}, "beta"),
+]
+
+
+@pytest.mark.parametrize("which,name,desc,kw,msg", MULTI_CASES, ids=[c[0] + "-" + c[1] for c in MULTI_CASES])
+def test_verify_commit_reject(lib, which, name, desc, kw, msg):
+    call = call_verify if which == "verify" else call_commit
+    assert call(lib, desc, **kw) != la.LA_OK
+    assert msg in la.la_last_error()
+
+
+def test_verify_commit_empty_is_a_no_op(lib):
+    assert call_verify(lib, D(T=0), q=None, k=None, v=None, out=None, S=None, gate=None, beta=None) == la.LA_OK
+    assert call_commit(lib, D(B=0, T=4), k=None, v=None, S=None, gate=None, beta=None, accepted=None) == la.LA_OK
