@@ -17,11 +17,11 @@ import torch
 
 from ._lib import (LA_BF16, LA_EHIP, LA_EINVAL, LA_EUNSUPPORTED, LA_F32, LA_GATED,  # noqa: F401
                    LA_GATED_DELTA, LA_NORMALIZED, LA_OK, LA_PHI_ELU1, LA_PHI_IDENTITY,
-                   LA_RETENTION, LaDesc, LaError, check, load)
+                   LA_RETENTION, LA_KDA, LaDesc, LaError, check, load)
 
 __all__ = ["la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step", "la_verify", "la_commit", "la_chunk_fwd_workspace", "la_status_str",
            "la_last_error", "la_abi_version", "make_desc", "LaDesc", "LaError",
-           "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_RETENTION", "LA_F32", "LA_BF16",
+           "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_RETENTION", "LA_KDA", "LA_F32", "LA_BF16",
            "LA_PHI_IDENTITY", "LA_PHI_ELU1"]
 
 _DTYPES = {torch.float32: LA_F32, torch.bfloat16: LA_BF16}

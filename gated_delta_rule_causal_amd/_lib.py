@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libla.so")
 
 LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP = 0, 1, 2, 3
-LA_NORMALIZED, LA_GATED, LA_GATED_DELTA, LA_RETENTION = 0, 1, 2, 3
+LA_NORMALIZED, LA_GATED, LA_GATED_DELTA, LA_RETENTION, LA_KDA = 0, 1, 2, 3, 4
 LA_F32, LA_BF16 = 0, 1
 LA_PHI_IDENTITY, LA_PHI_ELU1 = 0, 1
 LA_ABI_VERSION = 2

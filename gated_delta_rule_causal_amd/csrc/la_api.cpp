@@ -52,14 +52,14 @@ bool misaligned(const void *p, uintptr_t a) { return p && (reinterpret_cast<uint
 // Checks shared by both entry points.  n_tok = tokens per head that the call reads.
 la_status check_desc(const la_desc *d, bool chunked) {
     if (!d) return fail(LA_EINVAL, "desc is NULL");
-    if (d->variant < LA_NORMALIZED || d->variant > LA_RETENTION)
+    if (d->variant < LA_NORMALIZED || d->variant > LA_KDA)
         return fail(LA_EINVAL, "variant %d is not a la_variant", d->variant);
     if (d->dtype != LA_F32 && d->dtype != LA_BF16) return fail(LA_EINVAL, "dtype %d is not a la_dtype", d->dtype);
     if (d->phi != LA_PHI_IDENTITY && d->phi != LA_PHI_ELU1) return fail(LA_EINVAL, "phi %d is not a la_phi", d->phi);
     if (d->variant == LA_NORMALIZED && d->phi != LA_PHI_ELU1)
         return fail(LA_EINVAL, "LA_NORMALIZED needs LA_PHI_ELU1 (the normalizer needs positive features)");
-    if (d->variant == LA_GATED_DELTA && d->phi != LA_PHI_IDENTITY)
-        return fail(LA_EINVAL, "LA_GATED_DELTA needs LA_PHI_IDENTITY (keys are unit vectors)");
+    if ((d->variant == LA_GATED_DELTA || d->variant == LA_KDA) && d->phi != LA_PHI_IDENTITY)
+        return fail(LA_EINVAL, "the delta rules need LA_PHI_IDENTITY (keys are unit vectors)");
     if (d->B < 0 || d->H < 0) return fail(LA_EINVAL, "B=%d, H=%d must be >= 0", d->B, d->H);
     if (chunked && d->T < 0) return fail(LA_EINVAL, "T=%d must be >= 0", d->T);
     if (d->d_k <= 0 || d->d_v <= 0) return fail(LA_EINVAL, "d_k=%d, d_v=%d must be > 0", d->d_k, d->d_v);
@@ -85,7 +85,7 @@ GateKind gate_kind(int variant) {
     if (variant == LA_GATED_DELTA) return GATE_PER_TOKEN;
     return GATE_PER_CHANNEL;
 }
-bool has_beta(int variant) { return variant == LA_GATED_DELTA; }
+bool has_beta(int variant) { return variant == LA_GATED_DELTA || variant == LA_KDA; }
 
 la_status check_role(const la_desc *d, const float *gate, const float *beta, const float *z_in,
                      const float *z_out, bool need_data) {
@@ -94,7 +94,7 @@ la_status check_role(const la_desc *d, const float *gate, const float *beta, con
     if (gate_kind(d->variant) != GATE_PER_HEAD && need_data && !gate)
         return fail(LA_EINVAL, "gate is required for this variant");
     if (!has_beta(d->variant) && beta) return fail(LA_EINVAL, "beta must be NULL for this variant");
-    if (has_beta(d->variant) && need_data && !beta) return fail(LA_EINVAL, "beta is required for LA_GATED_DELTA");
+    if (has_beta(d->variant) && need_data && !beta) return fail(LA_EINVAL, "beta is required for the delta rules");
     return LA_OK;
 }
 

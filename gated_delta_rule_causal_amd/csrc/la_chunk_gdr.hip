@@ -809,7 +809,9 @@ static hipError_t gdr_dk(const ChunkArgs &a) {
 hipError_t launch_chunk_linear(const ChunkArgs &a);
 hipError_t launch_chunk_gdr(const ChunkArgs &a);
 hipError_t launch_chunk(const ChunkArgs &a) {
-    return a.variant == LA_GATED_DELTA ? launch_chunk_gdr(a) : launch_chunk_linear(a);
+    if (a.variant == LA_GATED_DELTA) return launch_chunk_gdr(a);
+    if (a.variant == LA_KDA) return launch_chunk_kda(a);
+    return launch_chunk_linear(a);
 }
 
 hipError_t launch_chunk_gdr(const ChunkArgs &a) {

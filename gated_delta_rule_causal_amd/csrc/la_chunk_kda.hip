@@ -1,0 +1,446 @@
+// la_chunk_kda.hip -- chunked forward of the delta rule with a per-key-channel
+// (diagonal) decay, the finer-grained gate of page "Beyond -- Linear attention
+// and recurrent memory", section "From fixed decay to KDA's gated delta write"
+// (gfx950).
+//
+// Recurrence (decay first, as page "Module 18 Beyond attention", 18.2 orders
+// the scalar-gate rule), d_v x d_k state:
+//   S_t = S_{t-1} diag(alpha_t) + u_t k_t^T,
+//   u_t = beta_t (v_t - S_{t-1} diag(alpha_t) k_t),   o_t = S_t q_t.
+// Within a chunk entering with S0, let b_tc be the chunk-local cumulative sum
+// of log alpha_c and D_tjc = prod_{j < i <= t} alpha_ic = e^{b_tc - b_jc}.
+// Unrolling gives S_t = S0 diag(e^{b_t}) + sum_{j<=t} u_j (k_j o D_tj)^T, and
+// substituting it into u_t gives one unit-lower-triangular system
+//   (I + A) U = diag(beta) V - diag(beta) (K o e^b) S0^T,
+//   A_tj = beta_t sum_c k_tc k_jc D_tjc  (j < t),
+// so that with W = (I + A)^{-1} diag(beta) (K o e^b) and
+// U' = (I + A)^{-1} diag(beta) V (neither depends on S0):
+//   U   = U' - W S0^T
+//   O   = (Q o e^b) S0^T + P U,   P_tj = sum_c q_tc k_jc D_tjc  (j <= t)
+//   S_C = S0 diag(e^{b_n}) + U^T (K o e^{b_n - b})   (n tokens in the chunk).
+// Every factor used is at most 1.
+//
+// Two kernels:
+//   kda_prep_kernel  one workgroup per chunk of one head, all chunks at once:
+//     the scores (off the 16-token block diagonal through a reference token
+//     between query and key, so both operand factors are at most 1; on it
+//     exactly, from running products of the gates), the triangular solve for
+//     W and U' (one column per thread, forward substitution), and the scaled
+//     tiles, written to a workspace record per chunk;
+//   kda_chain_kernel one workgroup per (head, block of value channels), the
+//     chunks in order: the state-dependent products only, the state slice of
+//     each wave held in matrix-core accumulators for the whole sequence.
+#include "la_chunk_common.hpp"
+
+namespace la {
+
+// Workspace record of one chunk of one head (element type Op of the matrix
+// cores: float32 for float32 inputs, bfloat16 otherwise).
+template <class Op, int DK, int DV, int C>
+struct KdaRec {
+    static constexpr size_t QT = 0;                                 // Q o e^b,            C x DK
+    static constexpr size_t WT = QT + C * DK * sizeof(Op);          // W,                  C x DK
+    static constexpr size_t KT = WT + C * DK * sizeof(Op);          // K o e^{b_n - b},    C x DK
+    static constexpr size_t UP = KT + C * DK * sizeof(Op);          // U',                 C x DV
+    static constexpr size_t PT = UP + C * DV * sizeof(Op);          // P (blocks J <= I),  C x C
+    static constexpr size_t EC = PT + C * C * sizeof(Op);           // e^{b_n},            DK float32
+    static constexpr size_t BYTES = (EC + DK * 4 + 255) / 256 * 256;
+};
+
+constexpr int kKdaPrepThreads = 256;
+
+// ------------------------------------------------------------------ prep
+template <class DT, int DK, int DV, int C>
+__global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkParams p, unsigned char *ws) {
+    typedef typename DT::storage IO;
+    typedef typename OpOf<DT>::type Op;
+    typedef Group<Op> Gp;
+    typedef KdaRec<Op, DK, DV, C> R;
+    constexpr int NTHR = kKdaPrepThreads;
+    constexpr int NB = C / 16;
+    constexpr int LDQ = DK + 16 / (int)sizeof(Op);   // raw q, k rows
+    constexpr int LDB = DK + 1;                       // cumulative log2 gates
+    constexpr int LDA = C + 4;                        // A and P, float32
+    static_assert(DK + DV <= NTHR && C <= 64 && C % 16 == 0 && DK % 16 == 0, "prep tiling");
+
+    __shared__ __align__(16) Op sQ[C * LDQ];
+    __shared__ __align__(16) Op sK[C * LDQ];
+    __shared__ __align__(16) float sB[C * LDB];
+    __shared__ __align__(16) float sA[C * LDA];      // A (strict lower), float32
+    __shared__ __align__(16) float sP[C * LDA];      // P (lower), float32
+    __shared__ float sBeta[C];
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int nchunks = (p.T + C - 1) / C;
+    const int bh = blockIdx.x / nchunks, c = blockIdx.x % nchunks;
+    const int t0 = c * C, n = min(C, p.T - t0);
+    const size_t tok0 = static_cast<size_t>(bh) * p.T + t0;
+    const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
+    const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
+    const IO *vh = static_cast<const IO *>(p.v) + tok0 * DV;
+    const float *ah = p.gate + tok0 * DK;             // alpha, per token and key channel
+    unsigned char *rec = ws + (static_cast<size_t>(bh) * nchunks + c) * R::BYTES;
+
+    // ---- stage q, k (rows past n zero), beta (0 past n), and b = cumulative
+    // log2 alpha per channel (flat past n: the gates there count as 1)
+    stage_rows<C, DK>(sQ, LDQ, qh, DK, n, tid, NTHR);
+    stage_rows<C, DK>(sK, LDQ, kh, DK, n, tid, NTHR);
+    for (int t = tid; t < C; t += NTHR) sBeta[t] = t < n ? p.beta[tok0 + t] : 0.f;
+    for (int ch = tid; ch < DK; ch += NTHR) {
+        float acc = 0.f;
+        for (int t = 0; t < C; ++t) {
+            if (t < n) acc += __builtin_amdgcn_logf(ah[static_cast<size_t>(t) * DK + ch]);
+            sB[t * LDB + ch] = acc;
+        }
+    }
+    __syncthreads();
+
+    // ---- scores P and A by 16 x 16 tiles (I, J), J <= I, dealt to the waves
+    const int lr = lane & 15, lg = lane >> 4;
+    for (int tt = wave; tt < NB * (NB + 1) / 2; tt += NTHR / 64) {
+        int I = 0;
+        while ((I + 1) * (I + 2) / 2 <= tt) ++I;
+        const int J = tt - I * (I + 1) / 2;
+        if (J < I) {
+            // reference token r = last of key block J: for query t > r and key
+            // j <= r, D_tj = e^{b_t - b_r} e^{b_r - b_j}, both factors <= 1
+            const int t = 16 * I + lr, j = 16 * J + lr, r = 16 * J + 15;
+            f32x4 accP = zero4(), accA = zero4();
+#pragma unroll
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+                const int ch = k0 + 4 * lg;
+                float qs[4], ks[4], kj[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float br = sB[r * LDB + ch + i];
+                    const float ft = __builtin_amdgcn_exp2f(sB[t * LDB + ch + i] - br);
+                    const float fj = __builtin_amdgcn_exp2f(br - sB[j * LDB + ch + i]);
+                    qs[i] = to_f32(sQ[t * LDQ + ch + i]) * ft;
+                    ks[i] = to_f32(sK[t * LDQ + ch + i]) * ft;
+                    kj[i] = to_f32(sK[j * LDQ + ch + i]) * fj;
+                }
+                const auto gk = Gp::make(kj[0], kj[1], kj[2], kj[3]);
+                mma16(accP, Gp::make(qs[0], qs[1], qs[2], qs[3]), gk);
+                mma16(accA, Gp::make(ks[0], ks[1], ks[2], ks[3]), gk);
+            }
+            // result layout: lane holds rows (queries) 16 I + 4 lg + i of column
+            // (key) 16 J + lr
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tq = 16 * I + 4 * lg + i;
+                sP[tq * LDA + 16 * J + lr] = accP[i];
+                sA[tq * LDA + 16 * J + lr] = sBeta[tq] * accA[i];
+            }
+        } else {
+            // diagonal block: exact.  Lane (j, cq): key token j of the block and
+            // a group of channels; kd_c = k_jc prod_{j < i <= t} alpha_ic runs
+            // one query token t per step (gates re-read from global memory)
+            constexpr int NQ = DK / 8 < 4 ? DK / 8 : 4;
+            constexpr int CPL = DK / NQ;
+            const int j = lr, cq = lg;
+            const bool act = cq < NQ;
+            const int ch0 = (act ? cq : 0) * CPL;
+            const int rj = 16 * I + j;
+            float kd[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) kd[i] = act ? to_f32(sK[rj * LDQ + ch0 + i]) : 0.f;
+#pragma unroll 1
+            for (int t = 0; t < 16; ++t) {
+                const int rt = 16 * I + t;
+                const bool adv = t > j && rt < n;   // past n the gates count as 1
+                const float *arow = ah + static_cast<size_t>(min(rt, n - 1)) * DK + ch0;
+                float sp = 0.f, sa = 0.f;
+#pragma unroll
+                for (int cg = 0; cg < CPL; cg += 8) {
+                    asm volatile("" ::: "memory");   // one channel group's loads at a time
+                    float al[8];
+                    load8(arow + cg, al);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        kd[cg + i] *= adv ? al[i] : 1.f;
+                        sp += to_f32(sQ[rt * LDQ + ch0 + cg + i]) * kd[cg + i];
+                        sa += to_f32(sK[rt * LDQ + ch0 + cg + i]) * kd[cg + i];
+                    }
+                }
+                sp += __shfl_xor(sp, 16);
+                sp += __shfl_xor(sp, 32);
+                sa += __shfl_xor(sa, 16);
+                sa += __shfl_xor(sa, 32);
+                if (cq == 0) {
+                    sP[rt * LDA + 16 * I + j] = t >= j ? sp : 0.f;
+                    sA[rt * LDA + 16 * I + j] = t > j ? sBeta[rt] * sa : 0.f;
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- W and U': column col of [W | U'] per thread, forward substitution
+    //   x_i = rhs_i - sum_{m < i} A_im x_m
+    // with rhs = beta o (K o e^b) (W) or beta o V (U')
+    {
+        const int col = tid;
+        if (col < DK + DV) {
+            // right-hand sides first, then the substitution in place (ascending
+            // m in every row sum)
+            float x[C];
+#pragma unroll
+            for (int i = 0; i < C; ++i)
+                x[i] = col < DK ? sBeta[i] * to_f32(sK[i * LDQ + col]) * __builtin_amdgcn_exp2f(sB[i * LDB + col])
+                                : (i < n ? sBeta[i] * to_f32(vh[static_cast<size_t>(i) * DV + col - DK]) : 0.f);
+#pragma unroll
+            for (int i = 1; i < C; ++i) {
+                const float *arow = sA + i * LDA;
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < i; ++m) acc += arow[m] * x[m];
+                x[i] -= acc;
+            }
+            Op *dst = col < DK ? reinterpret_cast<Op *>(rec + R::WT) + col
+                               : reinterpret_cast<Op *>(rec + R::UP) + (col - DK);
+            const int ld = col < DK ? DK : DV;
+#pragma unroll
+            for (int i = 0; i < C; ++i) from_f32(dst[i * ld], x[i]);
+        }
+    }
+
+    // ---- Q o e^b, K o e^{b_n - b}, e^{b_n} and P (its lower blocks)
+    {
+        Op *qt = reinterpret_cast<Op *>(rec + R::QT);
+        Op *kt = reinterpret_cast<Op *>(rec + R::KT);
+        for (int e = tid; e < C * DK; e += NTHR) {
+            const int t = e / DK, ch = e % DK;
+            const float b = sB[t * LDB + ch], bn = sB[(n - 1) * LDB + ch];
+            from_f32(qt[e], to_f32(sQ[t * LDQ + ch]) * __builtin_amdgcn_exp2f(b));
+            from_f32(kt[e], to_f32(sK[t * LDQ + ch]) * __builtin_amdgcn_exp2f(bn - b));
+        }
+        float *ec = reinterpret_cast<float *>(rec + R::EC);
+        for (int ch = tid; ch < DK; ch += NTHR) ec[ch] = __builtin_amdgcn_exp2f(sB[(n - 1) * LDB + ch]);
+        Op *pt = reinterpret_cast<Op *>(rec + R::PT);
+        for (int e = tid; e < C * C; e += NTHR) {
+            const int t = e / C, j = e % C;
+            if (j / 16 <= t / 16) from_f32(pt[e], sP[t * LDA + j]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ chain
+// One workgroup per (head, DVB value channels): NW waves, the first DVB / 16
+// of them state waves (16 value channels each).  Every wave loads the next
+// chunk's record into registers while the state waves work on the current
+// one; the stores to LDS follow a barrier.
+template <class DT, int DK, int DV, int DVB, int C, int NW>
+__global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p, const unsigned char *ws) {
+    typedef typename DT::storage IO;
+    typedef typename OpOf<DT>::type Op;
+    typedef Group<Op> Gp;
+    typedef typename Gp::type G4;
+    typedef KdaRec<Op, DK, DV, C> R;
+    constexpr int WS = DVB / 16;
+    constexpr int NTHR = NW * 64;
+    constexpr int NB = C / 16, NCB = DK / 16;
+    constexpr int PAD = 16 / sizeof(Op);
+    constexpr int LDK = DK + PAD, LDU = DVB + PAD, LDC = C + PAD;
+    static_assert(WS <= NW && C <= 64 && C % 16 == 0, "chain tiling");
+
+    __shared__ __align__(16) Op sQt[C * LDK];
+    __shared__ __align__(16) Op sWt[C * LDK];
+    __shared__ __align__(16) Op sKt[C * LDK];
+    __shared__ __align__(16) Op sUp[C * LDU];
+    __shared__ __align__(16) Op sPt[C * LDC];
+    __shared__ __align__(16) float sEC[DK];
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    int bh, vb;
+    block_to_head(blockIdx.x, p.n_heads, p.n_vblk, bh, vb);
+    const int nchunks = (p.T + C - 1) / C;
+    const bool state_wave = wave < WS;
+    const int vloc = 16 * wave + lr;
+    const int vch = vb * DVB + vloc;
+    const size_t srow = (static_cast<size_t>(bh) * DV + (state_wave ? vch : 0)) * DK;
+    IO *oh = static_cast<IO *>(p.out) + static_cast<size_t>(bh) * p.T * DV;
+
+    f32x4 st[NCB];   // S^T[c][v]: key channels 16 cb + 4 lg + i of this lane's value column
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        st[cb] = zero4();
+        if (p.S0 && state_wave) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(p.S0 + srow + 16 * cb + 4 * lg);
+            st[cb] = f32x4{s4.x, s4.y, s4.z, s4.w};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    TilePrefetch<C, DK, NTHR, Op> pq, pw, pk;
+    TilePrefetch<C, DVB, NTHR, Op> pu;
+    TilePrefetch<C, C, NTHR, Op> pp;
+    float4 pe = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto load = [&](int c) {
+        const unsigned char *rec = ws + (static_cast<size_t>(bh) * nchunks + c) * R::BYTES;
+        pq.load(reinterpret_cast<const Op *>(rec + R::QT), DK, C, tid);
+        pw.load(reinterpret_cast<const Op *>(rec + R::WT), DK, C, tid);
+        pk.load(reinterpret_cast<const Op *>(rec + R::KT), DK, C, tid);
+        pu.load(reinterpret_cast<const Op *>(rec + R::UP) + vb * DVB, DV, C, tid);
+        pp.load(reinterpret_cast<const Op *>(rec + R::PT), C, C, tid);
+        if (tid < DK / 4) pe = reinterpret_cast<const float4 *>(rec + R::EC)[tid];
+    };
+    auto store = [&]() {
+        pq.store(sQt, LDK, tid);
+        pw.store(sWt, LDK, tid);
+        pk.store(sKt, LDK, tid);
+        pu.store(sUp, LDU, tid);
+        pp.store(sPt, LDC, tid);
+        if (tid < DK / 4) reinterpret_cast<float4 *>(sEC)[tid] = pe;
+    };
+
+    if (nchunks > 0) {
+        load(0);
+        store();
+        __syncthreads();
+    }
+    for (int c = 0; c < nchunks; ++c) {
+        if (c + 1 < nchunks) load(c + 1);
+        if (state_wave) {
+            G4 sb[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
+            // X^T = S0 (Q o e^b)^T (lane: values 4 lg .. of token 16 I + lr) and
+            // W S0^T (lane: tokens 16 I + 4 lg + i of value lr)
+            f32x4 xs[NB], wsv[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                xs[I] = zero4();
+                wsv[I] = zero4();
+                const Op *qr = sQt + (16 * I + lr) * LDK + 4 * lg;
+                const Op *wr = sWt + (16 * I + lr) * LDK + 4 * lg;
+#pragma unroll
+                for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
+                    mma32(xs[I], sb[s2], sb[s2 + 1], ld_group(qr + 16 * s2), ld_group(qr + 16 * s2 + 16));
+                    mma32(wsv[I], ld_group(wr + 16 * s2), ld_group(wr + 16 * s2 + 16), sb[s2], sb[s2 + 1]);
+                }
+                if constexpr (NCB % 2 == 1) {
+                    mma16(xs[I], sb[NCB - 1], ld_group(qr + 16 * (NCB - 1)));
+                    mma16(wsv[I], ld_group(wr + 16 * (NCB - 1)), sb[NCB - 1]);
+                }
+            }
+            // U = U' - W S0^T, as operand groups (rows: tokens)
+            G4 ub[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                f32x4 u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[i] = to_f32(sUp[(16 * I + 4 * lg + i) * LDU + vloc]) - wsv[I][i];
+                ub[I] = Gp::make(u);
+            }
+            // O^T = X^T + U^T P^T, stored four values of a token at a time
+            const int n = min(C, p.T - c * C);
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                f32x4 o = xs[I];
+                tile_mma_rl_n<NB>(o, ub, sPt + 16 * I * LDC, LDC, I + 1, lane);
+                const int t = 16 * I + lr;
+                if (t < n) st_group(oh + static_cast<size_t>(c * C + t) * DV + vb * DVB + 16 * wave + 4 * lg, Gp::make(o));
+            }
+            // S^T <- diag(e^{b_n}) S^T + (K o e^{b_n - b})^T U
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const float4 e4 = *reinterpret_cast<const float4 *>(sEC + 16 * cb + 4 * lg);
+                st[cb][0] *= e4.x; st[cb][1] *= e4.y; st[cb][2] *= e4.z; st[cb][3] *= e4.w;
+#pragma unroll
+                for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
+                    mma32(st[cb], kt_group<0>(sKt, LDK, 16 * s2, 16 * cb, lane),
+                          kt_group<0>(sKt, LDK, 16 * s2 + 16, 16 * cb, lane), ub[s2], ub[s2 + 1]);
+                if constexpr (NB % 2 == 1) mma16(st[cb], kt_group<0>(sKt, LDK, 16 * (NB - 1), 16 * cb, lane), ub[NB - 1]);
+            }
+        }
+        __syncthreads();
+        if (c + 1 < nchunks) store();
+        __syncthreads();
+    }
+
+    if (p.S_T && state_wave) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+            *reinterpret_cast<float4 *>(p.S_T + srow + 16 * cb + 4 * lg) = make_float4(st[cb][0], st[cb][1], st[cb][2], st[cb][3]);
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+
+constexpr int kKdaChainWaves = 4;
+
+template <class DT, int DK, int DV, int C>
+static constexpr size_t kda_rec_bytes() { return KdaRec<typename OpOf<DT>::type, DK, DV, C>::BYTES; }
+
+template <class DT, int DK, int DV, int C>
+static hipError_t launch_kda_t(const ChunkArgs &a) {
+    ChunkParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.beta = a.beta; p.S0 = a.S0; p.z0 = nullptr;
+    p.out = a.out; p.S_T = a.S_T; p.z_T = nullptr;
+    p.T = a.T; p.d_v = DV; p.n_heads = a.B * a.H;
+    constexpr int DVB = DV >= 32 ? 32 : 16;
+    p.n_vblk = DV / DVB;
+    const int nchunks = (a.T + C - 1) / C;
+    unsigned char *ws = static_cast<unsigned char *>(a.workspace);
+    if (nchunks > 0) {
+        const int64_t prep_blocks = static_cast<int64_t>(p.n_heads) * nchunks;
+        hipLaunchKernelGGL((kda_prep_kernel<DT, DK, DV, C>), dim3(static_cast<uint32_t>(prep_blocks)),
+                           dim3(kKdaPrepThreads), 0, a.stream, p, ws);
+    }
+    const int64_t blocks = static_cast<int64_t>(p.n_heads) * p.n_vblk;
+    hipLaunchKernelGGL((kda_chain_kernel<DT, DK, DV, DVB, C, kKdaChainWaves>), dim3(static_cast<uint32_t>(blocks)),
+                       dim3(kKdaChainWaves * 64), 0, a.stream, p, static_cast<const unsigned char *>(ws));
+    return hipGetLastError();
+}
+
+// chunk lengths of this path: 16, 32 or 64 (128 runs as 64)
+static int kda_chunk(int chunk) { return chunk == 16 ? 16 : chunk == 32 ? 32 : 64; }
+
+template <class DT, int DK, int DV>
+static hipError_t kda_c(const ChunkArgs &a) {
+    switch (kda_chunk(a.chunk)) {
+        case 16: return launch_kda_t<DT, DK, DV, 16>(a);
+        case 32: return launch_kda_t<DT, DK, DV, 32>(a);
+    }
+    return launch_kda_t<DT, DK, DV, 64>(a);
+}
+
+template <class DT, int DK>
+static hipError_t kda_dv(const ChunkArgs &a) {
+    switch (a.d_v) {
+        case 16: return kda_c<DT, DK, 16>(a);
+        case 32: return kda_c<DT, DK, 32>(a);
+        case 64: return kda_c<DT, DK, 64>(a);
+        case 128: return kda_c<DT, DK, 128>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <class DT>
+static hipError_t kda_dk(const ChunkArgs &a) {
+    switch (a.d_k) {
+        case 16: return kda_dv<DT, 16>(a);
+        case 32: return kda_dv<DT, 32>(a);
+        case 64: return kda_dv<DT, 64>(a);
+        case 128: return kda_dv<DT, 128>(a);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_kda(const ChunkArgs &a) {
+    if (a.dtype == LA_BF16) return kda_dk<BF16>(a);
+    return kda_dk<F32>(a);
+}
+
+// Workspace of the per-channel-decay path: one record per chunk and head.
+size_t kda_workspace_bytes(const ChunkArgs &a) {
+    if (a.T <= 0) return 0;
+    const int C = kda_chunk(a.chunk);
+    const size_t op = a.dtype == LA_BF16 ? 2 : 4;
+    const size_t rec = ((3 * static_cast<size_t>(C) * a.d_k + static_cast<size_t>(C) * a.d_v +
+                         static_cast<size_t>(C) * C) * op + a.d_k * 4 + 255) / 256 * 256;
+    return static_cast<size_t>(a.B) * a.H * ((a.T + C - 1) / C) * rec;
+}
+
+}  // namespace la

@@ -1444,6 +1444,7 @@ static hipError_t linear_variant(const ChunkArgs &a) {
 // Workspace of the chunked forward: the segment slots of the normalized
 // variant (none for the other variants).
 size_t chunk_workspace_bytes(const ChunkArgs &a) {
+    if (a.variant == LA_KDA) return kda_workspace_bytes(a);
     if ((a.variant != LA_NORMALIZED && a.variant != LA_RETENTION) || a.T <= 0) return 0;
     const int64_t n = linear_max_segments(a);
     const size_t heads = static_cast<size_t>(a.B) * a.H;

@@ -27,6 +27,11 @@
 //     o_i = (r + v_i (phi(k).phi(q))) / (gamma z_old.phi(q) + phi(k).phi(q))
 //   retention (page "Ch. 11 Linear attention and Hyena", 11.3, RetNet bullet):
 //     the same without z: o_i = r + v_i (phi(k).phi(q))
+//   delta rule with a per-channel decay alpha (page "Beyond -- Linear
+//   attention and recurrent memory", "From fixed decay to KDA's gated delta
+//   write"; decay first as above): with a = alpha o k, b = alpha o q,
+//     p = S_i.a, r = S_i.b, u = beta (v_i - p),
+//     S_i <- S_i o alpha + u k,  o_i = r + u (k.q)
 #include "la_internal.hpp"
 
 namespace la {
@@ -65,7 +70,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         vv[r] = load1(v + h * DV + row0 + r * GPH);
     }
 
-    if constexpr (VAR == LA_GATED_DELTA) {
+    if constexpr (VAR == LA_KDA) {
+        float al[8], ak[8], aq[8];
+        load8(gate + h * DK + c0, al);
+        const float b = beta[h];
+        float kq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { kq += kk[c] * qq[c]; ak[c] = al[c] * kk[c]; aq[c] = al[c] * qq[c]; }
+        kq = group_sum<G>(kq);
+#pragma unroll
+        for (int r = 0; r < RPG; ++r) {
+            float p = 0.f, rq = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) { p += s[r][c] * ak[c]; rq += s[r][c] * aq[c]; }
+            p = group_sum<G>(p);
+            rq = group_sum<G>(rq);
+            const float u = b * (vv[r] - p);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) s[r][c] = s[r][c] * al[c] + u * kk[c];
+            vv[r] = rq + u * kq;
+        }
+    } else if constexpr (VAR == LA_GATED_DELTA) {
         const float g = gate[h];
         const float b = beta[h];
         float kq = 0.f;
@@ -211,7 +236,34 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(
 #pragma unroll
         for (int r = 0; r < RPG; ++r) vv[r] = load1(v + tok * DV + row0 + r * GPH);
 
-        if constexpr (VAR == LA_GATED_DELTA) {
+        if constexpr (VAR == LA_KDA) {
+            float al[8], ak[8], aq[8];
+            load8(gate + tok * DK + c0, al);
+            const float b = beta[tok];
+            float kq = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                ak[c] = al[c] * kk[c];
+                aq[c] = COMMIT ? 0.f : al[c] * qq[c];
+                if constexpr (!COMMIT) kq += kk[c] * qq[c];
+            }
+            if constexpr (!COMMIT) kq = group_sum<G>(kq);
+#pragma unroll
+            for (int r = 0; r < RPG; ++r) {
+                float p = 0.f, rq = 0.f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    p += s[r][c] * ak[c];
+                    if constexpr (!COMMIT) rq += s[r][c] * aq[c];
+                }
+                p = group_sum<G>(p);
+                if constexpr (!COMMIT) rq = group_sum<G>(rq);
+                const float u = b * (vv[r] - p);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) s[r][c] = s[r][c] * al[c] + u * kk[c];
+                vv[r] = rq + u * kq;
+            }
+        } else if constexpr (VAR == LA_GATED_DELTA) {
             const float g = gate[tok], b = beta[tok];
             float kq = 0.f;
             if constexpr (!COMMIT) {
@@ -369,6 +421,7 @@ template <class DT>
 static hipError_t decode_variant(const DecodeArgs &a) {
     if (a.variant == LA_NORMALIZED) return decode_dk<LA_NORMALIZED, DT, LA_PHI_ELU1>(a);
     if (a.variant == LA_GATED_DELTA) return decode_dk<LA_GATED_DELTA, DT, LA_PHI_IDENTITY>(a);
+    if (a.variant == LA_KDA) return decode_dk<LA_KDA, DT, LA_PHI_IDENTITY>(a);
     if (a.variant == LA_RETENTION) {
         if (a.phi == LA_PHI_ELU1) return decode_dk<LA_RETENTION, DT, LA_PHI_ELU1>(a);
         return decode_dk<LA_RETENTION, DT, LA_PHI_IDENTITY>(a);

@@ -39,6 +39,8 @@ struct ChunkArgs {
 
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_chunk(const ChunkArgs &a);
+hipError_t launch_chunk_kda(const ChunkArgs &a);
 size_t chunk_workspace_bytes(const ChunkArgs &a);
+size_t kda_workspace_bytes(const ChunkArgs &a);
 
 }  // namespace la

@@ -23,6 +23,12 @@
  *                   o_t = S_t q_t.
  *                   Page "Module 18 Beyond attention", section 18.2; page
  *                   "Linear Attention", gated-delta-rule formulation.
+ *   LA_KDA          the gated delta rule with a per-key-channel (diagonal)
+ *                   decay alpha_t in (0,1]^{d_k}, decay first:
+ *                   S_t = S_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T)
+ *                         + beta_t v_t k_t^T,  o_t = S_t q_t.
+ *                   Page "Beyond -- Linear attention and recurrent memory",
+ *                   section "From fixed decay to KDA's gated delta write".
  *   LA_RETENTION    linear attention with a fixed per-head decay gamma_h and
  *                   no normalizer (the constant gate):
  *                   S_t = gamma_h S_{t-1} + v_t phi(k_t)^T,  o_t = S_t phi(q_t).
@@ -82,7 +88,7 @@ typedef enum {
     LA_EHIP = 3           /* the HIP runtime reported an error at launch */
 } la_status;
 
-typedef enum { LA_NORMALIZED = 0, LA_GATED = 1, LA_GATED_DELTA = 2, LA_RETENTION = 3 } la_variant;
+typedef enum { LA_NORMALIZED = 0, LA_GATED = 1, LA_GATED_DELTA = 2, LA_RETENTION = 3, LA_KDA = 4 } la_variant;
 typedef enum { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
 typedef enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1 } la_phi;
 
@@ -92,7 +98,8 @@ typedef enum { LA_PHI_IDENTITY = 0, LA_PHI_ELU1 = 1 } la_phi;
  *   dtype    la_dtype of q, k, v, out.
  *   phi      feature map on q and k.  LA_NORMALIZED requires LA_PHI_ELU1 (the
  *            normalizer needs positive features); LA_GATED and LA_RETENTION
- *            accept either; LA_GATED_DELTA requires LA_PHI_IDENTITY.
+ *            accept either; LA_GATED_DELTA and LA_KDA require
+ *            LA_PHI_IDENTITY.
  *   B, H     batch size and heads, >= 0.
  *   T        tokens per sequence, >= 0 (ignored by la_decode_step).
  *   d_k      key/query head size; d_v value head size.  Supported:
@@ -113,7 +120,10 @@ typedef struct {
 
 /*
  * Bytes of device workspace la_chunk_fwd needs for `desc` (0 when none).
- * Only LA_NORMALIZED with T > 0 uses one.  When its heads alone cannot occupy
+ * LA_KDA with T > 0 needs one record per chunk of every head, holding the
+ * chunk's state-independent tiles (Q and K scaled by their decays, W, U' and
+ * the scores; about 72.5 KiB per 64-token chunk at d_k = d_v = 128 in bf16).
+ * LA_NORMALIZED and LA_RETENTION with T > 0 use one as follows.  When its heads alone cannot occupy
  * the GPU its state is a plain sum over the tokens, so the sequence runs as
  * concurrent segments whose state increments are staged in the workspace
  * (one d_v x d_k + d_k float32 slot per head and segment); otherwise the
@@ -138,10 +148,11 @@ size_t la_chunk_fwd_workspace(const la_desc *desc);
  *   q     (B,H,T,d_k) dtype.            k (B,H,T,d_k) dtype.
  *   v     (B,H,T,d_v) dtype.
  *   gate  LA_GATED: gamma (B,H,T,d_k) f32, 16-byte aligned;
+ *         LA_KDA: alpha (B,H,T,d_k) f32, 16-byte aligned;
  *         LA_GATED_DELTA: g (B,H,T) f32;
  *         LA_NORMALIZED, LA_RETENTION: the fixed decay gamma_h (H,) f32,
  *         shared by the batch, or NULL for none (gamma_h = 1).
- *   beta  LA_GATED_DELTA: (B,H,T) f32; otherwise must be NULL.
+ *   beta  LA_GATED_DELTA, LA_KDA: (B,H,T) f32; otherwise must be NULL.
  *   S0    initial state (B,H,d_v,d_k) f32, or NULL for zeros.
  *   z0    LA_NORMALIZED: initial normalizer (B,H,d_k) f32 or NULL for
  *         zeros; otherwise must be NULL.
@@ -194,9 +205,10 @@ la_status la_chunk_fwd_noalloc(const la_desc *desc,
  * streamed through registers once.  desc->T and desc->chunk are ignored.
  *
  *   q, k  (B,H,d_k) dtype.   v (B,H,d_v) dtype.
- *   gate  LA_GATED: gamma (B,H,d_k) f32; LA_GATED_DELTA: g (B,H) f32;
- *         LA_NORMALIZED, LA_RETENTION: gamma_h (H,) f32 or NULL.
- *   beta  LA_GATED_DELTA: (B,H) f32; otherwise must be NULL.
+ *   gate  LA_GATED: gamma (B,H,d_k) f32; LA_KDA: alpha (B,H,d_k) f32;
+ *         LA_GATED_DELTA: g (B,H) f32; LA_NORMALIZED, LA_RETENTION:
+ *         gamma_h (H,) f32 or NULL.
+ *   beta  LA_GATED_DELTA, LA_KDA: (B,H) f32; otherwise must be NULL.
  *   S     (B,H,d_v,d_k) f32, read and overwritten with the new state.
  *   z     LA_NORMALIZED: (B,H,d_k) f32, read and overwritten; otherwise NULL.
  *   out   (B,H,d_v) dtype, written; must not overlap any other argument.
