@@ -244,7 +244,7 @@ def main(argv=None):
     stream = torch.cuda.current_stream()
 
     # ---------------- chunked forward (headline)
-    w = wl.WORKLOADS[args.workload]
+    w = wl.WORKLOADS[args.workload] if args.workload in wl.WORKLOADS else wl.EXTRA_WORKLOADS[args.workload]
     assert not w.decode, "--workload names a chunked-forward workload"
     inp = wl.chunk_inputs(w)
     d = {k: to_dev(v) for k, v in inp.items()}
@@ -272,12 +272,19 @@ def main(argv=None):
         flops = gdr_chunk_flops_per_token_head(w.d_k, w.d_v, w.chunk) * w.B * w.H * w.T
         nbytes = gdr_chunk_bytes(w.B, w.H, w.T, w.d_k, w.d_v, io_bytes)
         kname, vname = "gdr_chunk_kernel", "gated_delta_rule"
+    elif w.variant == la.LA_KDA:
+        flops = gdr_chunk_flops_per_token_head(w.d_k, w.d_v, w.chunk) * w.B * w.H * w.T
+        # per-channel gates: d_k floats per token instead of one
+        nbytes = gdr_chunk_bytes(w.B, w.H, w.T, w.d_k, w.d_v, io_bytes) + w.B * w.H * w.T * (w.d_k - 1) * 4
+        kname, vname = "kda_prep_kernel + kda_chain_kernel", "kda"
     else:
         norm = w.variant == la.LA_NORMALIZED
+        gated = w.variant == la.LA_GATED
         flops = linear_chunk_flops_per_token_head(w.d_k, w.d_v, w.chunk, norm) * w.B * w.H * w.T
-        nbytes = linear_chunk_bytes(w.B, w.H, w.T, w.d_k, w.d_v, io_bytes, not norm, norm)
+        nbytes = linear_chunk_bytes(w.B, w.H, w.T, w.d_k, w.d_v, io_bytes, gated, norm)
         kname = "linear_chunk_kernel"
-        vname = "normalized_linear_attention" if norm else "gated_linear_attention"
+        vname = {la.LA_NORMALIZED: "normalized_linear_attention", la.LA_GATED: "gated_linear_attention",
+                 la.LA_RETENTION: "retention"}[w.variant]
     gbs = nbytes / (ms_avg * 1e-3) / 1e9
     tflops = flops / (ms_avg * 1e-3) / 1e12
     traffic = read_traffic() if args.workload == CHUNK_WORKLOAD else None

@@ -47,7 +47,7 @@ struct KdaRec {
     static constexpr size_t BYTES = (EC + DK * 4 + 255) / 256 * 256;
 };
 
-constexpr int kKdaPrepThreads = 256;
+constexpr int kKdaPrepThreads = 512;
 
 // ------------------------------------------------------------------ prep
 template <class DT, int DK, int DV, int C>
@@ -86,25 +86,52 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     stage_rows<C, DK>(sQ, LDQ, qh, DK, n, tid, NTHR);
     stage_rows<C, DK>(sK, LDQ, kh, DK, n, tid, NTHR);
     for (int t = tid; t < C; t += NTHR) sBeta[t] = t < n ? p.beta[tok0 + t] : 0.f;
+    // the gates, 16-byte loads issued together (rows past n: 1)
+    for (int e = tid; e < C * DK / 4; e += NTHR) {
+        const int t = e / (DK / 4), ch = (e % (DK / 4)) * 4;
+        float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
+        if (t < n) g = *reinterpret_cast<const float4 *>(ah + static_cast<size_t>(t) * DK + ch);
+        sB[t * LDB + ch] = g.x; sB[t * LDB + ch + 1] = g.y; sB[t * LDB + ch + 2] = g.z; sB[t * LDB + ch + 3] = g.w;
+    }
+    __syncthreads();
+    // cumulative log2 per channel: one column per thread, in registers
     for (int ch = tid; ch < DK; ch += NTHR) {
-        float acc = 0.f;
-        for (int t = 0; t < C; ++t) {
-            if (t < n) acc += __builtin_amdgcn_logf(ah[static_cast<size_t>(t) * DK + ch]);
-            sB[t * LDB + ch] = acc;
-        }
+        float col[C];
+#pragma unroll
+        for (int t = 0; t < C; ++t) col[t] = __builtin_amdgcn_logf(sB[t * LDB + ch]);
+#pragma unroll
+        for (int t = 1; t < C; ++t) col[t] += col[t - 1];
+#pragma unroll
+        for (int t = 0; t < C; ++t) sB[t * LDB + ch] = col[t];
     }
     __syncthreads();
 
     // ---- scores P and A by 16 x 16 tiles (I, J), J <= I, dealt to the waves
+    // round robin along the diagonals (the diagonal tiles first)
     const int lr = lane & 15, lg = lane >> 4;
     for (int tt = wave; tt < NB * (NB + 1) / 2; tt += NTHR / 64) {
-        int I = 0;
-        while ((I + 1) * (I + 2) / 2 <= tt) ++I;
-        const int J = tt - I * (I + 1) / 2;
-        if (J < I) {
-            // reference token r = last of key block J: for query t > r and key
-            // j <= r, D_tj = e^{b_t - b_r} e^{b_r - b_j}, both factors <= 1
-            const int t = 16 * I + lr, j = 16 * J + lr, r = 16 * J + 15;
+        int dgl = 0, first = 0;                        // tile tt lies on sub-diagonal dgl
+        while (first + (NB - dgl) <= tt) first += NB - dgl++;
+        const int J = tt - first, I = J + dgl;
+        // Off the diagonal (J < I) the reference token is the last of key block
+        // J: for query t > r and key j <= r, D_tj = e^{b_t - b_r} e^{b_r - b_j},
+        // both factors <= 1.  On the diagonal the reference is the token
+        // before the block (b = 0 before the chunk): the query factor is <= 1,
+        // the key factor e^{b_r - b_j} >= 1 is bounded by the channel's decay
+        // over the block, so this form is taken only while every channel's
+        // decay over the block stays within 2^64 (`fast`), else the exact
+        // routine below.
+        const bool diag = J == I;
+        const int r = diag ? 16 * I - 1 : 16 * J + 15;
+        bool fast = !diag;
+        if (diag) {
+            bool weak = false;
+            for (int ch = lane; ch < DK; ch += 64)
+                weak |= (r >= 0 ? sB[r * LDB + ch] : 0.f) - sB[(16 * I + 15) * LDB + ch] > 64.f;
+            fast = __builtin_amdgcn_ballot_w64(weak) == 0;
+        }
+        if (fast) {
+            const int t = 16 * I + lr, j = 16 * J + lr;
             f32x4 accP = zero4(), accA = zero4();
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 16) {
@@ -112,55 +139,54 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
                 float qs[4], ks[4], kj[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float br = sB[r * LDB + ch + i];
+                    const float br = r >= 0 ? sB[r * LDB + ch + i] : 0.f;
                     const float ft = __builtin_amdgcn_exp2f(sB[t * LDB + ch + i] - br);
                     const float fj = __builtin_amdgcn_exp2f(br - sB[j * LDB + ch + i]);
                     qs[i] = to_f32(sQ[t * LDQ + ch + i]) * ft;
                     ks[i] = to_f32(sK[t * LDQ + ch + i]) * ft;
                     kj[i] = to_f32(sK[j * LDQ + ch + i]) * fj;
                 }
-                const auto gk = Gp::make(kj[0], kj[1], kj[2], kj[3]);
-                mma16(accP, Gp::make(qs[0], qs[1], qs[2], qs[3]), gk);
-                mma16(accA, Gp::make(ks[0], ks[1], ks[2], ks[3]), gk);
+                // float32 operands whatever the input type: the scaled operands
+                // are not exact in bf16, and rounding them would be amplified
+                // where q.k cancels
+                const float4 gk = make_float4(kj[0], kj[1], kj[2], kj[3]);
+                mma16(accP, make_float4(qs[0], qs[1], qs[2], qs[3]), gk);
+                mma16(accA, make_float4(ks[0], ks[1], ks[2], ks[3]), gk);
             }
             // result layout: lane holds rows (queries) 16 I + 4 lg + i of column
-            // (key) 16 J + lr
+            // (key) 16 J + lr; on the diagonal keep j <= t (P) and j < t (A)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int tq = 16 * I + 4 * lg + i;
-                sP[tq * LDA + 16 * J + lr] = accP[i];
-                sA[tq * LDA + 16 * J + lr] = sBeta[tq] * accA[i];
+                const int tq = 16 * I + 4 * lg + i, jk = 16 * J + lr;
+                sP[tq * LDA + jk] = !diag || jk <= tq ? accP[i] : 0.f;
+                sA[tq * LDA + jk] = !diag || jk < tq ? sBeta[tq] * accA[i] : 0.f;
             }
         } else {
             // diagonal block: exact.  Lane (j, cq): key token j of the block and
-            // a group of channels; kd_c = k_jc prod_{j < i <= t} alpha_ic runs
-            // one query token t per step (gates re-read from global memory)
+            // a group of channels; for each query token t >= j the decay factor
+            // e^{b_tc - b_jc} (exponent <= 0) is formed directly
             constexpr int NQ = DK / 8 < 4 ? DK / 8 : 4;
             constexpr int CPL = DK / NQ;
             const int j = lr, cq = lg;
             const bool act = cq < NQ;
             const int ch0 = (act ? cq : 0) * CPL;
             const int rj = 16 * I + j;
-            float kd[CPL];
+            float kj[CPL], bj[CPL];
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) kd[i] = act ? to_f32(sK[rj * LDQ + ch0 + i]) : 0.f;
+            for (int i = 0; i < CPL; ++i) {
+                kj[i] = act ? to_f32(sK[rj * LDQ + ch0 + i]) : 0.f;
+                bj[i] = sB[rj * LDB + ch0 + i];
+            }
 #pragma unroll 1
             for (int t = 0; t < 16; ++t) {
                 const int rt = 16 * I + t;
-                const bool adv = t > j && rt < n;   // past n the gates count as 1
-                const float *arow = ah + static_cast<size_t>(min(rt, n - 1)) * DK + ch0;
                 float sp = 0.f, sa = 0.f;
 #pragma unroll
-                for (int cg = 0; cg < CPL; cg += 8) {
-                    asm volatile("" ::: "memory");   // one channel group's loads at a time
-                    float al[8];
-                    load8(arow + cg, al);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        kd[cg + i] *= adv ? al[i] : 1.f;
-                        sp += to_f32(sQ[rt * LDQ + ch0 + cg + i]) * kd[cg + i];
-                        sa += to_f32(sK[rt * LDQ + ch0 + cg + i]) * kd[cg + i];
-                    }
+                for (int i = 0; i < CPL; ++i) {
+                    // t < j: the exponent is positive, but those entries are masked below
+                    const float kd = kj[i] * __builtin_amdgcn_exp2f(fminf(sB[rt * LDB + ch0 + i] - bj[i], 0.f));
+                    sp += to_f32(sQ[rt * LDQ + ch0 + i]) * kd;
+                    sa += to_f32(sK[rt * LDQ + ch0 + i]) * kd;
                 }
                 sp += __shfl_xor(sp, 16);
                 sp += __shfl_xor(sp, 32);
@@ -181,8 +207,7 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     {
         const int col = tid;
         if (col < DK + DV) {
-            // right-hand sides first, then the substitution in place (ascending
-            // m in every row sum)
+            // right-hand sides first, then the substitution in place
             float x[C];
 #pragma unroll
             for (int i = 0; i < C; ++i)
@@ -190,11 +215,13 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
                                 : (i < n ? sBeta[i] * to_f32(vh[static_cast<size_t>(i) * DV + col - DK]) : 0.f);
 #pragma unroll
             for (int i = 1; i < C; ++i) {
+                // four independent partial sums (m mod 4), so that the row sum
+                // is not one chain of dependent multiply-adds
                 const float *arow = sA + i * LDA;
-                float acc = 0.f;
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 0; m < i; ++m) acc += arow[m] * x[m];
-                x[i] -= acc;
+                for (int m = 0; m < i; ++m) acc[m & 3] += arow[m] * x[m];
+                x[i] -= (acc[0] + acc[1]) + (acc[2] + acc[3]);
             }
             Op *dst = col < DK ? reinterpret_cast<Op *>(rec + R::WT) + col
                                : reinterpret_cast<Op *>(rec + R::UP) + (col - DK);

@@ -135,6 +135,16 @@ WORKLOADS = {
 # Workload order of the five shapes the operator is specified on.
 WORKLOAD_ORDER = list(WORKLOADS)
 
+# Further workloads of the same recipe at the specified shapes, for the
+# variants added beside the five (benchmarked, not part of the five).
+EXTRA_WORKLOADS = {
+    "kda_bf16_b4h16t8192d128": Workload(
+        "kda_bf16_b4h16t8192d128", KDA, "bf16", 4, 16, 8192, 128, 128, 64, 128 ** -0.5,
+        gate_mean=4.0, beta_mean=0.0, seed=6),
+    "ret_bf16_b4h8t2048d64": Workload(
+        "ret_bf16_b4h8t2048d64", RETENTION, "bf16", 4, 8, 2048, 64, 64, 64, 64 ** -0.5, gate_mean=3.0, seed=7),
+}
+
 
 def chunk_inputs(w: Workload, seed: int | None = None, *, T: int | None = None,
                  B: int | None = None, H: int | None = None,
