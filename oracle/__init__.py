@@ -87,6 +87,8 @@ class OracleLib:
         lib.oracle_forward.restype = i
         lib.oracle_decode_step.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, i]
         lib.oracle_decode_step.restype = i
+        lib.oracle_backward.argtypes = [i, i, i, i, i, i, i] + [dp] * 15
+        lib.oracle_backward.restype = i
         lib.oracle_phi.argtypes = [i, ctypes.c_double]
         lib.oracle_phi.restype = ctypes.c_double
         lib.oracle_num_threads.argtypes = []
@@ -131,6 +133,32 @@ class OracleLib:
         if rc != 0:
             raise RuntimeError("oracle_forward failed with code %d" % rc)
         return out, S_T, z_T
+
+    def backward(self, variant, q, k, v, dout, gate=None, S0=None, z0=None, dS_T=None, dz_T=None,
+                 phi_kind=None):
+        """Gradients of forward() for NORMALIZED and RETENTION (reverse-mode
+        through the token recurrence).  Returns a dict with dq, dk, dv, dS0,
+        dz0 (NORMALIZED) and dgate ((H,), summed over the batch; None without
+        a gate)."""
+        if phi_kind is None:
+            phi_kind = default_phi(variant)
+        assert variant in (NORMALIZED, RETENTION)
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        gate, S0, z0, dS_T, dz_T = _f64(gate), _f64(S0), _f64(z0), _f64(dS_T), _f64(dz_T)
+        B, H, T, dk = q.shape
+        dv = v.shape[-1]
+        assert dout.shape == (B, H, T, dv)
+        assert gate is None or gate.shape == (H,)
+        res = {"dq": np.empty((B, H, T, dk)), "dk": np.empty((B, H, T, dk)), "dv": np.empty((B, H, T, dv)),
+               "dS0": np.empty((B, H, dv, dk)), "dz0": np.empty((B, H, dk)) if variant == NORMALIZED else None,
+               "dgate": np.empty(H) if gate is not None else None}
+        rc = self._lib.oracle_backward(variant, phi_kind, B, H, T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                                       _ptr(S0), _ptr(z0), _ptr(dout), _ptr(dS_T), _ptr(dz_T), _ptr(res["dq"]),
+                                       _ptr(res["dk"]), _ptr(res["dv"]), _ptr(res["dgate"]), _ptr(res["dS0"]),
+                                       _ptr(res["dz0"]))
+        if rc != 0:
+            raise RuntimeError("oracle_backward failed with code %d" % rc)
+        return res
 
     def decode_step(self, variant, S, q, k, v, gate=None, beta=None, z=None,
                     phi_kind=None, nthreads=0):
@@ -187,3 +215,7 @@ def forward(*args, **kwargs):
 
 def decode_step(*args, **kwargs):
     return load().decode_step(*args, **kwargs)
+
+
+def backward(*args, **kwargs):
+    return load().backward(*args, **kwargs)

@@ -301,3 +301,148 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Gradients of oracle_forward for variants 0 (normalized, optional per-head
+ * decay) and 3 (retention): reverse-mode differentiation of the token
+ * recurrence, token by token from the last to the first, in double
+ * precision.  The recurrence (page "Beyond -- Linear attention and
+ * recurrent memory", sections "The big idea" and "Fixed decay versus an
+ * input-dependent gate"), update first, then read:
+ *     S_t = gamma S_{t-1} + phi(k_t) v_t^T,   z_t = gamma z_{t-1} + phi(k_t),
+ *     variant 0: out_t = S_t^T phi(q_t) / (z_t . phi(q_t));
+ *     variant 3: out_t = S_t^T phi(q_t).
+ * Going back from token t, with num_t = S_t^T phi(q_t) and den_t = z_t.phi(q_t):
+ *     d num = d out / den,  d den = -(d out . out) / den      (variant 0)
+ *     dS_t += phi(q_t) d num^T,  dz_t += d den phi(q_t),
+ *     d phi(q_t) = S_t d num + d den z_t,
+ *     d v_t = dS_t^T phi(k_t),  d phi(k_t) = dS_t v_t + dz_t,
+ *     d gamma += <dS_t, S_{t-1}> + dz_t . z_{t-1},
+ *     dS_{t-1} = gamma dS_t,  dz_{t-1} = gamma dz_t,
+ * and dq = d phi(q) phi'(q), dk = d phi(k) phi'(k) (phi' = 1 for the identity;
+ * for elu + 1, 1 above zero and e^x at or below).  The states S_t, z_t of the
+ * forward pass are kept for every token (small problems only).
+ *
+ * Layouts as oracle_forward; dS_T, dz_T may be NULL (zero).  Outputs dq, dk
+ * (B,H,T,d_k), dv (B,H,T,d_v), dS0 (B,H,d_v,d_k), dz0 (B,H,d_k) (variant 0)
+ * and dgate (H,) summed over the batch (only when gate is given; otherwise
+ * may be NULL).  Returns 0 on success, 1 on bad arguments, 2 on allocation
+ * failure.  Runs on one thread (the decay gradient sums over heads).
+ */
+static double phi_prime(int phi, double x)
+{
+    if (phi == 1)
+        return x > 0.0 ? 1.0 : exp(x);
+    return 1.0;
+}
+
+int oracle_backward(int variant, int phi, int B, int H, int T, int dk, int dv,
+                    const double *q, const double *k, const double *v, const double *gate,
+                    const double *S0, const double *z0,
+                    const double *dout, const double *dS_T, const double *dz_T,
+                    double *dq, double *dk_out, double *dv_out, double *dgate,
+                    double *dS0, double *dz0)
+{
+    if (variant != 0 && variant != 3) return 1;
+    if (B < 0 || H < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
+    const size_t sz = (size_t)dk * dv;
+    double *Sall = (double *)malloc(((size_t)T + 1) * sz * sizeof(double));   /* S_{-1} .. S_{T-1}, [c][i] */
+    double *zall = (double *)malloc(((size_t)T + 1) * dk * sizeof(double));
+    double *dS = (double *)malloc(sz * sizeof(double));
+    double *dz = (double *)malloc((size_t)dk * sizeof(double));
+    double *fq = (double *)malloc((size_t)dk * sizeof(double));
+    double *fk = (double *)malloc((size_t)dk * sizeof(double));
+    double *dnum = (double *)malloc((size_t)dv * sizeof(double));
+    double *num = (double *)malloc((size_t)dv * sizeof(double));
+    if (!Sall || !zall || !dS || !dz || !fq || !fk || !dnum || !num) {
+        free(Sall); free(zall); free(dS); free(dz); free(fq); free(fk); free(dnum); free(num);
+        return 2;
+    }
+    if (gate)
+        for (int h = 0; h < H; ++h) dgate[h] = 0.0;
+    for (long bh = 0; bh < (long)B * H; ++bh) {
+        const double gam = gate ? gate[bh % H] : 1.0;
+        const double *qh = q + (size_t)bh * T * dk, *kh = k + (size_t)bh * T * dk, *vh = v + (size_t)bh * T * dv;
+        const double *doh = dout + (size_t)bh * T * dv;
+        /* forward, keeping every state (internal layout [c][i], d_k x d_v) */
+        for (int i = 0; i < dv; ++i)
+            for (int c = 0; c < dk; ++c) Sall[(size_t)c * dv + i] = S0 ? S0[(size_t)bh * sz + (size_t)i * dk + c] : 0.0;
+        for (int c = 0; c < dk; ++c) zall[c] = (variant == 0 && z0) ? z0[(size_t)bh * dk + c] : 0.0;
+        for (int t = 0; t < T; ++t) {
+            const double *Sp = Sall + (size_t)t * sz, *zp = zall + (size_t)t * dk;
+            double *Sn = Sall + (size_t)(t + 1) * sz, *zn = zall + (size_t)(t + 1) * dk;
+            for (int c = 0; c < dk; ++c) {
+                const double f = phi_apply(phi, kh[(size_t)t * dk + c]);
+                for (int i = 0; i < dv; ++i) Sn[(size_t)c * dv + i] = gam * Sp[(size_t)c * dv + i] + f * vh[(size_t)t * dv + i];
+                zn[c] = gam * zp[c] + f;
+            }
+        }
+        /* backward */
+        for (int i = 0; i < dv; ++i)
+            for (int c = 0; c < dk; ++c) dS[(size_t)c * dv + i] = dS_T ? dS_T[(size_t)bh * sz + (size_t)i * dk + c] : 0.0;
+        for (int c = 0; c < dk; ++c) dz[c] = (variant == 0 && dz_T) ? dz_T[(size_t)bh * dk + c] : 0.0;
+        double dg = 0.0;
+        for (int t = T - 1; t >= 0; --t) {
+            const double *St = Sall + (size_t)(t + 1) * sz, *zt = zall + (size_t)(t + 1) * dk;
+            const double *Sp = Sall + (size_t)t * sz, *zp = zall + (size_t)t * dk;
+            const double *dot = doh + (size_t)t * dv;
+            for (int c = 0; c < dk; ++c) {
+                fq[c] = phi_apply(phi, qh[(size_t)t * dk + c]);
+                fk[c] = phi_apply(phi, kh[(size_t)t * dk + c]);
+            }
+            double dden = 0.0;
+            if (variant == 0) {
+                double den = 0.0;
+                for (int c = 0; c < dk; ++c) den += zt[c] * fq[c];
+                double dot_o = 0.0;
+                for (int i = 0; i < dv; ++i) {
+                    double s = 0.0;
+                    for (int c = 0; c < dk; ++c) s += St[(size_t)c * dv + i] * fq[c];
+                    num[i] = s;
+                    dot_o += dot[i] * (s / den);
+                    dnum[i] = dot[i] / den;
+                }
+                dden = -dot_o / den;
+            } else {
+                for (int i = 0; i < dv; ++i) dnum[i] = dot[i];
+            }
+            /* the read of token t: dS_t += phi(q) dnum^T, dz_t += dden phi(q) */
+            for (int c = 0; c < dk; ++c) {
+                for (int i = 0; i < dv; ++i) dS[(size_t)c * dv + i] += fq[c] * dnum[i];
+                dz[c] += dden * fq[c];
+            }
+            /* d phi(q_t) = S_t dnum + dden z_t */
+            for (int c = 0; c < dk; ++c) {
+                double s = 0.0;
+                for (int i = 0; i < dv; ++i) s += St[(size_t)c * dv + i] * dnum[i];
+                s += dden * zt[c];
+                dq[((size_t)bh * T + t) * dk + c] = s * phi_prime(phi, qh[(size_t)t * dk + c]);
+            }
+            /* the write of token t */
+            for (int i = 0; i < dv; ++i) {
+                double s = 0.0;
+                for (int c = 0; c < dk; ++c) s += dS[(size_t)c * dv + i] * fk[c];
+                dv_out[((size_t)bh * T + t) * dv + i] = s;
+            }
+            for (int c = 0; c < dk; ++c) {
+                double s = 0.0;
+                for (int i = 0; i < dv; ++i) s += dS[(size_t)c * dv + i] * vh[(size_t)t * dv + i];
+                s += dz[c];
+                dk_out[((size_t)bh * T + t) * dk + c] = s * phi_prime(phi, kh[(size_t)t * dk + c]);
+            }
+            /* the decay of token t */
+            for (size_t e = 0; e < sz; ++e) dg += dS[e] * Sp[e];
+            for (int c = 0; c < dk; ++c) dg += dz[c] * zp[c];
+            for (size_t e = 0; e < sz; ++e) dS[e] *= gam;
+            for (int c = 0; c < dk; ++c) dz[c] *= gam;
+        }
+        if (gate) dgate[bh % H] += dg;
+        if (dS0)
+            for (int i = 0; i < dv; ++i)
+                for (int c = 0; c < dk; ++c) dS0[(size_t)bh * sz + (size_t)i * dk + c] = dS[(size_t)c * dv + i];
+        if (dz0 && variant == 0)
+            for (int c = 0; c < dk; ++c) dz0[(size_t)bh * dk + c] = dz[c];
+    }
+    free(Sall); free(zall); free(dS); free(dz); free(fq); free(fk); free(dnum); free(num);
+    return 0;
+}

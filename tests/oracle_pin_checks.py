@@ -508,4 +508,89 @@ def check_split_call_equals_single_call(orc):
         assert _maxdiff(S2, S_T) <= TOL
 
 
+
+
+# ------------------------------------------------ gradients (training, backward)
+
+def _loss_fd(orc, variant, phi_kind, inp, cot, name, idx, h):
+    """Central difference of L = <dout, out> + <dS_T, S_T> + <dz_T, z_T> in one
+    input element (the forward pass is the pinned recurrence)."""
+    def loss(x):
+        a = dict(inp)
+        a[name] = x
+        out, S_T, z_T = orc.forward(variant, a["q"], a["k"], a["v"], gate=a.get("gate"), S0=a.get("S0"),
+                                    z0=a.get("z0"), phi_kind=phi_kind)
+        s = float(np.sum(cot["dout"] * out) + np.sum(cot["dS_T"] * S_T))
+        if z_T is not None:
+            s += float(np.sum(cot["dz_T"] * z_T))
+        return s
+    xp, xm = inp[name].copy(), inp[name].copy()
+    xp[idx] += h
+    xm[idx] -= h
+    return (loss(xp) - loss(xm)) / (2 * h)
+
+
+def _bwd_case(r, variant, B, H, T, dk, dv, decay):
+    inp = {"q": r.standard_normal((B, H, T, dk)), "k": r.standard_normal((B, H, T, dk)),
+           "v": r.standard_normal((B, H, T, dv)), "S0": r.standard_normal((B, H, dv, dk)) * 0.5}
+    if variant == NORMALIZED:
+        inp["z0"] = np.abs(r.standard_normal((B, H, dk))) + 1.0
+    if decay:
+        inp["gate"] = r.uniform(0.5, 0.99, H)
+    cot = {"dout": r.standard_normal((B, H, T, dv)), "dS_T": r.standard_normal((B, H, dv, dk)),
+           "dz_T": r.standard_normal((B, H, dk))}
+    return inp, cot
+
+
+def _check_grads_by_fd(orc, variant, phi_kind, decay, seed):
+    r = _rng(seed)
+    inp, cot = _bwd_case(r, variant, 2, 2, 7, 3, 2, decay)
+    g = orc.backward(variant, inp["q"], inp["k"], inp["v"], cot["dout"], gate=inp.get("gate"), S0=inp["S0"],
+                     z0=inp.get("z0"), dS_T=cot["dS_T"], dz_T=cot["dz_T"] if variant == NORMALIZED else None,
+                     phi_kind=phi_kind)
+    names = {"q": "dq", "k": "dk", "v": "dv", "S0": "dS0", "z0": "dz0", "gate": "dgate"}
+    for name, gname in names.items():
+        if name not in inp:
+            continue
+        x = inp[name]
+        for idx in np.ndindex(x.shape):
+            fd = _loss_fd(orc, variant, phi_kind, inp, cot, name, idx, 1e-6)
+            assert abs(g[gname][idx] - fd) <= 1e-6 * max(1.0, abs(fd)), (name, idx, g[gname][idx], fd)
+
+
+def check_grad_la_by_finite_differences(orc):
+    _check_grads_by_fd(orc, NORMALIZED, PHI_ELU1, False, 901)
+
+
+def check_grad_la_decay_by_finite_differences(orc):
+    _check_grads_by_fd(orc, NORMALIZED, PHI_ELU1, True, 902)
+
+
+def check_grad_retention_by_finite_differences(orc):
+    _check_grads_by_fd(orc, RETENTION, PHI_IDENTITY, True, 903)
+    _check_grads_by_fd(orc, RETENTION, PHI_ELU1, True, 904)
+
+
+def check_grad_retention_matches_masked_form(orc):
+    """Retention, phi = identity: out = (D o Q K^T) V with D_tj = gamma^(t-j)
+    (j <= t), so dV = (D o Q K^T)^T dO, dQ = (D o dO V^T) K, dK = (D o dO V^T)^T Q
+    exactly (zero initial state, no state cotangent)."""
+    r = _rng(905)
+    T, dk, dv, g = 40, 6, 5, 0.8
+    q, k, v, do = (r.standard_normal((1, 1, T, d)) for d in (dk, dk, dv, dv))
+    gr = orc.backward(RETENTION, q, k, v, do, gate=np.array([g]), phi_kind=PHI_IDENTITY)
+    Q, K, V, dO = q[0, 0], k[0, 0], v[0, 0], do[0, 0]
+    t = np.arange(T)
+    D = np.where(t[:, None] >= t[None, :], g ** (t[:, None] - t[None, :]).clip(min=0), 0.0)
+    A = D * (Q @ K.T)
+    G = D * (dO @ V.T)
+    assert _maxdiff(gr["dv"][0, 0], A.T @ dO) <= TOL * 10
+    assert _maxdiff(gr["dq"][0, 0], G @ K) <= TOL * 10
+    assert _maxdiff(gr["dk"][0, 0], G.T @ Q) <= TOL * 10
+    # dgamma: d/dg of sum_{t>=j} g^(t-j) (q_t.k_j)(dO_t.v_j)
+    E = (t[:, None] - t[None, :]).clip(min=0)
+    dD = np.where((t[:, None] > t[None, :]), E * g ** (E - 1).clip(min=0), 0.0)
+    assert abs(gr["dgate"][0] - np.sum(dD * (Q @ K.T) * (dO @ V.T))) <= TOL * 100
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_") and callable(v)]

@@ -55,6 +55,17 @@ MUTANTS = {
         ("for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] += err * kt[c];",
          "for (int c = 0; c < dk; ++c) S[(size_t)i * dk + c] = alpha[c] * S[(size_t)i * dk + c] + err * kt[c];")],
     "kda_beta_dropped": [("const double err = bw * (vt[i] - pred[i]);", "const double err = (vt[i] - pred[i]);")],
+    # gradients
+    "bwd_normalizer_cotangent_sign": [("dden = -dot_o / den;", "dden = dot_o / den;")],
+    "bwd_normalizer_cotangent_dropped": [("s += dden * zt[c];", "s += 0.0 * zt[c];")],
+    "bwd_phi_prime_dropped": [("return x > 0.0 ? 1.0 : exp(x);", "return 1.0;")],
+    "bwd_state_cotangent_not_decayed": [("for (size_t e = 0; e < sz; ++e) dS[e] *= gam;", "")],
+    "bwd_decay_grad_misses_normalizer": [("for (int c = 0; c < dk; ++c) dg += dz[c] * zp[c];", "")],
+    "bwd_decay_grad_uses_new_state": [("for (size_t e = 0; e < sz; ++e) dg += dS[e] * Sp[e];",
+                                       "for (size_t e = 0; e < sz; ++e) dg += dS[e] * St[e];")],
+    "bwd_key_grad_misses_normalizer": [("        s += dz[c];\n", "")],
+    "bwd_value_grad_uses_query": [("for (int c = 0; c < dk; ++c) s += dS[(size_t)c * dv + i] * fk[c];",
+                                   "for (int c = 0; c < dk; ++c) s += dS[(size_t)c * dv + i] * fq[c];")],
     "initial_state_ignored_for_gla": [("else                              S[(size_t)c * dv + i] = s;",
                                        "else                              S[(size_t)c * dv + i] = (variant == 1) ? 0.0 : s;")],
 }
