@@ -19,7 +19,8 @@ from ._lib import (LA_BF16, LA_EHIP, LA_EINVAL, LA_EUNSUPPORTED, LA_F32, LA_GATE
                    LA_GATED_DELTA, LA_NORMALIZED, LA_OK, LA_PHI_ELU1, LA_PHI_IDENTITY,
                    LA_RETENTION, LA_KDA, LaDesc, LaError, check, load)
 
-__all__ = ["la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step", "la_verify", "la_commit", "la_chunk_fwd_workspace", "la_status_str",
+__all__ = ["la_chunk_fwd", "la_chunk_fwd_noalloc", "la_chunk_bwd", "la_chunk_bwd_workspace",
+           "la_decode_step", "la_verify", "la_commit", "la_chunk_fwd_workspace", "la_status_str",
            "la_last_error", "la_abi_version", "make_desc", "LaDesc", "LaError",
            "LA_NORMALIZED", "LA_GATED", "LA_GATED_DELTA", "LA_RETENTION", "LA_KDA", "LA_F32", "LA_BF16",
            "LA_PHI_IDENTITY", "LA_PHI_ELU1"]
@@ -118,6 +119,17 @@ def la_chunk_fwd_workspace(desc: LaDesc) -> int:
     return int(load().la_chunk_fwd_workspace(ctypes.byref(desc)))
 
 
+def _workspace(workspace, ws_bytes, dev):
+    """The caller's workspace tensor (checked) or a new one of ws_bytes."""
+    ws = workspace
+    if ws is not None:
+        if not isinstance(ws, torch.Tensor) or ws.device != dev or not ws.is_contiguous():
+            raise ValueError("workspace: a contiguous tensor on q's device")
+    if ws is None and ws_bytes:
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    return ws, (0 if ws is None else ws.numel() * ws.element_size())
+
+
 def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, chunk=0,
                  phi=None, out=None, S_T=None, z_T=None, return_state=True, workspace=None,
                  stream=None):
@@ -149,18 +161,53 @@ def la_chunk_fwd(q, k, v, *, variant, gate=None, beta=None, S0=None, z0=None, ch
         S_T = torch.empty((B, H, d_v, d_k), dtype=f32, device=dev)
     if return_state and variant == LA_NORMALIZED and z_T is None:
         z_T = torch.empty((B, H, d_k), dtype=f32, device=dev)
-    ws_bytes = int(lib.la_chunk_fwd_workspace(ctypes.byref(desc)))
-    ws = workspace
-    if ws is not None:
-        if not isinstance(ws, torch.Tensor) or ws.device != dev or not ws.is_contiguous():
-            raise ValueError("workspace: a contiguous tensor on q's device")
-    if ws is None and ws_bytes:
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    ws_given = 0 if ws is None else ws.numel() * ws.element_size()
+    ws, ws_given = _workspace(workspace, int(lib.la_chunk_fwd_workspace(ctypes.byref(desc))), dev)
     check(lib.la_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                            _ptr(S0), _ptr(z0), _ptr(out), _ptr(S_T), _ptr(z_T), _ptr(ws),
                            ws_given, _stream(stream)))
     return out, S_T, z_T
+
+
+def la_chunk_bwd_workspace(desc: LaDesc) -> int:
+    return int(load().la_chunk_bwd_workspace(ctypes.byref(desc)))
+
+
+def la_chunk_bwd(q, k, v, dout, *, variant, gate=None, S0=None, z0=None, dS_T=None, dz_T=None, phi=None,
+                 want_dgate=None, want_dS0=True, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Chunked backward pass of LA_NORMALIZED and LA_RETENTION (C:
+    ``la_chunk_bwd``).  q, k, v, gate, S0, z0 as given to the forward; dout
+    (B,H,T,d_v) in q's dtype; dS_T / dz_T float32 or None (zero).  Returns (dq, dk, dv, dgate,
+    dS0, dz0): dgate (H,) when gate is given (and want_dgate is not False),
+    dS0 / dz0 when want_dS0; None otherwise."""
+    lib = load()
+    dt, d_k, d_v = _check_qkv(q, k, v, "BHT")
+    B, H, T = q.shape[:3]
+    dev, f32 = q.device, torch.float32
+    norm = variant == LA_NORMALIZED
+    _check("gate", gate, (H,), f32, dev)
+    _check("S0", S0, (B, H, d_v, d_k), f32, dev)
+    _check("z0", z0, (B, H, d_k), f32, dev)
+    _check("dout", dout, (B, H, T, d_v), q.dtype, dev)
+    _check("dS_T", dS_T, (B, H, d_v, d_k), f32, dev)
+    _check("dz_T", dz_T, (B, H, d_k), f32, dev)
+    _check("dq", dq, (B, H, T, d_k), q.dtype, dev)
+    _check("dk", dk, (B, H, T, d_k), q.dtype, dev)
+    _check("dv", dv, (B, H, T, d_v), q.dtype, dev)
+    if dout is None:
+        raise ValueError("dout: required")
+    _require_gpu(q)
+    desc = make_desc(variant, dt, B, H, T, d_k, d_v, 0, phi)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    dgate = torch.empty((H,), dtype=f32, device=dev) if gate is not None and want_dgate is not False else None
+    dS0 = torch.empty((B, H, d_v, d_k), dtype=f32, device=dev) if want_dS0 else None
+    dz0 = torch.empty((B, H, d_k), dtype=f32, device=dev) if want_dS0 and norm else None
+    ws, ws_given = _workspace(workspace, int(lib.la_chunk_bwd_workspace(ctypes.byref(desc))), dev)
+    check(lib.la_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(S0), _ptr(z0),
+                           _ptr(dout), _ptr(dS_T), _ptr(dz_T), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(dgate), _ptr(dS0), _ptr(dz0), _ptr(ws), ws_given, _stream(stream)))
+    return dq, dk, dv, dgate, dS0, dz0
 
 
 def la_chunk_fwd_noalloc(q, k, v, *, variant, out, gate=None, beta=None, S0=None, z0=None, chunk=0,

@@ -19,10 +19,11 @@ LA_OK, LA_EINVAL, LA_EUNSUPPORTED, LA_EHIP = 0, 1, 2, 3
 LA_NORMALIZED, LA_GATED, LA_GATED_DELTA, LA_RETENTION, LA_KDA = 0, 1, 2, 3, 4
 LA_F32, LA_BF16 = 0, 1
 LA_PHI_IDENTITY, LA_PHI_ELU1 = 0, 1
-LA_ABI_VERSION = 2
+LA_ABI_VERSION = 3
 
-EXPORTED = ("la_chunk_fwd_workspace", "la_chunk_fwd", "la_chunk_fwd_noalloc", "la_decode_step",
-            "la_verify", "la_commit", "la_status_str", "la_last_error", "la_abi_version")
+EXPORTED = ("la_chunk_fwd_workspace", "la_chunk_fwd", "la_chunk_fwd_noalloc",
+            "la_chunk_bwd_workspace", "la_chunk_bwd", "la_decode_step", "la_verify", "la_commit",
+            "la_status_str", "la_last_error", "la_abi_version")
 LA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
@@ -50,6 +51,10 @@ def load(path: str = LIB_PATH):
     lib.la_chunk_fwd_workspace.restype = sz
     lib.la_chunk_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp, vp, sz, vp]
     lib.la_chunk_fwd.restype = ctypes.c_int
+    lib.la_chunk_bwd_workspace.argtypes = [dp]
+    lib.la_chunk_bwd_workspace.restype = sz
+    lib.la_chunk_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, vp, fp, fp, vp, vp, vp, fp, fp, fp, vp, sz, vp]
+    lib.la_chunk_bwd.restype = ctypes.c_int
     lib.la_chunk_fwd_noalloc.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, fp, fp, vp]
     lib.la_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.la_decode_step.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, vp, vp]

@@ -249,6 +249,82 @@ static la_status chunk_fwd(const la_desc *d, const void *q, const void *k, const
     return LA_OK;
 }
 
+static void bwd_args(const la_desc *d, la::BwdArgs &a) {
+    a = la::BwdArgs{};
+    a.variant = d->variant; a.dtype = d->dtype; a.phi = d->phi;
+    a.B = d->B; a.H = d->H; a.T = d->T; a.d_k = d->d_k; a.d_v = d->d_v;
+}
+
+size_t la_chunk_bwd_workspace(const la_desc *d) {
+    if (check_desc(d, true) != LA_OK) return 0;
+    if (d->variant != LA_NORMALIZED && d->variant != LA_RETENTION) return 0;
+    la::BwdArgs a;
+    bwd_args(d, a);
+    return la::bwd_workspace_bytes(a);
+}
+
+la_status la_chunk_bwd(const la_desc *d, const void *q, const void *k, const void *v, const float *gate,
+                       const float *S0, const float *z0, const void *dout,
+                       const float *dS_T, const float *dz_T, void *dq, void *dk, void *dv, float *dgate,
+                       float *dS0, float *dz0, void *workspace, size_t workspace_bytes, void *stream) {
+    g_last_error[0] = '\0';
+    la_status st = check_desc(d, true);
+    if (st != LA_OK) return st;
+    if (d->variant != LA_NORMALIZED && d->variant != LA_RETENTION)
+        return fail(LA_EUNSUPPORTED, "la_chunk_bwd covers LA_NORMALIZED and LA_RETENTION");
+    const bool norm = d->variant == LA_NORMALIZED;
+    const size_t heads = static_cast<size_t>(d->B) * d->H;
+    const size_t tok = heads * static_cast<size_t>(d->T);
+    if (!norm && (z0 || dz_T || dz0)) return fail(LA_EINVAL, "z0, dz_T and dz0 must be NULL for LA_RETENTION");
+    if (!gate && dgate) return fail(LA_EINVAL, "dgate needs gate (there is no decay to differentiate)");
+    if (tok > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
+        return fail(LA_EINVAL, "q, k, v, dout, dq, dk and dv are required when B*H*T > 0");
+
+    const size_t esz = d->dtype == LA_BF16 ? 2 : 4;
+    const void *ptrs[] = {q, k, v, gate, S0, z0, dout, dS_T, dz_T, dq, dk, dv, dgate, dS0, dz0, workspace};
+    const char *names[] = {"q", "k", "v", "gate", "S0", "z0", "dout", "dS_T", "dz_T",
+                           "dq", "dk", "dv", "dgate", "dS0", "dz0", "workspace"};
+    for (int i = 0; i < 16; ++i) {
+        // gate and dgate are read or written one float at a time
+        const uintptr_t al = (i == 3 || i == 12) ? 4 : 16;
+        if (misaligned(ptrs[i], al)) return fail(LA_EINVAL, "%s is not %d-byte aligned", names[i], (int)al);
+    }
+    la::BwdArgs a;
+    bwd_args(d, a);
+    const size_t need_ws = la::bwd_workspace_bytes(a);
+    if (need_ws > 0 && (!workspace || workspace_bytes < need_ws))
+        return fail(LA_EINVAL, "workspace of %zu bytes required, %zu given", need_ws, workspace ? workspace_bytes : 0);
+
+    const size_t dkk = d->d_k, dvv = d->d_v;
+    const Range r_q = range("q", q, tok * dkk * esz), r_k = range("k", k, tok * dkk * esz);
+    const Range r_v = range("v", v, tok * dvv * esz), r_g = range("gate", gate, static_cast<size_t>(d->H) * 4);
+    const Range r_s0 = range("S0", S0, heads * dvv * dkk * 4), r_z0 = range("z0", z0, heads * dkk * 4);
+    const Range r_do = range("dout", dout, tok * dvv * esz);
+    const Range r_dst = range("dS_T", dS_T, heads * dvv * dkk * 4), r_dzt = range("dz_T", dz_T, heads * dkk * 4);
+    const Range r_dq = range("dq", dq, tok * dkk * esz), r_dk = range("dk", dk, tok * dkk * esz);
+    const Range r_dv = range("dv", dv, tok * dvv * esz), r_dg = range("dgate", dgate, static_cast<size_t>(d->H) * 4);
+    const Range r_ds0 = range("dS0", dS0, heads * dvv * dkk * 4), r_dz0 = range("dz0", dz0, heads * dkk * 4);
+    const Range r_ws = range("workspace", workspace, need_ws);
+    const Range inputs[] = {r_q, r_k, r_v, r_g, r_s0, r_z0, r_do, r_dst, r_dzt};
+    const Range outputs[] = {r_dq, r_dk, r_dv, r_dg, r_ds0, r_dz0, r_ws};
+    for (const Range &o : outputs) {
+        for (const Range &i : inputs)
+            if (overlaps(o, i)) return fail(LA_EINVAL, "%s overlaps %s", o.name, i.name);
+        for (const Range &o2 : outputs)
+            if (&o2 != &o && overlaps(o, o2)) return fail(LA_EINVAL, "%s overlaps %s", o.name, o2.name);
+    }
+    if (heads == 0) return LA_OK;
+
+    a.q = q; a.k = k; a.v = v; a.dout = dout;
+    a.gate = gate; a.S0 = S0; a.z0 = z0; a.dS_T = dS_T; a.dz_T = dz_T;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dgate = dgate; a.dS0 = dS0; a.dz0 = dz0;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = la::launch_chunk_bwd(a);
+    if (e != hipSuccess) return fail(LA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return LA_OK;
+}
+
 la_status la_decode_step(const la_desc *d, const void *q, const void *k, const void *v,
                          const float *gate, const float *beta, float *S, float *z, void *out,
                          void *stream) {

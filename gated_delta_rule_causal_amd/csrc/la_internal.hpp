@@ -37,10 +37,25 @@ struct ChunkArgs {
     hipStream_t stream;
 };
 
+struct BwdArgs {
+    int variant, dtype, phi;
+    int B, H, T, d_k, d_v;
+    const void *q, *k, *v, *dout;
+    const float *gate, *S0, *z0, *dS_T, *dz_T;
+    void *dq, *dk, *dv;
+    float *dgate, *dS0, *dz0;
+    void *workspace;
+    size_t workspace_bytes;
+    hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_chunk(const ChunkArgs &a);
 hipError_t launch_chunk_kda(const ChunkArgs &a);
 size_t chunk_workspace_bytes(const ChunkArgs &a);
 size_t kda_workspace_bytes(const ChunkArgs &a);
+hipError_t launch_chunk_bwd(const BwdArgs &a);
+size_t bwd_workspace_bytes(const BwdArgs &a);
+int bwd_chunk_length(const BwdArgs &a);
 
 }  // namespace la

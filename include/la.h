@@ -79,7 +79,7 @@
 extern "C" {
 #endif
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 
 typedef enum {
     LA_OK = 0,
@@ -173,6 +173,61 @@ la_status la_chunk_fwd(const la_desc *desc,
                        const float *gate, const float *beta,
                        const float *S0, const float *z0,
                        void *out, float *S_T, float *z_T,
+                       void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Bytes of device workspace la_chunk_bwd needs for `desc` (0 for an invalid
+ * descriptor): the state entering and the cotangent leaving every chunk of
+ * every head, float32 (d_k d_v values, plus d_k for LA_NORMALIZED's
+ * normalizer), one float per chunk and, for LA_NORMALIZED, two floats per
+ * token; about 2 x 64.5 KiB per 64-token chunk at d_k = d_v = 128.  The
+ * backward picks its own chunk length (64, or 32 where float32 tiles at
+ * head size 128 do not fit a compute unit's LDS); desc->chunk is ignored.
+ */
+size_t la_chunk_bwd_workspace(const la_desc *desc);
+
+/*
+ * Chunked backward pass (training) of LA_NORMALIZED and LA_RETENTION, with
+ * or without the fixed per-head decay: the gradients of a loss L with
+ * respect to every input of la_chunk_fwd, given its gradients with respect
+ * to the outputs.  The pages name chunkwise training without giving an
+ * algorithm (page "Linear Attention", question on sequential training; page
+ * "Beyond -- Linear attention and recurrent memory", section "The big
+ * idea"); the chunk equations are derived from the recurrence at the top of
+ * this file.  The forward pass is recomputed from the inputs, so nothing of
+ * it needs to be kept: the state entering every chunk (a scan over the
+ * chunks), for LA_NORMALIZED every token's output and denominator in float32
+ * from float32 features (its gradient nearly cancels between the value and
+ * normalizer parts, so the forward's rounded output would not do), then the
+ * cotangent leaving every chunk (a reverse scan), and finally every chunk's
+ * gradients on the matrix cores.  Other variants return LA_EUNSUPPORTED.
+ *
+ *   q, k, v, gate, S0, z0   the forward's inputs, as for la_chunk_fwd (there
+ *         is no beta in these variants).
+ *   dout  dL/dout (B,H,T,d_v) dtype.
+ *   dS_T  dL/dS_T (B,H,d_v,d_k) f32, or NULL for zero.
+ *   dz_T  LA_NORMALIZED: dL/dz_T (B,H,d_k) f32 or NULL for zero; otherwise
+ *         NULL.
+ *   dq, dk (B,H,T,d_k) dtype and dv (B,H,T,d_v) dtype, written.
+ *   dgate dL/dgamma (H,) f32 summed over the batch, written, or NULL; must
+ *         be NULL when gate is NULL.
+ *   dS0   dL/dS0 (B,H,d_v,d_k) f32, written, or NULL.
+ *   dz0   LA_NORMALIZED: dL/dz0 (B,H,d_k) f32, written, or NULL; otherwise
+ *         NULL.
+ *   workspace, workspace_bytes   at least la_chunk_bwd_workspace() bytes of
+ *         caller-owned device memory, 16-byte aligned; contents on entry do
+ *         not matter.
+ * Outputs must not overlap each other, the inputs or the workspace.
+ * Arithmetic is float32 (bf16 operands on the matrix cores for bf16 data,
+ * except where a product feeds a cancellation, as above).
+ */
+la_status la_chunk_bwd(const la_desc *desc,
+                       const void *q, const void *k, const void *v,
+                       const float *gate, const float *S0, const float *z0,
+                       const void *dout, const float *dS_T, const float *dz_T,
+                       void *dq, void *dk, void *dv,
+                       float *dgate, float *dS0, float *dz0,
                        void *workspace, size_t workspace_bytes,
                        void *stream);
 

@@ -330,3 +330,83 @@ def test_verify_commit_reject(lib, which, name, desc, kw, msg):
 def test_verify_commit_empty_is_a_no_op(lib):
     assert call_verify(lib, D(T=0), q=None, k=None, v=None, out=None, S=None, gate=None, beta=None) == la.LA_OK
     assert call_commit(lib, D(B=0, T=4), k=None, v=None, S=None, gate=None, beta=None, accepted=None) == la.LA_OK
+
+
+# ------------------------------------------------------- backward (training)
+
+def call_bwd(lib, desc, **kw):
+    norm = desc.variant == la.LA_NORMALIZED
+    args = dict(q=fake(0), k=fake(1), v=fake(2), gate=fake(5), S0=None, z0=None, dout=fake(7), dS_T=None,
+                dz_T=None, dq=fake(10), dk=fake(11), dv=fake(12), dgate=fake(13), dS0=fake(14),
+                dz0=fake(15) if norm else None, ws=fake(20), ws_bytes=1 << 30)
+    args.update(kw)
+    return lib.la_chunk_bwd(ctypes.byref(desc), args["q"], args["k"], args["v"], args["gate"], args["S0"],
+                            args["z0"], args["dout"], args["dS_T"], args["dz_T"],
+                            args["dq"], args["dk"], args["dv"], args["dgate"], args["dS0"], args["dz0"],
+                            args["ws"], args["ws_bytes"], None)
+
+
+BWD_CASES = [
+    ("gated_unsupported", D(la.LA_GATED), {}, la.LA_EUNSUPPORTED, "LA_NORMALIZED and LA_RETENTION"),
+    ("delta_unsupported", D(), {}, la.LA_EUNSUPPORTED, "LA_NORMALIZED and LA_RETENTION"),
+    ("kda_unsupported", D(la.LA_KDA), {}, la.LA_EUNSUPPORTED, "LA_NORMALIZED and LA_RETENTION"),
+    ("z0_on_retention", D(la.LA_RETENTION), {"z0": fake(8)}, la.LA_EINVAL, "must be NULL"),
+    ("dz_T_on_retention", D(la.LA_RETENTION), {"dz_T": fake(8)}, la.LA_EINVAL, "must be NULL"),
+    ("dz0_on_retention", D(la.LA_RETENTION), {"dz0": fake(15)}, la.LA_EINVAL, "must be NULL"),
+    ("misaligned_gate", D(la.LA_NORMALIZED), {"gate": fake(5, 2)}, la.LA_EINVAL, "aligned"),
+    ("dS0_overlaps_dS_T", D(la.LA_NORMALIZED), {"dS_T": fake(14, 256)}, la.LA_EINVAL, "overlaps"),
+    ("dgate_without_gate", D(la.LA_RETENTION), {"gate": None}, la.LA_EINVAL, "dgate needs gate"),
+    ("missing_dout", D(la.LA_RETENTION), {"dout": None}, la.LA_EINVAL, "required"),
+    ("missing_dq", D(la.LA_NORMALIZED), {"dq": None}, la.LA_EINVAL, "required"),
+    ("small_workspace", D(la.LA_RETENTION), {"ws_bytes": 1024}, la.LA_EINVAL, "workspace"),
+    ("missing_workspace", D(la.LA_NORMALIZED), {"ws": None}, la.LA_EINVAL, "workspace"),
+    ("misaligned_dq", D(la.LA_NORMALIZED), {"dq": fake(10, 8)}, la.LA_EINVAL, "aligned"),
+    ("dq_overlaps_q", D(la.LA_RETENTION), {"dq": fake(0, 512)}, la.LA_EINVAL, "overlaps"),
+    ("dv_overlaps_dk", D(la.LA_RETENTION), {"dv": fake(11, 256)}, la.LA_EINVAL, "overlaps"),
+    ("dS0_overlaps_workspace", D(la.LA_RETENTION), {"dS0": fake(20, 4096)}, la.LA_EINVAL, "overlaps"),
+    ("unsupported_dk", D(la.LA_RETENTION, d_k=24), {}, la.LA_EUNSUPPORTED, "head sizes"),
+]
+
+
+@pytest.mark.parametrize("name,desc,kw,status,msg", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_chunk_bwd_rejects(lib, name, desc, kw, status, msg):
+    assert call_bwd(lib, desc, **kw) == status
+    assert msg in la.la_last_error()
+
+
+def test_chunk_bwd_empty_is_a_no_op(lib):
+    d = D(la.LA_RETENTION, B=0)
+    assert call_bwd(lib, d, q=None, k=None, v=None, dout=None, dq=None, dk=None, dv=None, ws=None,
+                    ws_bytes=0) == la.LA_OK
+
+
+def test_chunk_bwd_workspace_sizes(lib):
+    # states and cotangents of every chunk, float32, one float per chunk, and
+    # (normalized) two floats per token
+    def ws(variant, B, H, T, dk, dv, C):
+        N = (T + C - 1) // C
+        norm = variant == la.LA_NORMALIZED
+        E = dk * dv + (dk if norm else 0)
+        b = (2 * B * H * N * E + B * H * N + (2 * B * H * T if norm else 0)) * 4
+        return (b + 255) // 256 * 256
+    for v in (la.LA_NORMALIZED, la.LA_RETENTION):
+        assert la.la_chunk_bwd_workspace(D(v, B=4, H=8, T=2048)) == ws(v, 4, 8, 2048, 64, 64, 64)
+        assert la.la_chunk_bwd_workspace(D(v, B=1, H=2, T=65, d_k=16, d_v=32)) == ws(v, 1, 2, 65, 16, 32, 64)
+        # float32 tiles at head size 128 run 32-token chunks
+        assert la.la_chunk_bwd_workspace(D(v, dtype=la.LA_F32, B=1, H=1, T=100, d_k=128, d_v=128)) == \
+            ws(v, 1, 1, 100, 128, 128, 32)
+        assert la.la_chunk_bwd_workspace(D(v, T=0)) == 0
+    assert la.la_chunk_bwd_workspace(D(la.LA_GATED)) == 0
+
+
+def test_binding_rejects_mismatched_bwd_args():
+    q = k = dout = __import__("torch").zeros((2, 3, 10, 16))
+    v = __import__("torch").zeros((2, 3, 10, 8))
+    with pytest.raises(ValueError, match="gate"):
+        la.la_chunk_bwd(q, k, v, __import__("torch").zeros((2, 3, 10, 8)), variant=la.LA_RETENTION,
+                        gate=__import__("torch").zeros((2,)))
+    with pytest.raises(ValueError, match="dout"):
+        la.la_chunk_bwd(q, k, v, dout, variant=la.LA_RETENTION)
+    with pytest.raises(ValueError, match="dS_T"):
+        la.la_chunk_bwd(q, k, v, __import__("torch").zeros((2, 3, 10, 8)), variant=la.LA_NORMALIZED,
+                        dS_T=__import__("torch").zeros((2, 3, 16, 8)))

@@ -188,6 +188,26 @@ def chunk_inputs(w: Workload, seed: int | None = None, *, T: int | None = None,
     return out
 
 
+def backward_cotangents(w: Workload, seed: int | None = None, *, T: int | None = None,
+                        B: int | None = None, H: int | None = None, state: bool = True) -> dict:
+    """Gradients of a loss with respect to a forward call's outputs, as
+    HostTensors, for the backward pass: dout (B,H,T,d_v) ~ N(0, 1) in the
+    workload's dtype, and (state=True) dS_T (B,H,d_v,d_k) ~ N(0, 1) f32 and,
+    for the normalized variant, dz_T (B,H,d_k) ~ N(0, 1) f32.  Drawn from
+    default_rng([seed, 2**30 + 3]), independent of chunk_inputs."""
+    seed = w.seed if seed is None else seed
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    rng = np.random.default_rng([seed, (1 << 30) + 3])
+    out = {"dout": _store(_normal(rng, (B, H, T, w.d_v)), w.dtype)}
+    if state:
+        out["dS_T"] = _store(_normal(rng, (B, H, w.d_v, w.d_k)), "f32")
+        if w.variant == NORMALIZED:
+            out["dz_T"] = _store(_normal(rng, (B, H, w.d_k)), "f32")
+    return out
+
+
 def decode_state(w: Workload, seed: int | None = None, *, B=None, H=None) -> HostTensor:
     """Initial state S0 ~ N(0, S0_std) of a decode workload, (B,H,d_v,d_k) f32."""
     seed = w.seed if seed is None else seed
