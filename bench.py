@@ -8,7 +8,9 @@ B=4, H=16, T=8192, d_k=d_v=128, bf16 q/k/v, fp32 gates and state, chunk 64
 (``la_chunk_fwd``, a single kernel launch).  The decode half of the metric,
 one recurrent step of the same rule over B=256 x H=16 heads of fp32 128x128
 state (``la_decode_step``), is timed in the same run and reported under
-"decode".  Inputs are seeded synthetic data, resident in GPU memory before
+"decode", and the chunked backward pass (``la_chunk_bwd``) of normalized
+attention with a per-head decay and of retention at a training shape under
+"backward".  Inputs are seeded synthetic data, resident in GPU memory before
 timing starts.  Prints ONE JSON line.
 
 Roofline figures use algorithmic counts: bytes the operator must move
@@ -76,6 +78,20 @@ def linear_chunk_bytes(B, H, T, d_k, d_v, io_bytes, gated, normalized):
     b = tok * ((2 * d_k + 2 * d_v) * io_bytes + (d_k * 4 if gated else 0))
     b += B * H * (d_v * d_k + (d_k if normalized else 0)) * 4
     return b
+
+
+def bwd_bytes(B, H, T, d_k, d_v, io_bytes):
+    """Bytes the backward must move: q, k, v and dout read once, dq, dk, dv
+    written once (io dtype)."""
+    return B * H * T * ((2 * d_k + 2 * d_v) + (2 * d_k + d_v)) * io_bytes
+
+
+def bwd_flops_per_token_head(d_k, d_v, C):
+    """Matrix flops of the chunked backward per token and head: per chunk the
+    scores phiQ phiK^T and dO V^T, G phiK, G^T phiQ and A^T dO
+    (2 C^2 (3 d_k + 2 d_v)), the state terms of dq, dk, dv and the two state
+    increments (5 x 2 C d_k d_v); divided by C."""
+    return 2 * C * (3 * d_k + 2 * d_v) + 10 * d_k * d_v
 
 
 def decode_bytes(B, H, d_k, d_v, io_bytes=2):
@@ -323,6 +339,38 @@ def main(argv=None):
     dbytesc = decode_bytes(Bc, wd.H, wd.d_k, wd.d_v)
     del Sc, poolc
 
+    # ---------------- backward pass (training)
+    backward = []
+    for name, wb in wl.BWD_WORKLOADS.items():
+        ib = wl.chunk_inputs(wb, head_decay=True)
+        cb = wl.backward_cotangents(wb, state=False)
+        db = {k: to_dev(v) for k, v in ib.items()}
+        dout = to_dev(cb["dout"])
+        descb = la.make_desc(wb.variant, la.LA_BF16 if wb.dtype == "bf16" else la.LA_F32, wb.B, wb.H, wb.T, wb.d_k,
+                             wb.d_v, 0, wb.phi_kind)
+        wsb = torch.empty(la.la_chunk_bwd_workspace(descb), dtype=torch.uint8, device="cuda")
+        grads = [torch.empty_like(db["q"]), torch.empty_like(db["k"]), torch.empty_like(db["v"])]
+
+        def bwd_step():
+            la.la_chunk_bwd(db["q"], db["k"], db["v"], dout, variant=wb.variant, gate=db.get("gate"),
+                            phi=wb.phi_kind, dq=grads[0], dk=grads[1], dv=grads[2], workspace=wsb)
+
+        bwall, bms, _ = time_launches(bwd_step, max(5, args.steps // 2), 3, stream)
+        if not all(bool(torch.isfinite(g).all()) for g in grads):
+            print("non-finite gradient", file=sys.stderr)
+            return 1
+        iob = 2 if wb.dtype == "bf16" else 4
+        bb = bwd_bytes(wb.B, wb.H, wb.T, wb.d_k, wb.d_v, iob)
+        bf = bwd_flops_per_token_head(wb.d_k, wb.d_v, wb.chunk) * wb.B * wb.H * wb.T
+        backward.append({"workload": name, "variant": "normalized_linear_attention" if wb.variant == la.LA_NORMALIZED
+                         else "retention", "entry": "la_chunk_bwd", "avg_call_ms": bms,
+                         "tokens_per_s": wb.B * wb.T / (bms * 1e-3), "workspace_bytes": wsb.numel(),
+                         "algorithmic_bytes": bb, "hbm_gbs": bb / (bms * 1e-3) / 1e9,
+                         "hbm_frac": bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_flops": bf,
+                         "tflops": bf / (bms * 1e-3) / 1e12,
+                         "mfma_frac": bf / (bms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS})
+        del db, dout, wsb, grads
+
     peaks = None if args.no_probes else measured_peaks(stream)
     if args.copy_bytes > 0:
         # one probe copy of a known size, for calibrating the traffic counters
@@ -357,6 +405,7 @@ def main(argv=None):
                                     "achieved_gbs": dbytesc / (dmsc * 1e-3) / 1e9,
                                     "frac": dbytesc / (dmsc * 1e-3) / 1e9 / HBM_PEAK_GBS}},
     }
+    result["backward"] = backward
     if peaks is not None:
         peaks["chunk_hbm_frac_of_measured"] = gbs / peaks["hbm_copy_gbs"]
         peaks["chunk_mfma_frac_of_measured"] = tflops / peaks["bf16_mfma_tflops"] if w.dtype == "bf16" else None

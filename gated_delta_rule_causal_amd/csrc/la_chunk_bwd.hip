@@ -153,8 +153,12 @@ struct BwdLds {
     static constexpr int LDK = DK + PAD, LDV = DV + PAD, LDC = C + PAD;
     static constexpr int F_FLOATS = (C + 1) + 2 * C + 2 * DK + 16;   // powers, 1/den, dden, z, dz, reduction
     static constexpr int SPLIT_ELEMS = split_operands<DT, NORM>() ? C * LDK + C * LDC : 0;   // low parts of phiK, G
+    // retention with bf16 data: the entering state as an LDS operand tile
+    static constexpr bool STAGE_S = !NORM && sizeof(Op) == 2;
+    static constexpr int STATE_ELEMS = STAGE_S ? DK * LDV : 0;
     static constexpr int GRAD_BYTES =
-        (2 * C * LDK + 2 * C * LDV + 2 * C * LDC + DK * LDV + SPLIT_ELEMS) * static_cast<int>(sizeof(Op)) +
+        (2 * C * LDK + 2 * C * LDV + 2 * C * LDC + DK * LDV + SPLIT_ELEMS + STATE_ELEMS) *
+            static_cast<int>(sizeof(Op)) +
         F_FLOATS * 4;
 };
 
@@ -523,7 +527,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
     typedef typename OpOf<DT>::type Op;
     typedef Group<Op> Gp;
     typedef BwdLds<DT, DK, DV, C, NORM> L;
-    constexpr bool SPLIT = split_operands<DT, NORM>();
+    constexpr bool SPLIT = split_operands<DT, NORM>(), STAGE_S = L::STAGE_S;
     constexpr int NTHR = kBwdWaves * 64, NB = C / 16, NCB = DK / 16, NIB = DV / 16;
     constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC;
     static_assert(L::GRAD_BYTES <= 160 * 1024, "LDS budget");
@@ -536,6 +540,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
     __shared__ __align__(16) Op sdS[DK * LDV];  // cotangent leaving the chunk, [key][value]
     __shared__ __align__(16) Op sKl[SPLIT ? C * LDK : 8];   // low parts of phi(k) and of G
     __shared__ __align__(16) Op sGl[SPLIT ? C * LDC : 8];
+    __shared__ __align__(16) Op sS[STAGE_S ? DK * LDV : 8];   // retention, bf16: the entering state, [key][value]
     __shared__ float sPow[C + 1], sInv[C], sDd[C], sZ[DK], sdZ[DK], sRed[16];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -577,9 +582,10 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
             const float4 d = *reinterpret_cast<const float4 *>(sr + e);
             const int c = e / DV, i = e % DV;
             st_group(sdS + c * LDV + i, Gp::make(d.x, d.y, d.z, d.w));
-            if (want_dg) {
+            if (STAGE_S || want_dg) {
                 const float4 s = *reinterpret_cast<const float4 *>(sf + e);
-                dl += wf * (d.x * s.x + d.y * s.y + d.z * s.z + d.w * s.w);
+                if constexpr (STAGE_S) st_group(sS + c * LDV + i, Gp::make(s.x, s.y, s.z, s.w));
+                if (want_dg) dl += wf * (d.x * s.x + d.y * s.y + d.z * s.z + d.w * s.w);
             }
         }
         if (norm)
@@ -659,15 +665,25 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
                 }
             }
         }
-        // the entering state: S'_c (key-major rows, float32 in the workspace)
-        // times dO_t, on the float32 matrix cores (it nearly cancels against
-        // the normalizer term below)
-        const float *srow = sf + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
+        if constexpr (!STAGE_S) {
+            // the entering state: S'_c (key-major rows, float32 in the
+            // workspace) times dO_t, on the float32 matrix cores (normalized:
+            // it nearly cancels against the normalizer term below)
+            const float *srow = sf + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
 #pragma unroll
-        for (int i0 = 0; i0 < DV; i0 += 16) {
-            float o4[4];
-            Gp::unpack(ld_group(sO + t * LDV + i0 + 4 * lg), o4);
-            mma16(xs, *reinterpret_cast<const float4 *>(srow + i0), make_float4(o4[0], o4[1], o4[2], o4[3]));
+            for (int i0 = 0; i0 < DV; i0 += 16) {
+                float o4[4];
+                Gp::unpack(ld_group(sO + t * LDV + i0 + 4 * lg), o4);
+                mma16(xs, *reinterpret_cast<const float4 *>(srow + i0), make_float4(o4[0], o4[1], o4[2], o4[3]));
+            }
+        } else {
+            // retention, bf16: S_c rows from LDS times dO_t
+            const Op *srow = sS + (16 * cb + lr) * LDV + 4 * lg;
+            const Op *orow = sO + t * LDV + 4 * lg;
+#pragma unroll
+            for (int i0 = 0; i0 + 32 <= DV; i0 += 32)
+                mma32(xs, ld_group(srow + i0), ld_group(srow + i0 + 16), ld_group(orow + i0), ld_group(orow + i0 + 16));
+            if constexpr (DV % 32 == 16) mma16(xs, ld_group(srow + DV - 16), ld_group(orow + DV - 16));
         }
         if (t < n) {
             const int c0 = 16 * cb + 4 * lg;
@@ -699,16 +715,25 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
             else if (I < NB)
                 mma16(acc, kt_group<0>(sQ, LDK, 16 * I, 16 * cb, lane), kt_group<0>(sG, LDC, 16 * I, 16 * J, lane));
         }
-        // the leaving cotangent: dS'_{c+1} rows (key-major, float32 in the
-        // workspace) times v_j, on the float32 matrix cores (it nearly cancels
-        // against dz below)
-        const float *drow = sr + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
         const Op *vrow = sV + j * LDV + 4 * lg;
+        if constexpr (!STAGE_S) {
+            // the leaving cotangent: dS'_{c+1} rows (key-major, float32 in the
+            // workspace) times v_j, on the float32 matrix cores (normalized:
+            // it nearly cancels against dz below)
+            const float *drow = sr + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
 #pragma unroll
-        for (int i0 = 0; i0 < DV; i0 += 16) {
-            float v4[4];
-            Gp::unpack(ld_group(vrow + i0), v4);
-            mma16(ys, *reinterpret_cast<const float4 *>(drow + i0), make_float4(v4[0], v4[1], v4[2], v4[3]));
+            for (int i0 = 0; i0 < DV; i0 += 16) {
+                float v4[4];
+                Gp::unpack(ld_group(vrow + i0), v4);
+                mma16(ys, *reinterpret_cast<const float4 *>(drow + i0), make_float4(v4[0], v4[1], v4[2], v4[3]));
+            }
+        } else {
+            // retention, bf16: dS_{c+1} rows from LDS times v_j
+            const Op *drow = sdS + (16 * cb + lr) * LDV + 4 * lg;
+#pragma unroll
+            for (int i0 = 0; i0 + 32 <= DV; i0 += 32)
+                mma32(ys, ld_group(drow + i0), ld_group(drow + i0 + 16), ld_group(vrow + i0), ld_group(vrow + i0 + 16));
+            if constexpr (DV % 32 == 16) mma16(ys, ld_group(drow + DV - 16), ld_group(vrow + DV - 16));
         }
         if (j < n) {
             const int c0 = 16 * cb + 4 * lg;

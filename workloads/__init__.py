@@ -145,6 +145,18 @@ EXTRA_WORKLOADS = {
         "ret_bf16_b4h8t2048d64", RETENTION, "bf16", 4, 8, 2048, 64, 64, 64, 64 ** -0.5, gate_mean=3.0, seed=7),
 }
 
+# Training (backward-pass) workloads: the normalized configuration with a
+# fixed per-head decay sigmoid(N(3, 1)) (drawn with head_decay=True), and
+# retention at the delta rule's training shape; the loss gradient dout comes
+# from backward_cotangents.
+BWD_WORKLOADS = {
+    "la_decay_bf16_b4h8t2048d64": Workload(
+        "la_decay_bf16_b4h8t2048d64", NORMALIZED, "bf16", 4, 8, 2048, 64, 64, 64, 64 ** -0.5, gate_mean=3.0, seed=2),
+    "ret_bf16_b4h16t8192d128": Workload(
+        "ret_bf16_b4h16t8192d128", RETENTION, "bf16", 4, 16, 8192, 128, 128, 64, 128 ** -0.5, gate_mean=4.0, seed=8,
+        phi=0),
+}
+
 
 def chunk_inputs(w: Workload, seed: int | None = None, *, T: int | None = None,
                  B: int | None = None, H: int | None = None,
