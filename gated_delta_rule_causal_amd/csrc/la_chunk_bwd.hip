@@ -100,48 +100,51 @@ __device__ __forceinline__ void store4(bf16_t *p, const float (&x)[4]) {
     *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
 }
 
-// Stage rows [0, n) of a C x D token-major tile (global rows D elements
-// apart) into LDS rows `ld` apart as the operand type, element x of row t
-// becoming f(t, x); rows [n, C) are zero (a padded token carries no
-// feature: phi(0) would be 1).
-template <int C, int D, int NTHR, class IO, class Op, class F>
-__device__ __forceinline__ void stage_tile(Op *dst, int ld, const IO *src, int n, int tid, F f) {
-    constexpr int VE = 16 / sizeof(IO);
-    constexpr int VPR = D / VE;
-    for (int e = tid; e < C * VPR; e += NTHR) {
-        const int t = e / VPR, c = (e % VPR) * VE;
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (t < n) load16(src + static_cast<size_t>(t) * D + c, x);
-#pragma unroll
-        for (int j = 0; j < VE; ++j) x[j] = t < n ? f(t, x[j]) : 0.f;
-#pragma unroll
-        for (int j = 0; j < VE; j += 4) st_group(dst + t * ld + c + j, Group<Op>::make(x[j], x[j + 1], x[j + 2], x[j + 3]));
-    }
+// one staged 16-byte vector as floats (4 float32 or 8 bf16)
+__device__ __forceinline__ void unpack16(const uint4 &w, float (&x)[8], float) {
+    x[0] = __uint_as_float(w.x); x[1] = __uint_as_float(w.y); x[2] = __uint_as_float(w.z); x[3] = __uint_as_float(w.w);
+}
+__device__ __forceinline__ void unpack16(const uint4 &w, float (&x)[8], bf16_t) {
+    x[0] = lo_bf16(w.x); x[1] = hi_bf16(w.x); x[2] = lo_bf16(w.y); x[3] = hi_bf16(w.y);
+    x[4] = lo_bf16(w.z); x[5] = hi_bf16(w.z); x[6] = lo_bf16(w.w); x[7] = hi_bf16(w.w);
 }
 
-// bf16 operands of the normalized variant's cancelling products carry a low
-// part as well (x = hi + lo, both bf16, about 16 significant bits)
-// stage_tile into a high and a low operand part: hi = Op(f), lo = Op(f - hi)
-template <int C, int D, int NTHR, class IO, class Op, class F>
-__device__ __forceinline__ void stage_tile_split(Op *hi, Op *lo, int ld, const IO *src, int n, int tid, F f) {
-    constexpr int VE = 16 / sizeof(IO);
-    constexpr int VPR = D / VE;
-    for (int e = tid; e < C * VPR; e += NTHR) {
-        const int t = e / VPR, c = (e % VPR) * VE;
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (t < n) load16(src + static_cast<size_t>(t) * D + c, x);
+// Commit a tile staged in registers (TilePrefetch: every global load of the
+// tile issued at once) to LDS rows `ld` apart as the operand type, element x
+// of row t becoming f(t, x); rows the staging marked invalid (past the
+// chunk's tokens: a padded token carries no feature, phi(0) would be 1)
+// become zero.  With `lo`, also the low operand part Op(f - Op(f)).
+template <int NTHR, class TP, class Op, class F>
+__device__ __forceinline__ void commit_tile(const TP &tp, Op *dst, Op *lo, int ld, int tid, F f) {
+    typedef Group<Op> Gp;
 #pragma unroll
-        for (int j = 0; j < VE; ++j) x[j] = t < n ? f(t, x[j]) : 0.f;
+    for (int i = 0; i < TP::PER; ++i) {
+        const int e = tid + i * NTHR;
+        if (TP::TOTAL % NTHR != 0 && e >= TP::TOTAL) continue;
+        const int t = e / TP::VPR, c = (e % TP::VPR) * TP::VE;
+        float x[8];
+        unpack16(tp.r[i], x, decltype(tp.tag){});
+        const bool ok = (tp.valid >> i) & 1u;
 #pragma unroll
-        for (int j = 0; j < VE; j += 4) {
-            const typename Group<Op>::type h = Group<Op>::make(x[j], x[j + 1], x[j + 2], x[j + 3]);
-            float r[4];
-            Group<Op>::unpack(h, r);
-            st_group(hi + t * ld + c + j, h);
-            st_group(lo + t * ld + c + j, Group<Op>::make(x[j] - r[0], x[j + 1] - r[1], x[j + 2] - r[2], x[j + 3] - r[3]));
+        for (int j = 0; j < TP::VE; ++j) x[j] = ok ? f(t, x[j]) : 0.f;
+#pragma unroll
+        for (int j = 0; j < TP::VE; j += 4) {
+            const typename Gp::type h = Gp::make(x[j], x[j + 1], x[j + 2], x[j + 3]);
+            st_group(dst + t * ld + c + j, h);
+            if (lo) {
+                float r[4];
+                Gp::unpack(h, r);
+                st_group(lo + t * ld + c + j, Gp::make(x[j] - r[0], x[j + 1] - r[1], x[j + 2] - r[2], x[j + 3] - r[3]));
+            }
         }
     }
 }
+
+// TilePrefetch with its element type visible to commit_tile
+template <int R, int D, int NTHR, class E>
+struct Staged : TilePrefetch<R, D, NTHR, E> {
+    E tag;
+};
 
 template <class DT, bool NORM>
 constexpr bool split_operands() { return NORM && sizeof(typename OpOf<DT>::type) == 2; }
@@ -220,20 +223,24 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_increments_kernel(const Bw
     const float l2g = head_l2g(p, bh);
     const bool elu = p.elu;
 
-    auto kw = [&](int t, float x) { return phi_rt(x, elu) * __builtin_amdgcn_exp2f(static_cast<float>(n - 1 - t) * l2g); };
-    auto qw = [&](int t, float x) { return phi_rt(x, elu) * __builtin_amdgcn_exp2f(static_cast<float>(t + 1) * l2g); };
-    if constexpr (SPLIT)
-        stage_tile_split<C, DK, NTHR>(sK, sKl, LDK, static_cast<const IO *>(p.k) + tok0 * DK, n, tid, kw);
-    else
-        stage_tile<C, DK, NTHR>(sK, LDK, static_cast<const IO *>(p.k) + tok0 * DK, n, tid, kw);
-    stage_tile<C, DV, NTHR>(sV, LDV, static_cast<const IO *>(p.v) + tok0 * DV, n, tid, [](int, float x) { return x; });
+    // every global load of the chunk first, then the LDS commits
+    Staged<C, DK, NTHR, IO> pk, pq;
+    Staged<C, DV, NTHR, IO> pv, po;
+    pk.load(static_cast<const IO *>(p.k) + tok0 * DK, DK, n, tid);
+    pv.load(static_cast<const IO *>(p.v) + tok0 * DV, DV, n, tid);
     if constexpr (REV) {
-        if constexpr (SPLIT)
-            stage_tile_split<C, DK, NTHR>(sQ, sQl, LDK, static_cast<const IO *>(p.q) + tok0 * DK, n, tid, qw);
-        else
-            stage_tile<C, DK, NTHR>(sQ, LDK, static_cast<const IO *>(p.q) + tok0 * DK, n, tid, qw);
-        stage_tile<C, DV, NTHR>(sO, LDV, static_cast<const IO *>(p.dout) + tok0 * DV, n, tid,
-                                [](int, float x) { return x; });
+        pq.load(static_cast<const IO *>(p.q) + tok0 * DK, DK, n, tid);
+        po.load(static_cast<const IO *>(p.dout) + tok0 * DV, DV, n, tid);
+    }
+    commit_tile<NTHR>(pk, sK, SPLIT ? sKl : static_cast<Op *>(nullptr), LDK, tid, [&](int t, float x) {
+        return phi_rt(x, elu) * __builtin_amdgcn_exp2f(static_cast<float>(n - 1 - t) * l2g);
+    });
+    commit_tile<NTHR>(pv, sV, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+    if constexpr (REV) {
+        commit_tile<NTHR>(pq, sQ, SPLIT ? sQl : static_cast<Op *>(nullptr), LDK, tid, [&](int t, float x) {
+            return phi_rt(x, elu) * __builtin_amdgcn_exp2f(static_cast<float>(t + 1) * l2g);
+        });
+        commit_tile<NTHR>(po, sO, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
     }
     __syncthreads();
 
@@ -317,27 +324,18 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_normalizer_kernel(const Bw
     for (int e = tid; e <= C; e += NTHR) sPow[e] = __builtin_amdgcn_exp2f(static_cast<float>(e) * l2g);
     for (int c = tid; c < DK; c += NTHR) sZ[c] = sf[static_cast<size_t>(DK) * DV + c];
     {
-        // float32 features, four channels per lane step; padded tokens zero
-        const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
-        const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
-        for (int e = tid; e < C * (DK / 4); e += NTHR) {
-            const int t = e / (DK / 4), c = (e % (DK / 4)) * 4;
-            float xq[4] = {0.f, 0.f, 0.f, 0.f}, xk[4] = {0.f, 0.f, 0.f, 0.f};
-            if (t < n) {
-                load4(qh + static_cast<size_t>(t) * DK + c, xq);
-                load4(kh + static_cast<size_t>(t) * DK + c, xk);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xq[i] = phi_rt(xq[i], elu);
-                    xk[i] = phi_rt(xk[i], elu);
-                }
-            }
-            *reinterpret_cast<float4 *>(fQ + t * LFK + c) = make_float4(xq[0], xq[1], xq[2], xq[3]);
-            *reinterpret_cast<float4 *>(fK + t * LFK + c) = make_float4(xk[0], xk[1], xk[2], xk[3]);
-        }
+        // every global load of the chunk first; float32 features, padded tokens zero
+        Staged<C, DK, NTHR, IO> pq, pk;
+        Staged<C, DV, NTHR, IO> pv, po;
+        pq.load(static_cast<const IO *>(p.q) + tok0 * DK, DK, n, tid);
+        pk.load(static_cast<const IO *>(p.k) + tok0 * DK, DK, n, tid);
+        pv.load(static_cast<const IO *>(p.v) + tok0 * DV, DV, n, tid);
+        po.load(static_cast<const IO *>(p.dout) + tok0 * DV, DV, n, tid);
+        commit_tile<NTHR>(pq, fQ, static_cast<float *>(nullptr), LFK, tid, [&](int, float x) { return phi_rt(x, elu); });
+        commit_tile<NTHR>(pk, fK, static_cast<float *>(nullptr), LFK, tid, [&](int, float x) { return phi_rt(x, elu); });
+        commit_tile<NTHR>(pv, sV, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+        commit_tile<NTHR>(po, sO, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
     }
-    stage_tile<C, DV, NTHR>(sV, LDV, static_cast<const IO *>(p.v) + tok0 * DV, n, tid, [](int, float x) { return x; });
-    stage_tile<C, DV, NTHR>(sO, LDV, static_cast<const IO *>(p.dout) + tok0 * DV, n, tid, [](int, float x) { return x; });
     __syncthreads();
 
     // scores on the float32 matrix cores; a lane holds four keys j of query t
@@ -565,27 +563,39 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
             sInv[t] = t < n ? p.tok[2 * (tok0 + t)] : 0.f;
             sDd[t] = t < n ? p.tok[2 * (tok0 + t) + 1] : 0.f;
         }
-    // dO as it is: 1/den_t is applied in float32 to the products (the value
-    // and normalizer parts of the normalized gradient nearly cancel)
-    stage_tile<C, DK, NTHR>(sQ, LDK, qh, n, tid, [&](int, float x) { return phi_rt(x, elu); });
-    if constexpr (SPLIT)
-        stage_tile_split<C, DK, NTHR>(sK, sKl, LDK, kh, n, tid, [&](int, float x) { return phi_rt(x, elu); });
-    else
-        stage_tile<C, DK, NTHR>(sK, LDK, kh, n, tid, [&](int, float x) { return phi_rt(x, elu); });
-    stage_tile<C, DV, NTHR>(sV, LDV, static_cast<const IO *>(p.v) + tok0 * DV, n, tid, [](int, float x) { return x; });
-    stage_tile<C, DV, NTHR>(sO, LDV, static_cast<const IO *>(p.dout) + tok0 * DV, n, tid, [](int, float x) { return x; });
     {
-        // the cotangent as an operand tile; the state-coupling term
-        // n gamma^n <dS'_{c+1}, S'_c> from the float32 values
-        const float wf = static_cast<float>(n) * __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g);
-        for (int e = 4 * tid; e < DK * DV; e += 4 * NTHR) {
-            const float4 d = *reinterpret_cast<const float4 *>(sr + e);
-            const int c = e / DV, i = e % DV;
-            st_group(sdS + c * LDV + i, Gp::make(d.x, d.y, d.z, d.w));
-            if (STAGE_S || want_dg) {
-                const float4 s = *reinterpret_cast<const float4 *>(sf + e);
-                if constexpr (STAGE_S) st_group(sS + c * LDV + i, Gp::make(s.x, s.y, s.z, s.w));
-                if (want_dg) dl += wf * (d.x * s.x + d.y * s.y + d.z * s.z + d.w * s.w);
+        // every global load of the chunk first (inputs, and the float32
+        // state and cotangent rows), then the LDS commits.  dO goes in as it
+        // is: 1/den_t is applied in float32 to the products (the value and
+        // normalizer parts of the normalized gradient nearly cancel).
+        Staged<C, DK, NTHR, IO> pq, pk;
+        Staged<C, DV, NTHR, IO> pv, po;
+        Staged<DK, DV, NTHR, float> pd, ps;
+        pq.load(qh, DK, n, tid);
+        pk.load(kh, DK, n, tid);
+        pv.load(static_cast<const IO *>(p.v) + tok0 * DV, DV, n, tid);
+        po.load(static_cast<const IO *>(p.dout) + tok0 * DV, DV, n, tid);
+        pd.load(sr, DV, DK, tid);
+        const bool need_s = STAGE_S || want_dg;
+        if (need_s) ps.load(sf, DV, DK, tid);
+        commit_tile<NTHR>(pq, sQ, static_cast<Op *>(nullptr), LDK, tid, [&](int, float x) { return phi_rt(x, elu); });
+        commit_tile<NTHR>(pk, sK, SPLIT ? sKl : static_cast<Op *>(nullptr), LDK, tid,
+                          [&](int, float x) { return phi_rt(x, elu); });
+        commit_tile<NTHR>(pv, sV, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+        commit_tile<NTHR>(po, sO, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+        commit_tile<NTHR>(pd, sdS, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+        if (need_s) {
+            if constexpr (STAGE_S) commit_tile<NTHR>(ps, sS, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+            if (want_dg) {
+                // the state-coupling term n gamma^n <dS'_{c+1}, S'_c>, float32
+                const float wf = static_cast<float>(n) * __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g);
+#pragma unroll
+                for (int i = 0; i < pd.PER; ++i) {
+                    if (!((pd.valid >> i) & 1u)) continue;   // lanes past the tile re-read its last vector
+                    const uint4 a4 = pd.r[i], b4 = ps.r[i];
+                    dl += wf * (__uint_as_float(a4.x) * __uint_as_float(b4.x) + __uint_as_float(a4.y) * __uint_as_float(b4.y) +
+                                __uint_as_float(a4.z) * __uint_as_float(b4.z) + __uint_as_float(a4.w) * __uint_as_float(b4.w));
+                }
             }
         }
         if (norm)
@@ -593,7 +603,7 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
                 const float z = sf[static_cast<size_t>(DK) * DV + c], dz = sr[static_cast<size_t>(DK) * DV + c];
                 sZ[c] = z;
                 sdZ[c] = dz;
-                if (want_dg) dl += wf * z * dz;
+                if (want_dg) dl += static_cast<float>(n) * __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g) * z * dz;
             }
     }
     __syncthreads();
