@@ -25,8 +25,10 @@
 //     the scores (off the 16-token block diagonal through a reference token
 //     between query and key, so both operand factors are at most 1; on it
 //     exactly, from running products of the gates), the triangular solve for
-//     W and U' (one column per thread, forward substitution), and the scaled
-//     tiles, written to a workspace record per chunk;
+//     W and U' by 16-token blocks (the inverse of each diagonal block by
+//     forward substitution, then X_I = T_II (R_I - sum_{J<I} A_IJ X_J) on the
+//     float32 matrix cores, each wave solving its own 16-column tiles), and
+//     the scaled tiles, written to a workspace record per chunk;
 //   kda_chain_kernel one workgroup per (head, block of value channels), the
 //     chunks in order: the state-dependent products only, the state slice of
 //     each wave held in matrix-core accumulators for the whole sequence.
@@ -63,12 +65,18 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     constexpr int LDA = C + 4;                        // A and P, float32
     static_assert(DK + DV <= NTHR && C <= 64 && C % 16 == 0 && DK % 16 == 0, "prep tiling");
 
+    constexpr int LDT = 16 + 4;                       // inverses of the diagonal blocks, float32
     __shared__ __align__(16) Op sQ[C * LDQ];
     __shared__ __align__(16) Op sK[C * LDQ];
+    // values staged in LDS for bf16 inputs (float32 tiles at d = 128 would not fit)
+    constexpr bool STAGE_V = sizeof(Op) == 2;
+    __shared__ __align__(16) Op sV[STAGE_V ? C * (DV + 16 / (int)sizeof(Op)) : 8];
     __shared__ __align__(16) float sB[C * LDB];
     __shared__ __align__(16) float sA[C * LDA];      // A (strict lower), float32
     __shared__ __align__(16) float sP[C * LDA];      // P (lower), float32
+    __shared__ __align__(16) float sT[NB * 16 * LDT]; // (I + A_II)^{-1}, float32
     __shared__ float sBeta[C];
+    constexpr int LDVV = DV + 16 / (int)sizeof(Op);
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int nchunks = (p.T + C - 1) / C;
@@ -81,17 +89,31 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     const float *ah = p.gate + tok0 * DK;             // alpha, per token and key channel
     unsigned char *rec = ws + (static_cast<size_t>(bh) * nchunks + c) * R::BYTES;
 
-    // ---- stage q, k (rows past n zero), beta (0 past n), and b = cumulative
-    // log2 alpha per channel (flat past n: the gates there count as 1)
-    stage_rows<C, DK>(sQ, LDQ, qh, DK, n, tid, NTHR);
-    stage_rows<C, DK>(sK, LDQ, kh, DK, n, tid, NTHR);
-    for (int t = tid; t < C; t += NTHR) sBeta[t] = t < n ? p.beta[tok0 + t] : 0.f;
-    // the gates, 16-byte loads issued together (rows past n: 1)
-    for (int e = tid; e < C * DK / 4; e += NTHR) {
-        const int t = e / (DK / 4), ch = (e % (DK / 4)) * 4;
-        float4 g = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (t < n) g = *reinterpret_cast<const float4 *>(ah + static_cast<size_t>(t) * DK + ch);
-        sB[t * LDB + ch] = g.x; sB[t * LDB + ch + 1] = g.y; sB[t * LDB + ch + 2] = g.z; sB[t * LDB + ch + 3] = g.w;
+    // ---- stage q, k, v (rows past n zero), beta (0 past n), and b = cumulative
+    // log2 alpha per channel (flat past n: the gates there count as 1).  Every
+    // global load is issued before the first LDS write.
+    {
+        TilePrefetch<C, DK, NTHR, IO> pq, pk;
+        TilePrefetch<C, DV, NTHR, IO> pv;
+        TilePrefetch<C, DK, NTHR, float> pg;
+        pq.load(qh, DK, n, tid);
+        pk.load(kh, DK, n, tid);
+        if constexpr (STAGE_V) pv.load(vh, DV, n, tid);
+        pg.load(ah, DK, n, tid);
+        const float beta = tid < C && tid < n ? p.beta[tok0 + tid] : 0.f;
+        pq.store(sQ, LDQ, tid);
+        pk.store(sK, LDQ, tid);
+        if constexpr (STAGE_V) pv.store(sV, LDVV, tid);
+        if (tid < C) sBeta[tid] = beta;
+#pragma unroll
+        for (int i = 0; i < pg.PER; ++i) {
+            const int e = tid + i * NTHR;
+            if (pg.TOTAL % NTHR != 0 && e >= pg.TOTAL) continue;
+            const int t = e / pg.VPR, ch = (e % pg.VPR) * 4;
+            float4 g = make_float4(1.f, 1.f, 1.f, 1.f);   // rows past n: no decay
+            if ((pg.valid >> i) & 1u) g = *reinterpret_cast<const float4 *>(&pg.r[i]);
+            sB[t * LDB + ch] = g.x; sB[t * LDB + ch + 1] = g.y; sB[t * LDB + ch + 2] = g.z; sB[t * LDB + ch + 3] = g.w;
+        }
     }
     __syncthreads();
     // cumulative log2 per channel: one column per thread, in registers
@@ -201,33 +223,70 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     }
     __syncthreads();
 
-    // ---- W and U': column col of [W | U'] per thread, forward substitution
-    //   x_i = rhs_i - sum_{m < i} A_im x_m
-    // with rhs = beta o (K o e^b) (W) or beta o V (U')
-    {
-        const int col = tid;
-        if (col < DK + DV) {
-            // right-hand sides first, then the substitution in place
-            float x[C];
+    // ---- T_II = (I + A_II)^{-1} of the diagonal blocks: wave I, lane c < 16
+    // forms column c by forward substitution (unit lower triangular)
+    for (int I = wave; I < NB; I += NTHR / 64) {
+        if (lane < 16) {
+            const float *ab = sA + 16 * I * LDA + 16 * I;
+            float x[16];
 #pragma unroll
-            for (int i = 0; i < C; ++i)
-                x[i] = col < DK ? sBeta[i] * to_f32(sK[i * LDQ + col]) * __builtin_amdgcn_exp2f(sB[i * LDB + col])
-                                : (i < n ? sBeta[i] * to_f32(vh[static_cast<size_t>(i) * DV + col - DK]) : 0.f);
+            for (int i = 0; i < 16; ++i) {
+                float s0 = i == lane ? 1.f : 0.f, s1 = 0.f;
 #pragma unroll
-            for (int i = 1; i < C; ++i) {
-                // four independent partial sums (m mod 4), so that the row sum
-                // is not one chain of dependent multiply-adds
-                const float *arow = sA + i * LDA;
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc[m & 3] += arow[m] * x[m];
-                x[i] -= (acc[0] + acc[1]) + (acc[2] + acc[3]);
+                for (int m = 0; m < i; ++m) {
+                    if (m & 1) s1 -= ab[i * LDA + m] * x[m];
+                    else s0 -= ab[i * LDA + m] * x[m];
+                }
+                x[i] = s0 + s1;
             }
-            Op *dst = col < DK ? reinterpret_cast<Op *>(rec + R::WT) + col
-                               : reinterpret_cast<Op *>(rec + R::UP) + (col - DK);
-            const int ld = col < DK ? DK : DV;
 #pragma unroll
-            for (int i = 0; i < C; ++i) from_f32(dst[i * ld], x[i]);
+            for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LDT + lane] = x[i];
+        }
+    }
+    __syncthreads();
+
+    // ---- W and U': X = [W | U'] solves (I + A) X = R, R = [beta o (K o e^b) |
+    // beta o V], by 16-token block rows: X_I = T_II (R_I - sum_{J<I} A_IJ X_J).
+    // The columns are independent, so each wave solves its own 16-column tiles
+    // with no barrier; a result tile (rows = tokens) is already the B operand
+    // of the next product.  float32 matrix cores throughout.
+    {
+        const int lr = lane & 15, lg = lane >> 4;
+        constexpr int NCT = (DK + DV) / 16;
+        for (int ct = wave; ct < NCT; ct += NTHR / 64) {
+            const int col = 16 * ct + lr;
+            const bool wcol = col < DK;
+            f32x4 X[NB];
+#pragma unroll
+            for (int I = 0; I < NB; ++I) {
+                f32x4 y;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = 16 * I + 4 * lg + r;
+                    float vv = 0.f;
+                    if (!wcol) {
+                        if constexpr (STAGE_V) vv = to_f32(sV[t * LDVV + col - DK]);
+                        else vv = t < n ? load1(vh + static_cast<size_t>(t) * DV + col - DK) : 0.f;
+                    }
+                    y[r] = wcol ? sBeta[t] * to_f32(sK[t * LDQ + col]) * __builtin_amdgcn_exp2f(sB[t * LDB + col])
+                                : sBeta[t] * vv;
+                }
+#pragma unroll
+                for (int J = 0; J < I; ++J) {
+                    const float4 a = *reinterpret_cast<const float4 *>(sA + (16 * I + lr) * LDA + 16 * J + 4 * lg);
+                    mma16(y, make_float4(-a.x, -a.y, -a.z, -a.w), make_float4(X[J][0], X[J][1], X[J][2], X[J][3]));
+                }
+                X[I] = zero4();
+                mma16(X[I], *reinterpret_cast<const float4 *>(sT + (16 * I + lr) * LDT + 4 * lg),
+                      make_float4(y[0], y[1], y[2], y[3]));
+            }
+            // rows 16 I + 4 lg + r of column col, to the record
+            Op *dst = wcol ? reinterpret_cast<Op *>(rec + R::WT) + col : reinterpret_cast<Op *>(rec + R::UP) + (col - DK);
+            const int ld = wcol ? DK : DV;
+#pragma unroll
+            for (int I = 0; I < NB; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) from_f32(dst[(16 * I + 4 * lg + r) * ld], X[I][r]);
         }
     }
 
