@@ -33,8 +33,8 @@ COMMON_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 
-SOURCES = ["la_api.cpp", "la_decode.hip", "la_chunk_linear.hip", "la_chunk_gdr.hip", "la_chunk_kda.hip",
-           "la_chunk_bwd.hip"]
+SOURCES = ["la_api.cpp", "la_decode.hip", "la_chunk_linear.hip", "la_chunk_segment.hip", "la_chunk_gdr.hip",
+           "la_chunk_kda.hip", "la_chunk_bwd.hip"]
 # peak probes (a streaming copy, a matrix-core loop), a library of their own
 PROBE_SOURCES = ["la_probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libla_probe.so")

@@ -1445,6 +1445,8 @@ static hipError_t linear_variant(const ChunkArgs &a) {
 // variant (none for the other variants).
 size_t chunk_workspace_bytes(const ChunkArgs &a) {
     if (a.variant == LA_KDA) return kda_workspace_bytes(a);
+    int seg_len, n_seg;
+    if (seg_plan(a, seg_len, n_seg)) return seg_workspace_bytes(a);
     if ((a.variant != LA_NORMALIZED && a.variant != LA_RETENTION) || a.T <= 0) return 0;
     const int64_t n = linear_max_segments(a);
     const size_t heads = static_cast<size_t>(a.B) * a.H;
@@ -1455,6 +1457,8 @@ size_t chunk_workspace_bytes(const ChunkArgs &a) {
 }
 
 hipError_t launch_chunk_linear(const ChunkArgs &a) {
+    int seg_len, n_seg;
+    if (seg_plan(a, seg_len, n_seg)) return launch_seg(a);
     if (a.dtype == LA_BF16) return linear_variant<BF16>(a);
     return linear_variant<F32>(a);
 }

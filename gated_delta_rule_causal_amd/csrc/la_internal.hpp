@@ -54,6 +54,10 @@ hipError_t launch_chunk(const ChunkArgs &a);
 hipError_t launch_chunk_kda(const ChunkArgs &a);
 size_t chunk_workspace_bytes(const ChunkArgs &a);
 size_t kda_workspace_bytes(const ChunkArgs &a);
+// normalized / retention over segments held whole in LDS (la_chunk_segment.hip)
+bool seg_plan(const ChunkArgs &a, int &seg_len, int &n_seg);
+size_t seg_workspace_bytes(const ChunkArgs &a);
+hipError_t launch_seg(const ChunkArgs &a);
 hipError_t launch_chunk_bwd(const BwdArgs &a);
 size_t bwd_workspace_bytes(const BwdArgs &a);
 int bwd_chunk_length(const BwdArgs &a);

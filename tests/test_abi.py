@@ -159,21 +159,27 @@ def test_workspace_query_of_invalid_desc_is_zero(lib):
 
 
 def test_workspace_sizes(lib):
-    # Only the normalized and retention variants use a workspace: one slot of d_v*d_k + d_k
-    # floats per head and segment, when the heads (value blocks of up to 64
-    # channels) give fewer workgroups than the 256 compute units (the segment
-    # count is bounded by 256 / workgroups and by the 16-token chunks over
-    # two); otherwise a staged copy of z0, d_k floats per head.
+    # Only the normalized and retention variants use a workspace, slots of
+    # d_v*d_k + d_k floats.  With d_k, d_v in {64, 128} and fewer heads than
+    # compute units, the segment path: n_seg + 1 slots per head (slot 0 the
+    # initial state), segments of up to 256 tokens (bf16, d = 64; 128 for
+    # d = 128) halved while one workgroup per compute unit remains.  Other
+    # few-head shapes: the chained path's slots, one per head and segment (the
+    # count bounded by 256 / workgroups and by the 16-token chunks over two);
+    # otherwise a staged copy of z0, d_k floats per head.
     slot = lambda dk, dv: (dv * dk + dk) * 4  # noqa: E731
-    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=4, H=8, T=2048)) == 32 * 8 * slot(64, 64)
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=4, H=8, T=2048)) == 32 * 9 * slot(64, 64)
     assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=1, H=1, T=100, d_k=16, d_v=16)) == 3 * slot(16, 16)
     assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, B=16, H=16, T=2048)) == 256 * 64 * 4   # 256 heads
     assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=0)) == 0
-    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=31)) == 6 * 64 * 4   # one 16-token chunk pair at most
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=31)) == 6 * 2 * slot(64, 64)   # one 64-token segment
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=31, d_k=32, d_v=32)) == 6 * 32 * 4   # one pass
+    # d = 128: 64-token segments, at most three per head (four slots a workgroup)
+    assert la.la_chunk_fwd_workspace(D(la.LA_NORMALIZED, T=100, d_k=128, d_v=128)) == 6 * 3 * slot(128, 128)
     assert la.la_chunk_fwd_workspace(D(la.LA_GATED, T=2048)) == 0
     assert la.la_chunk_fwd_workspace(D(la.LA_GATED_DELTA, T=2048)) == 0
-    # retention: the same segment slots, no z0 staging
-    assert la.la_chunk_fwd_workspace(D(la.LA_RETENTION, B=4, H=8, T=2048)) == 32 * 8 * slot(64, 64)
+    # retention: the same slots, no z0 staging
+    assert la.la_chunk_fwd_workspace(D(la.LA_RETENTION, B=4, H=8, T=2048)) == 32 * 9 * slot(64, 64)
     assert la.la_chunk_fwd_workspace(D(la.LA_RETENTION, B=16, H=16, T=2048)) == 0
 
 

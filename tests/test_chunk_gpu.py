@@ -209,10 +209,11 @@ def test_in_place_state_and_empty_sequence(name):
 
 @pytest.mark.parametrize("T", [40, 1000])
 def test_la_in_place_one_pass_many_value_blocks(T):
-    """Normalized variant in one pass with several value blocks per head (B=1,
-    H=2, d=64 gives four 16-channel blocks; T=40 is too short to segment), z_T
-    and S_T in place of z0 and S0: every block reads z0, one writes z_T."""
-    w = wl.variant_workload(la.LA_NORMALIZED, "f32", 64, 64, chunk=16, phi=la.LA_PHI_ELU1, seed=61)
+    """Normalized variant on the chained path with several value blocks per
+    head (B=1, H=2, d=32 gives two 16-channel blocks; T=40 is too short to
+    segment, T=1000 runs as segments), z_T and S_T in place of z0 and S0:
+    every block reads z0, one writes z_T."""
+    w = wl.variant_workload(la.LA_NORMALIZED, "f32", 32, 32, chunk=16, phi=la.LA_PHI_ELU1, seed=61)
     inp = wl.chunk_inputs(w, B=1, H=2, T=T, S0_std=0.1, z0=True)
     d = {k: dev(v) for k, v in inp.items()}
     ref = la.la_chunk_fwd(d["q"], d["k"], d["v"], variant=w.variant, S0=d["S0"], z0=d["z0"], chunk=16)
