@@ -490,24 +490,32 @@ __global__ void __launch_bounds__(kSegThreads) seg_attention_kernel(const SegPar
             const Op *srow = sS + (row0 + lr) * LDK + 4 * lg;
 #pragma unroll
             for (int g = 0; g < NKG; ++g) sg[g] = ld_group(srow + 16 * g);
-            f32x4 x0 = zero4(), x1 = zero4();
+            auto term = [&](f32x4 &x0, f32x4 &x1) {
 #pragma unroll
-            for (int g = 0; g + 2 <= NKG; g += 2) {
-                mma32(x0, sg[g], sg[g + 1], q0[g], q0[g + 1]);
-                mma32(x1, sg[g], sg[g + 1], q1[g], q1[g + 1]);
-            }
-            if constexpr (NKG % 2 == 1) {
-                mma16(x0, sg[NKG - 1], q0[NKG - 1]);
-                mma16(x1, sg[NKG - 1], q1[NKG - 1]);
-            }
+                for (int g = 0; g + 2 <= NKG; g += 2) {
+                    mma32(x0, sg[g], sg[g + 1], q0[g], q0[g + 1]);
+                    mma32(x1, sg[g], sg[g + 1], q1[g], q1[g + 1]);
+                }
+                if constexpr (NKG % 2 == 1) {
+                    mma16(x0, sg[NKG - 1], q0[NKG - 1]);
+                    mma16(x1, sg[NKG - 1], q1[NKG - 1]);
+                }
+            };
+            if (decay) {
+                f32x4 x0 = zero4(), x1 = zero4();
+                term(x0, x1);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                o0[a][r] += lead0 * x0[r];
-                o1[a][r] += lead1 * x1[r];
+                for (int r = 0; r < 4; ++r) {
+                    o0[a][r] += lead0 * x0[r];
+                    o1[a][r] += lead1 * x1[r];
+                }
+            } else {
+                term(o0[a], o1[a]);   // no decay: straight into the accumulators
             }
         }
-        const float inv0 = NORM ? 1.f / o0[NACC - 1][0] : 1.f;
-        const float inv1 = NORM ? 1.f / o1[NACC - 1][0] : 1.f;
+        // the denominators are positive (phi > 0): hardware reciprocal (1 ulp)
+        const float inv0 = NORM ? __builtin_amdgcn_rcpf(o0[NACC - 1][0]) : 1.f;
+        const float inv1 = NORM ? __builtin_amdgcn_rcpf(o1[NACC - 1][0]) : 1.f;
         IO *orow = static_cast<IO *>(p.out) + (tok0 + t0) * DV + 16 * vt0 + 4 * lg;
         if (t0 < n) {
 #pragma unroll
