@@ -517,6 +517,154 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(const BwdParams p, int DK
     }
 }
 
+// ----------------------------------------------------- chained states
+
+// Retention over many chunks: launches 1 and 2 as one chain per (head,
+// direction, block of VB value channels).  The workgroup keeps its columns of
+// the state (forward) or of the cotangent (reverse) in matrix-core
+// accumulators, walks the chunks in order, writes each chunk's entering state
+// (leaving cotangent) to its slot and adds the chunk's increment on the
+// matrix cores, with the same split operands as bwd_increments_kernel:
+//   forward  S_{c+1}  = gamma^n S_c + phiK^T diag(gamma^(n-1-j)) V,  from S0,
+//   reverse  dS_c     = gamma^n dS_{c+1} + phiQ^T diag(gamma^(t+1)) dO, from dS_T,
+// ending in dS0.  The slots are written once, and no increment goes through
+// memory.  Eight waves; wave w keeps the (key, value) 16x16 tiles w, w + 8, ...
+constexpr int kChainWaves = 8;
+constexpr int kChainMinChunks = 16;   // fewer chunks: increments + scan
+
+template <class DT, int DK, int DV, int C, int VB>
+__global__ void __launch_bounds__(kChainWaves * 64) bwd_chain_kernel(const BwdParams p) {
+    typedef typename DT::storage IO;
+    typedef typename OpOf<DT>::type Op;
+    constexpr bool SPLIT = sizeof(Op) == 2;
+    constexpr int NTHR = kChainWaves * 64, NCB = DK / 16, NIB = VB / 16;
+    constexpr int NT = NCB * NIB, TPW = (NT + kChainWaves - 1) / kChainWaves;
+    constexpr int PAD = 16 / sizeof(Op), LDK = DK + PAD, LDV = VB + PAD;
+    constexpr int NVB = DV / VB;
+    static_assert(DV % VB == 0 && VB % 16 == 0, "value blocks");
+    __shared__ __align__(16) Op sA[C * LDK];                 // weighted phi(k) (forward) or phi(q) (reverse)
+    __shared__ __align__(16) Op sAl[SPLIT ? C * LDK : 8];     // its low part
+    __shared__ __align__(16) Op sB[C * LDV];                 // this block's v (forward) or dO (reverse)
+
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int lr = lane & 15, lg = lane >> 4;
+    // workgroup -> (head, direction, value block); with a multiple of 8 heads
+    // the workgroups that read one head's keys (or queries) share an XCD
+    const int heads = p.B * p.H;
+    int bh, rev, vb;
+    {
+        const int bid = blockIdx.x;
+        if ((heads & 7) == 0) {
+            const int x = bid & 7, r = bid >> 3;
+            vb = r % NVB;
+            rev = (r / NVB) & 1;
+            bh = (r / NVB >> 1) * 8 + x;
+        } else {
+            vb = bid % NVB;
+            rev = (bid / NVB) & 1;
+            bh = bid / (2 * NVB);
+        }
+    }
+    const int N = p.n_chunk;
+    const float l2g = head_l2g(p, bh);
+    const bool elu = p.elu;
+    const size_t E = static_cast<size_t>(DK) * DV;
+    float *slots = (rev ? p.slot_r : p.slot_f) + static_cast<size_t>(bh) * N * E;
+    const IO *ah = static_cast<const IO *>(rev ? p.q : p.k) + static_cast<size_t>(bh) * p.T * DK;
+    const IO *bhp = static_cast<const IO *>(rev ? p.dout : p.v) + static_cast<size_t>(bh) * p.T * DV + vb * VB;
+    const float *init = rev ? p.dS_T : p.S0;   // library layout (d_v, d_k)
+
+    // the tiles of this wave: acc[i][r] = element (key 16 cb + 4 lg + r,
+    // value 16 ib + lr of the block)
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        acc[i] = zero4();
+        const int u = wave + kChainWaves * i;
+        if (u < NT && init) {
+            const int cb = u % NCB, ib = u / NCB;
+            const float *src = init + (static_cast<size_t>(bh) * DV + vb * VB + 16 * ib + lr) * DK + 16 * cb + 4 * lg;
+            const float4 x = *reinterpret_cast<const float4 *>(src);
+            acc[i] = f32x4{x.x, x.y, x.z, x.w};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    Staged<C, DK, NTHR, IO> pa;
+    Staged<C, VB, NTHR, IO> pb;
+    auto chunk_of = [&](int i) { return rev ? N - 1 - i : i; };   // i-th chunk of the walk
+    auto load = [&](int c) {
+        const int n = min(C, p.T - c * C);
+        pa.load(ah + static_cast<size_t>(c) * C * DK, DK, n, tid);
+        pb.load(bhp + static_cast<size_t>(c) * C * DV, DV, n, tid);
+    };
+    // slot stores per thread and chunk, issued after the next chunk's loads
+    constexpr int NST = (NT % kChainWaves == 0 ? TPW : 0) * 4;
+    load(chunk_of(0));
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    for (int i = 0; i < N; ++i) {
+        const int c = chunk_of(i);
+        const int n = min(C, p.T - c * C);
+        // this chunk's loads have landed; the previous chunk's slot stores,
+        // issued after them, stay in flight
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(NST));
+        // the chunk's token operands, decay-weighted as in bwd_increments_kernel
+        commit_tile<NTHR>(pa, sA, SPLIT ? sAl : static_cast<Op *>(nullptr), LDK, tid, [&](int t, float x) {
+            return phi_rt(x, elu) * __builtin_amdgcn_exp2f(static_cast<float>(rev ? t + 1 : n - 1 - t) * l2g);
+        });
+        commit_tile<NTHR>(pb, sB, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+        __syncthreads();
+        // the next chunk's loads (the last one re-read at the end), then the
+        // slot stores, which the next commit's wait for those loads leaves in
+        // flight: the state entering (cotangent leaving) chunk c
+        load(chunk_of(min(i + 1, N - 1)));
+        float *slot = slots + static_cast<size_t>(c) * E + vb * VB;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int u = wave + kChainWaves * j;
+            if (NT % kChainWaves == 0 || u < NT) {
+                const int cb = u % NCB, ib = u / NCB;
+                float *dst = slot + static_cast<size_t>(16 * cb + 4 * lg) * DV + 16 * ib + lr;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[r * DV] = acc[j][r];
+            }
+        }
+        const float gn = __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g);
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int u = wave + kChainWaves * j;
+            if (NT % kChainWaves != 0 && u >= NT) break;
+            const int cb = u % NCB, ib = u / NCB;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[j][r] *= gn;
+#pragma unroll
+            for (int t0 = 0; t0 + 32 <= C; t0 += 32) {
+                const auto b0 = kt_group<0>(sB, LDV, t0, 16 * ib, lane), b1 = kt_group<0>(sB, LDV, t0 + 16, 16 * ib, lane);
+                mma32(acc[j], kt_group<0>(sA, LDK, t0, 16 * cb, lane), kt_group<0>(sA, LDK, t0 + 16, 16 * cb, lane), b0, b1);
+                if constexpr (SPLIT)
+                    mma32(acc[j], kt_group<0>(sAl, LDK, t0, 16 * cb, lane), kt_group<0>(sAl, LDK, t0 + 16, 16 * cb, lane), b0, b1);
+            }
+            if constexpr (C % 32 == 16) {
+                const auto b0 = kt_group<0>(sB, LDV, C - 16, 16 * ib, lane);
+                mma16(acc[j], kt_group<0>(sA, LDK, C - 16, 16 * cb, lane), b0);
+                if constexpr (SPLIT) mma16(acc[j], kt_group<0>(sAl, LDK, C - 16, 16 * cb, lane), b0);
+            }
+        }
+        __syncthreads();
+    }
+    if (rev && p.dS0) {
+#pragma unroll
+        for (int j = 0; j < TPW; ++j) {
+            const int u = wave + kChainWaves * j;
+            if (u < NT) {
+                const int cb = u % NCB, ib = u / NCB;
+                float *dst = p.dS0 + (static_cast<size_t>(bh) * DV + vb * VB + 16 * ib + lr) * DK + 16 * cb + 4 * lg;
+                *reinterpret_cast<float4 *>(dst) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------------- gradients
 
 template <class DT, int DK, int DV, int C, bool NORM>
@@ -847,6 +995,10 @@ hipError_t bwd_launch(const BwdArgs &a) {
         hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, a.stream, p, DK, DV, C, 1);
         if (wgs) hipLaunchKernelGGL((bwd_normalizer_kernel<DT, DK, DV, C>), dim3(wgs), blk, 0, a.stream, p);
         hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, a.stream, p, DK, DV, C, 2);
+    } else if (p.n_chunk >= kChainMinChunks) {
+        constexpr int VB = DV >= 64 ? 64 : DV;
+        const uint32_t chains = static_cast<uint32_t>(heads * 2 * (DV / VB));
+        hipLaunchKernelGGL((bwd_chain_kernel<DT, DK, DV, C, VB>), dim3(chains), dim3(kChainWaves * 64), 0, a.stream, p);
     } else {
         if (wgs) hipLaunchKernelGGL((bwd_increments_kernel<DT, DK, DV, C, false>), dim3(wgs), blk, 0, a.stream, p);
         hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, a.stream, p, DK, DV, C, 3);

@@ -177,3 +177,18 @@ def test_bwd_retention_training_shape_sampled_heads():
             errs[n] = max(errs.get(n, 0.0), e)
     record("workload-bwd-ret_bf16_b4h16t8192d128-heads0,9", errs, "bf16")
     assert max(errs.values()) <= TOL["bf16"], errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,H,dk,dv", [("ret", 3, 64, 64), ("ret_elu", 8, 128, 32), ("ret", 8, 32, 128)])
+def test_bwd_retention_many_chunks(kind, H, dk, dv, dtype):
+    """Retention over many chunks (18 of 64 tokens, the last one ragged), where
+    the chunk states come from one chain per head, direction and value block:
+    every gradient against the oracle, with 3 heads and with 8 (the two
+    workgroup orders)."""
+    T = 17 * 64 + 29
+    w, inp, cot = _case(kind, dtype, dk, dv, 1, H, T, seed=251)
+    print("bwd chain", kind, dtype, H, dk, dv, "T", T, flush=True)
+    errs = _errors(_run_gpu(w, inp, cot), _oracle(w, inp, cot))
+    record("bwd-chain-%s-%s-H%d-dk%d-dv%d" % (kind, dtype, H, dk, dv), errs, dtype)
+    assert max(errs.values()) <= TOL[dtype], errs
