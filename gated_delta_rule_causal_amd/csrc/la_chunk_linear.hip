@@ -133,18 +133,25 @@ __device__ __forceinline__ float row_scan_mul(float x) {
     "v_mul_f32_dpp %2, %6, %2 " CTRL "\n\tv_mul_f32_dpp %3, %7, %3 " CTRL
 // x[i] <- y[i] (moved by the DPP control) times x[i]
 #define LA_DPP4_OPS(x, y) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]) : "v"(y[0]), "v"(y[1]), "v"(y[2]), "v"(y[3])
+// the same with y = x, in place (the DPP source is read before the write), so
+// that no copy of x is made for each step
+#define LA_DPP4_SELF(CTRL)                                                                                              \
+    "s_nop 1\n\t"                                                                                                   \
+    "v_mul_f32_dpp %0, %0, %0 " CTRL "\n\tv_mul_f32_dpp %1, %1, %1 " CTRL "\n\t"                                     \
+    "v_mul_f32_dpp %2, %2, %2 " CTRL "\n\tv_mul_f32_dpp %3, %3, %3 " CTRL
+#define LA_DPP4_SELF_OPS(x) "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3])
 __device__ __forceinline__ void row_scan_mul4(float (&x)[4]) {
-    asm(LA_DPP4("row_shr:1 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
-    asm(LA_DPP4("row_shr:2 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
-    asm(LA_DPP4("row_shr:4 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
-    asm(LA_DPP4("row_shr:8 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4_SELF("row_shr:1 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
+    asm(LA_DPP4_SELF("row_shr:2 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
+    asm(LA_DPP4_SELF("row_shr:4 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
+    asm(LA_DPP4_SELF("row_shr:8 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
 }
 // x <- y[last lane of the row before] * x on rows 1 and 3, then
 // x <- x[lane 31] * x on rows 2 and 3 (with x = y on entry: the inclusive
 // prefix over the whole wave, from the row-wise one)
 __device__ __forceinline__ void wave_prefix_from_rows4(const float (&y)[4], float (&x)[4]) {
     asm(LA_DPP4("row_bcast:15 row_mask:0xa bank_mask:0xf") : LA_DPP4_OPS(x, y));
-    asm(LA_DPP4("row_bcast:31 row_mask:0xc bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4_SELF("row_bcast:31 row_mask:0xc bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
 }
 // x <- y[lane 31] * x on row 2
 __device__ __forceinline__ void mul_bcast15_row2_4(const float (&y)[4], float (&x)[4]) {
@@ -162,10 +169,10 @@ __device__ __forceinline__ float row_suffix_mul(float x) {
     return x;
 }
 __device__ __forceinline__ void row_suffix_mul4(float (&x)[4]) {
-    asm(LA_DPP4("row_shl:1 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
-    asm(LA_DPP4("row_shl:2 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
-    asm(LA_DPP4("row_shl:4 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
-    asm(LA_DPP4("row_shl:8 row_mask:0xf bank_mask:0xf") : LA_DPP4_OPS(x, x));
+    asm(LA_DPP4_SELF("row_shl:1 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
+    asm(LA_DPP4_SELF("row_shl:2 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
+    asm(LA_DPP4_SELF("row_shl:4 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
+    asm(LA_DPP4_SELF("row_shl:8 row_mask:0xf bank_mask:0xf") : LA_DPP4_SELF_OPS(x));
 }
 // the next lane's value within its 16-lane row, 1 at the row end: with
 // x = row_suffix_mul(g), the exclusive suffix product g_{i+1} * ... * g_15
