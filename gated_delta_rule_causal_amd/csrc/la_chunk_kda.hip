@@ -49,7 +49,7 @@ struct KdaRec {
     static constexpr size_t BYTES = (EC + DK * 4 + 255) / 256 * 256;
 };
 
-constexpr int kKdaPrepThreads = 512;
+constexpr int kKdaPrepThreads = 1024;   // sixteen waves
 
 // ------------------------------------------------------------------ prep
 template <class DT, int DK, int DV, int C>
@@ -61,7 +61,7 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     constexpr int NTHR = kKdaPrepThreads;
     constexpr int NB = C / 16;
     constexpr int LDQ = DK + 16 / (int)sizeof(Op);   // raw q, k rows
-    constexpr int LDB = DK + 1;                       // cumulative log2 gates
+    constexpr int LDB = DK + 4;                       // cumulative log2 gates (16-byte rows)
     constexpr int LDA = C + 4;                        // A and P, float32
     static_assert(DK + DV <= NTHR && C <= 64 && C % 16 == 0 && DK % 16 == 0, "prep tiling");
 
@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
             const int t = e / pg.VPR, ch = (e % pg.VPR) * 4;
             float4 g = make_float4(1.f, 1.f, 1.f, 1.f);   // rows past n: no decay
             if ((pg.valid >> i) & 1u) g = *reinterpret_cast<const float4 *>(&pg.r[i]);
-            sB[t * LDB + ch] = g.x; sB[t * LDB + ch + 1] = g.y; sB[t * LDB + ch + 2] = g.z; sB[t * LDB + ch + 3] = g.w;
+            *reinterpret_cast<float4 *>(sB + t * LDB + ch) = g;
         }
     }
     __syncthreads();
@@ -158,15 +158,25 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
 #pragma unroll
             for (int k0 = 0; k0 < DK; k0 += 16) {
                 const int ch = k0 + 4 * lg;
+                // four channels of each row at once (16-byte rows of b, 8- or
+                // 16-byte groups of q and k)
+                const float4 b4t = *reinterpret_cast<const float4 *>(sB + t * LDB + ch);
+                const float4 b4j = *reinterpret_cast<const float4 *>(sB + j * LDB + ch);
+                const float4 b4r = r >= 0 ? *reinterpret_cast<const float4 *>(sB + r * LDB + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
+                float xq[4], xt[4], xj[4];
+                Gp::unpack(ld_group(sQ + t * LDQ + ch), xq);
+                Gp::unpack(ld_group(sK + t * LDQ + ch), xt);
+                Gp::unpack(ld_group(sK + j * LDQ + ch), xj);
+                const float bt[4] = {b4t.x, b4t.y, b4t.z, b4t.w}, bjv[4] = {b4j.x, b4j.y, b4j.z, b4j.w};
+                const float brv[4] = {b4r.x, b4r.y, b4r.z, b4r.w};
                 float qs[4], ks[4], kj[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float br = r >= 0 ? sB[r * LDB + ch + i] : 0.f;
-                    const float ft = __builtin_amdgcn_exp2f(sB[t * LDB + ch + i] - br);
-                    const float fj = __builtin_amdgcn_exp2f(br - sB[j * LDB + ch + i]);
-                    qs[i] = to_f32(sQ[t * LDQ + ch + i]) * ft;
-                    ks[i] = to_f32(sK[t * LDQ + ch + i]) * ft;
-                    kj[i] = to_f32(sK[j * LDQ + ch + i]) * fj;
+                    const float ft = __builtin_amdgcn_exp2f(bt[i] - brv[i]);
+                    const float fj = __builtin_amdgcn_exp2f(brv[i] - bjv[i]);
+                    qs[i] = xq[i] * ft;
+                    ks[i] = xt[i] * ft;
+                    kj[i] = xj[i] * fj;
                 }
                 // float32 operands whatever the input type: the scaled operands
                 // are not exact in bf16, and rounding them would be amplified
