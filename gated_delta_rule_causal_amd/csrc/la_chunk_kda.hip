@@ -322,9 +322,11 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
 
 // ------------------------------------------------------------------ chain
 // One workgroup per (head, DVB value channels): NW waves, the first DVB / 16
-// of them state waves (16 value channels each).  Every wave loads the next
-// chunk's record into registers while the state waves work on the current
-// one; the stores to LDS follow a barrier.
+// of them state waves (16 value channels each).  When two copies of a chunk's
+// tiles fit in LDS, the other waves stage chunk c + 1 into the second copy while
+// the state waves work on chunk c (one barrier per chunk); otherwise every wave
+// loads the next chunk's record into registers during the state work and
+// stores it to LDS after a barrier.
 template <class DT, int DK, int DV, int DVB, int C, int NW>
 __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p, const unsigned char *ws) {
     typedef typename DT::storage IO;
@@ -338,13 +340,17 @@ __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p,
     constexpr int PAD = 16 / sizeof(Op);
     constexpr int LDK = DK + PAD, LDU = DVB + PAD, LDC = C + PAD;
     static_assert(WS <= NW && C <= 64 && C % 16 == 0, "chain tiling");
+    constexpr int TILE_BYTES = (3 * C * LDK + C * LDU + C * LDC) * (int)sizeof(Op) + DK * 4;
+    constexpr int NBUF = WS < NW && 2 * TILE_BYTES <= 150 * 1024 ? 2 : 1;
+    // staging threads: the non-state waves with two buffers, else all
+    constexpr int LTHR = NBUF == 2 ? (NW - WS) * 64 : NTHR;
 
-    __shared__ __align__(16) Op sQt[C * LDK];
-    __shared__ __align__(16) Op sWt[C * LDK];
-    __shared__ __align__(16) Op sKt[C * LDK];
-    __shared__ __align__(16) Op sUp[C * LDU];
-    __shared__ __align__(16) Op sPt[C * LDC];
-    __shared__ __align__(16) float sEC[DK];
+    __shared__ __align__(16) Op sQt[NBUF * C * LDK];
+    __shared__ __align__(16) Op sWt[NBUF * C * LDK];
+    __shared__ __align__(16) Op sKt[NBUF * C * LDK];
+    __shared__ __align__(16) Op sUp[NBUF * C * LDU];
+    __shared__ __align__(16) Op sPt[NBUF * C * LDC];
+    __shared__ __align__(16) float sEC[NBUF * DK];
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
@@ -368,36 +374,47 @@ __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p,
     }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-    TilePrefetch<C, DK, NTHR, Op> pq, pw, pk;
-    TilePrefetch<C, DVB, NTHR, Op> pu;
-    TilePrefetch<C, C, NTHR, Op> pp;
+    const bool loader = NBUF == 1 || !state_wave;
+    const int ltid = NBUF == 2 ? tid - WS * 64 : tid;
+    TilePrefetch<C, DK, LTHR, Op> pq, pw, pk;
+    TilePrefetch<C, DVB, LTHR, Op> pu;
+    TilePrefetch<C, C, LTHR, Op> pp;
     float4 pe = make_float4(0.f, 0.f, 0.f, 0.f);
     auto load = [&](int c) {
         const unsigned char *rec = ws + (static_cast<size_t>(bh) * nchunks + c) * R::BYTES;
-        pq.load(reinterpret_cast<const Op *>(rec + R::QT), DK, C, tid);
-        pw.load(reinterpret_cast<const Op *>(rec + R::WT), DK, C, tid);
-        pk.load(reinterpret_cast<const Op *>(rec + R::KT), DK, C, tid);
-        pu.load(reinterpret_cast<const Op *>(rec + R::UP) + vb * DVB, DV, C, tid);
-        pp.load(reinterpret_cast<const Op *>(rec + R::PT), C, C, tid);
-        if (tid < DK / 4) pe = reinterpret_cast<const float4 *>(rec + R::EC)[tid];
+        pq.load(reinterpret_cast<const Op *>(rec + R::QT), DK, C, ltid);
+        pw.load(reinterpret_cast<const Op *>(rec + R::WT), DK, C, ltid);
+        pk.load(reinterpret_cast<const Op *>(rec + R::KT), DK, C, ltid);
+        pu.load(reinterpret_cast<const Op *>(rec + R::UP) + vb * DVB, DV, C, ltid);
+        pp.load(reinterpret_cast<const Op *>(rec + R::PT), C, C, ltid);
+        if (ltid < DK / 4) pe = reinterpret_cast<const float4 *>(rec + R::EC)[ltid];
     };
-    auto store = [&]() {
-        pq.store(sQt, LDK, tid);
-        pw.store(sWt, LDK, tid);
-        pk.store(sKt, LDK, tid);
-        pu.store(sUp, LDU, tid);
-        pp.store(sPt, LDC, tid);
-        if (tid < DK / 4) reinterpret_cast<float4 *>(sEC)[tid] = pe;
+    auto store = [&](int b) {
+        pq.store(sQt + b * C * LDK, LDK, ltid);
+        pw.store(sWt + b * C * LDK, LDK, ltid);
+        pk.store(sKt + b * C * LDK, LDK, ltid);
+        pu.store(sUp + b * C * LDU, LDU, ltid);
+        pp.store(sPt + b * C * LDC, LDC, ltid);
+        if (ltid < DK / 4) reinterpret_cast<float4 *>(sEC + b * DK)[ltid] = pe;
     };
 
     if (nchunks > 0) {
-        load(0);
-        store();
+        if (loader) {
+            load(0);
+            store(0);
+        }
         __syncthreads();
     }
     for (int c = 0; c < nchunks; ++c) {
-        if (c + 1 < nchunks) load(c + 1);
+        const int b = NBUF == 2 ? (c & 1) : 0;
+        if (loader && c + 1 < nchunks) {
+            load(c + 1);
+            if constexpr (NBUF == 2) store(b ^ 1);   // buffer b ^ 1 was last read in chunk c - 1
+        }
         if (state_wave) {
+            const Op *sQc = sQt + b * C * LDK, *sWc = sWt + b * C * LDK, *sKc = sKt + b * C * LDK;
+            const Op *sUc = sUp + b * C * LDU, *sPc = sPt + b * C * LDC;
+            const float *sEc = sEC + b * DK;
             G4 sb[NCB];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) sb[cb] = Gp::make(st[cb]);
@@ -408,8 +425,8 @@ __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p,
             for (int I = 0; I < NB; ++I) {
                 xs[I] = zero4();
                 wsv[I] = zero4();
-                const Op *qr = sQt + (16 * I + lr) * LDK + 4 * lg;
-                const Op *wr = sWt + (16 * I + lr) * LDK + 4 * lg;
+                const Op *qr = sQc + (16 * I + lr) * LDK + 4 * lg;
+                const Op *wr = sWc + (16 * I + lr) * LDK + 4 * lg;
 #pragma unroll
                 for (int s2 = 0; s2 + 2 <= NCB; s2 += 2) {
                     mma32(xs[I], sb[s2], sb[s2 + 1], ld_group(qr + 16 * s2), ld_group(qr + 16 * s2 + 16));
@@ -426,7 +443,7 @@ __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p,
             for (int I = 0; I < NB; ++I) {
                 f32x4 u;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) u[i] = to_f32(sUp[(16 * I + 4 * lg + i) * LDU + vloc]) - wsv[I][i];
+                for (int i = 0; i < 4; ++i) u[i] = to_f32(sUc[(16 * I + 4 * lg + i) * LDU + vloc]) - wsv[I][i];
                 ub[I] = Gp::make(u);
             }
             // O^T = X^T + U^T P^T, stored four values of a token at a time
@@ -434,25 +451,27 @@ __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p,
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
                 f32x4 o = xs[I];
-                tile_mma_rl_n<NB>(o, ub, sPt + 16 * I * LDC, LDC, I + 1, lane);
+                tile_mma_rl_n<NB>(o, ub, sPc + 16 * I * LDC, LDC, I + 1, lane);
                 const int t = 16 * I + lr;
                 if (t < n) st_group(oh + static_cast<size_t>(c * C + t) * DV + vb * DVB + 16 * wave + 4 * lg, Gp::make(o));
             }
             // S^T <- diag(e^{b_n}) S^T + (K o e^{b_n - b})^T U
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                const float4 e4 = *reinterpret_cast<const float4 *>(sEC + 16 * cb + 4 * lg);
+                const float4 e4 = *reinterpret_cast<const float4 *>(sEc + 16 * cb + 4 * lg);
                 st[cb][0] *= e4.x; st[cb][1] *= e4.y; st[cb][2] *= e4.z; st[cb][3] *= e4.w;
 #pragma unroll
                 for (int s2 = 0; s2 + 2 <= NB; s2 += 2)
-                    mma32(st[cb], kt_group<0>(sKt, LDK, 16 * s2, 16 * cb, lane),
-                          kt_group<0>(sKt, LDK, 16 * s2 + 16, 16 * cb, lane), ub[s2], ub[s2 + 1]);
-                if constexpr (NB % 2 == 1) mma16(st[cb], kt_group<0>(sKt, LDK, 16 * (NB - 1), 16 * cb, lane), ub[NB - 1]);
+                    mma32(st[cb], kt_group<0>(sKc, LDK, 16 * s2, 16 * cb, lane),
+                          kt_group<0>(sKc, LDK, 16 * s2 + 16, 16 * cb, lane), ub[s2], ub[s2 + 1]);
+                if constexpr (NB % 2 == 1) mma16(st[cb], kt_group<0>(sKc, LDK, 16 * (NB - 1), 16 * cb, lane), ub[NB - 1]);
             }
         }
         __syncthreads();
-        if (c + 1 < nchunks) store();
-        __syncthreads();
+        if constexpr (NBUF == 1) {
+            if (c + 1 < nchunks) store(0);
+            __syncthreads();
+        }
     }
 
     if (p.S_T && state_wave) {
