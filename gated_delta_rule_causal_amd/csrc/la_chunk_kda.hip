@@ -483,7 +483,7 @@ __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p,
 
 // ------------------------------------------------------------------ dispatch
 
-constexpr int kKdaChainWaves = 4;
+constexpr int kKdaChainWaves = 6;
 
 template <class DT, int DK, int DV, int C>
 static constexpr size_t kda_rec_bytes() { return KdaRec<typename OpOf<DT>::type, DK, DV, C>::BYTES; }
