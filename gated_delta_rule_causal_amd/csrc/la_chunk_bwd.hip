@@ -529,6 +529,9 @@ __global__ void __launch_bounds__(256) bwd_scan_kernel(const BwdParams p, int DK
 //   reverse  dS_c     = gamma^n dS_{c+1} + phiQ^T diag(gamma^(t+1)) dO, from dS_T,
 // ending in dS0.  The slots are written once, and no increment goes through
 // memory.  Eight waves; wave w keeps the (key, value) 16x16 tiles w, w + 8, ...
+// The chunk operands sit in two LDS copies: each wave commits chunk i + 1 to
+// one while the matrix-core work of chunk i reads the other (one barrier per
+// chunk).
 constexpr int kChainWaves = 8;
 constexpr int kChainMinChunks = 16;   // fewer chunks: increments + scan
 
@@ -542,9 +545,9 @@ __global__ void __launch_bounds__(kChainWaves * 64) bwd_chain_kernel(const BwdPa
     constexpr int PAD = 16 / sizeof(Op), LDK = DK + PAD, LDV = VB + PAD;
     constexpr int NVB = DV / VB;
     static_assert(DV % VB == 0 && VB % 16 == 0, "value blocks");
-    __shared__ __align__(16) Op sA[C * LDK];                 // weighted phi(k) (forward) or phi(q) (reverse)
-    __shared__ __align__(16) Op sAl[SPLIT ? C * LDK : 8];     // its low part
-    __shared__ __align__(16) Op sB[C * LDV];                 // this block's v (forward) or dO (reverse)
+    __shared__ __align__(16) Op sA[2 * C * LDK];                 // weighted phi(k) (forward) or phi(q) (reverse)
+    __shared__ __align__(16) Op sAl[SPLIT ? 2 * C * LDK : 8];     // its low part
+    __shared__ __align__(16) Op sB[2 * C * LDV];                 // this block's v (forward) or dO (reverse)
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
@@ -600,22 +603,26 @@ __global__ void __launch_bounds__(kChainWaves * 64) bwd_chain_kernel(const BwdPa
     };
     // slot stores per thread and chunk, issued after the next chunk's loads
     constexpr int NST = (NT % kChainWaves == 0 ? TPW : 0) * 4;
+    // the chunk's token operands into copy b, decay-weighted as in bwd_increments_kernel
+    auto commit = [&](int c, int b) {
+        const int n = min(C, p.T - c * C);
+        commit_tile<NTHR>(pa, sA + b * C * LDK, SPLIT ? sAl + b * C * LDK : static_cast<Op *>(nullptr), LDK, tid,
+                          [&](int t, float x) {
+                              return phi_rt(x, elu) * __builtin_amdgcn_exp2f(static_cast<float>(rev ? t + 1 : n - 1 - t) * l2g);
+                          });
+        commit_tile<NTHR>(pb, sB + b * C * LDV, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+    };
     load(chunk_of(0));
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    commit(chunk_of(0), 0);
+    __syncthreads();
     for (int i = 0; i < N; ++i) {
         const int c = chunk_of(i);
         const int n = min(C, p.T - c * C);
-        // this chunk's loads have landed; the previous chunk's slot stores,
-        // issued after them, stay in flight
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt(NST));
-        // the chunk's token operands, decay-weighted as in bwd_increments_kernel
-        commit_tile<NTHR>(pa, sA, SPLIT ? sAl : static_cast<Op *>(nullptr), LDK, tid, [&](int t, float x) {
-            return phi_rt(x, elu) * __builtin_amdgcn_exp2f(static_cast<float>(rev ? t + 1 : n - 1 - t) * l2g);
-        });
-        commit_tile<NTHR>(pb, sB, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
-        __syncthreads();
+        const int b = i & 1;
+        const Op *cA = sA + b * C * LDK, *cAl = sAl + (SPLIT ? b * C * LDK : 0), *cB = sB + b * C * LDV;
         // the next chunk's loads (the last one re-read at the end), then the
-        // slot stores, which the next commit's wait for those loads leaves in
+        // slot stores, which the commit's wait for those loads leaves in
         // flight: the state entering (cotangent leaving) chunk c
         load(chunk_of(min(i + 1, N - 1)));
         float *slot = slots + static_cast<size_t>(c) * E + vb * VB;
@@ -639,17 +646,21 @@ __global__ void __launch_bounds__(kChainWaves * 64) bwd_chain_kernel(const BwdPa
             for (int r = 0; r < 4; ++r) acc[j][r] *= gn;
 #pragma unroll
             for (int t0 = 0; t0 + 32 <= C; t0 += 32) {
-                const auto b0 = kt_group<0>(sB, LDV, t0, 16 * ib, lane), b1 = kt_group<0>(sB, LDV, t0 + 16, 16 * ib, lane);
-                mma32(acc[j], kt_group<0>(sA, LDK, t0, 16 * cb, lane), kt_group<0>(sA, LDK, t0 + 16, 16 * cb, lane), b0, b1);
+                const auto b0 = kt_group<0>(cB, LDV, t0, 16 * ib, lane), b1 = kt_group<0>(cB, LDV, t0 + 16, 16 * ib, lane);
+                mma32(acc[j], kt_group<0>(cA, LDK, t0, 16 * cb, lane), kt_group<0>(cA, LDK, t0 + 16, 16 * cb, lane), b0, b1);
                 if constexpr (SPLIT)
-                    mma32(acc[j], kt_group<0>(sAl, LDK, t0, 16 * cb, lane), kt_group<0>(sAl, LDK, t0 + 16, 16 * cb, lane), b0, b1);
+                    mma32(acc[j], kt_group<0>(cAl, LDK, t0, 16 * cb, lane), kt_group<0>(cAl, LDK, t0 + 16, 16 * cb, lane), b0, b1);
             }
             if constexpr (C % 32 == 16) {
-                const auto b0 = kt_group<0>(sB, LDV, C - 16, 16 * ib, lane);
-                mma16(acc[j], kt_group<0>(sA, LDK, C - 16, 16 * cb, lane), b0);
-                if constexpr (SPLIT) mma16(acc[j], kt_group<0>(sAl, LDK, C - 16, 16 * cb, lane), b0);
+                const auto b0 = kt_group<0>(cB, LDV, C - 16, 16 * ib, lane);
+                mma16(acc[j], kt_group<0>(cA, LDK, C - 16, 16 * cb, lane), b0);
+                if constexpr (SPLIT) mma16(acc[j], kt_group<0>(cAl, LDK, C - 16, 16 * cb, lane), b0);
             }
         }
+        // chunk i + 1 into the other copy, last read by chunk i - 1 (before the
+        // previous barrier); its loads have landed, the slot stores stay in flight
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(NST));
+        if (i + 1 < N) commit(chunk_of(i + 1), b ^ 1);
         __syncthreads();
     }
     if (rev && p.dS0) {
