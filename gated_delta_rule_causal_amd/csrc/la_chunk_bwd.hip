@@ -40,8 +40,9 @@
 //      rounded output would not do;
 //   4. bwd_scan_kernel: the reverse scan turns the cotangent increments into
 //      the cotangent leaving every chunk, in place, and ends in dS0, dz0;
-//   5. bwd_grad_kernel (one workgroup per chunk): dq, dk, dv and the chunk's
-//      share of d(ln gamma);
+//   5. bwd_grad_kernel (one workgroup per chunk; retention in bf16: persistent,
+//      one workgroup per CU, the next chunk's loads in flight): dq, dk, dv and
+//      the chunk's share of d(ln gamma);
 //   6. bwd_dgate_kernel (one workgroup per head, only when the decay's
 //      gradient is asked for): the shares summed over batch and chunks.
 // The states are float32 in the workspace, key-major ([key channel][value
@@ -191,6 +192,7 @@ constexpr int bwd_chunk() {
 }
 
 constexpr int kBwdWaves = 8;
+constexpr uint32_t kGradPersistWGs = 256;   // MI355X compute units
 
 // ------------------------------------------------------------- increments
 
@@ -703,264 +705,303 @@ __global__ void __launch_bounds__(kBwdWaves * 64) bwd_grad_kernel(const BwdParam
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int lr = lane & 15, lg = lane >> 4;
     const int N = p.n_chunk;
-    const int bh = blockIdx.x / N, ch = blockIdx.x - bh * N;
-    const int n = min(C, p.T - ch * C);
-    const size_t tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(ch) * C;
-    const float l2g = head_l2g(p, bh);
+    const int jobs = p.B * p.H * N;
     const bool elu = p.elu, want_dg = p.dgate != nullptr;
     constexpr bool norm = NORM;
-    const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
-    const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
     const size_t E = static_cast<size_t>(DK) * DV + (norm ? DK : 0);
-    const float *sf = p.slot_f + (static_cast<size_t>(bh) * N + ch) * E;   // state entering the chunk
-    const float *sr = p.slot_r + (static_cast<size_t>(bh) * N + ch) * E;   // cotangent leaving it
-    float dl = 0.f;   // this lane's share of the chunk's d(ln gamma)
+    // With the states staged in LDS (retention, bf16) no product of a chunk
+    // reads global memory, so the workgroups are persistent and each keeps the
+    // next chunk's loads in flight during the current chunk's products.
+    // The derivative of phi = elu + 1 is min(phi, 1): with PF it is taken from
+    // the staged phi (bf16, relative error <= 2^-8) instead of a global load.
+    constexpr bool PF = STAGE_S;
 
-    for (int e = tid; e <= C; e += NTHR) sPow[e] = __builtin_amdgcn_exp2f(static_cast<float>(e) * l2g);
-    if (norm)
-        for (int t = tid; t < C; t += NTHR) {
-            sInv[t] = t < n ? p.tok[2 * (tok0 + t)] : 0.f;
-            sDd[t] = t < n ? p.tok[2 * (tok0 + t) + 1] : 0.f;
-        }
-    {
-        // every global load of the chunk first (inputs, and the float32
-        // state and cotangent rows), then the LDS commits.  dO goes in as it
-        // is: 1/den_t is applied in float32 to the products (the value and
-        // normalizer parts of the normalized gradient nearly cancel).
-        Staged<C, DK, NTHR, IO> pq, pk;
-        Staged<C, DV, NTHR, IO> pv, po;
-        Staged<DK, DV, NTHR, float> pd, ps;
-        pq.load(qh, DK, n, tid);
-        pk.load(kh, DK, n, tid);
+    Staged<C, DK, NTHR, IO> pq, pk;
+    Staged<C, DV, NTHR, IO> pv, po;
+    Staged<DK, DV, NTHR, float> pd, ps;
+    // every global load of a chunk (inputs, and the float32 state and
+    // cotangent rows), issued before any LDS commit
+    auto load_job = [&](int job) {
+        const int bh = job / N, ch = job - bh * N;
+        const int n = min(C, p.T - ch * C);
+        const size_t tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(ch) * C;
+        pq.load(static_cast<const IO *>(p.q) + tok0 * DK, DK, n, tid);
+        pk.load(static_cast<const IO *>(p.k) + tok0 * DK, DK, n, tid);
         pv.load(static_cast<const IO *>(p.v) + tok0 * DV, DV, n, tid);
         po.load(static_cast<const IO *>(p.dout) + tok0 * DV, DV, n, tid);
-        pd.load(sr, DV, DK, tid);
-        const bool need_s = STAGE_S || want_dg;
-        if (need_s) ps.load(sf, DV, DK, tid);
-        commit_tile<NTHR>(pq, sQ, static_cast<Op *>(nullptr), LDK, tid, [&](int, float x) { return phi_rt(x, elu); });
-        commit_tile<NTHR>(pk, sK, SPLIT ? sKl : static_cast<Op *>(nullptr), LDK, tid,
-                          [&](int, float x) { return phi_rt(x, elu); });
-        commit_tile<NTHR>(pv, sV, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
-        commit_tile<NTHR>(po, sO, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
-        commit_tile<NTHR>(pd, sdS, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
-        if (need_s) {
-            if constexpr (STAGE_S) commit_tile<NTHR>(ps, sS, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
-            if (want_dg) {
-                // the state-coupling term n gamma^n <dS'_{c+1}, S'_c>, float32
-                const float wf = static_cast<float>(n) * __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g);
-#pragma unroll
-                for (int i = 0; i < pd.PER; ++i) {
-                    if (!((pd.valid >> i) & 1u)) continue;   // lanes past the tile re-read its last vector
-                    const uint4 a4 = pd.r[i], b4 = ps.r[i];
-                    dl += wf * (__uint_as_float(a4.x) * __uint_as_float(b4.x) + __uint_as_float(a4.y) * __uint_as_float(b4.y) +
-                                __uint_as_float(a4.z) * __uint_as_float(b4.z) + __uint_as_float(a4.w) * __uint_as_float(b4.w));
-                }
-            }
-        }
+        pd.load(p.slot_r + static_cast<size_t>(job) * E, DV, DK, tid);
+        if (STAGE_S || want_dg) ps.load(p.slot_f + static_cast<size_t>(job) * E, DV, DK, tid);
+    };
+    if (PF && static_cast<int>(blockIdx.x) < jobs) load_job(blockIdx.x);
+
+    for (int job = blockIdx.x; job < jobs; job += gridDim.x) {
+        const int bh = job / N, ch = job - bh * N;
+        const int n = min(C, p.T - ch * C);
+        const size_t tok0 = static_cast<size_t>(bh) * p.T + static_cast<size_t>(ch) * C;
+        const float l2g = head_l2g(p, bh);
+        const IO *qh = static_cast<const IO *>(p.q) + tok0 * DK;
+        const IO *kh = static_cast<const IO *>(p.k) + tok0 * DK;
+        const float *sf = p.slot_f + (static_cast<size_t>(bh) * N + ch) * E;   // state entering the chunk
+        const float *sr = p.slot_r + (static_cast<size_t>(bh) * N + ch) * E;   // cotangent leaving it
+        float dl = 0.f;   // this lane's share of the chunk's d(ln gamma)
+
+        for (int e = tid; e <= C; e += NTHR) sPow[e] = __builtin_amdgcn_exp2f(static_cast<float>(e) * l2g);
         if (norm)
-            for (int c = tid; c < DK; c += NTHR) {
-                const float z = sf[static_cast<size_t>(DK) * DV + c], dz = sr[static_cast<size_t>(DK) * DV + c];
-                sZ[c] = z;
-                sdZ[c] = dz;
-                if (want_dg) dl += static_cast<float>(n) * __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g) * z * dz;
+            for (int t = tid; t < C; t += NTHR) {
+                sInv[t] = t < n ? p.tok[2 * (tok0 + t)] : 0.f;
+                sDd[t] = t < n ? p.tok[2 * (tok0 + t) + 1] : 0.f;
             }
-    }
-    __syncthreads();
-
-    // ---- score tiles A and G (16 x 16, lower block triangle), taken
-    // transposed so that a lane holds four consecutive keys j of one query t
-    for (int tt = wave; tt < NB * NB; tt += kBwdWaves) {
-        const int I = tt / NB, J = tt % NB;
-        const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
-        if (J > I) {
-            st_group(sA + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
-            st_group(sG + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
-            if constexpr (SPLIT) st_group(sGl + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
-            continue;
-        }
-        f32x4 a = zero4(), h = zero4();
-        tile_mma_ll<DK>(a, sK + 16 * J * LDK, LDK, sQ + 16 * I * LDK, LDK, lane);
-        tile_mma_ll<DV>(h, sV + 16 * J * LDV, LDV, sO + 16 * I * LDV, LDV, lane);
-        const float inv = norm ? sInv[t] : 1.f, dd = norm ? sDd[t] : 0.f;
-        float av[4], gv[4];
+        {
+            // the chunk's loads (issued during the previous chunk's products
+            // with PF), then the LDS commits.  dO goes in as it is: 1/den_t is
+            // applied in float32 to the products (the value and normalizer
+            // parts of the normalized gradient nearly cancel).
+            if (!PF) load_job(job);
+            const bool need_s = STAGE_S || want_dg;
+            commit_tile<NTHR>(pq, sQ, static_cast<Op *>(nullptr), LDK, tid, [&](int, float x) { return phi_rt(x, elu); });
+            commit_tile<NTHR>(pk, sK, SPLIT ? sKl : static_cast<Op *>(nullptr), LDK, tid,
+                              [&](int, float x) { return phi_rt(x, elu); });
+            commit_tile<NTHR>(pv, sV, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+            commit_tile<NTHR>(po, sO, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+            commit_tile<NTHR>(pd, sdS, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+            if (need_s) {
+                if constexpr (STAGE_S) commit_tile<NTHR>(ps, sS, static_cast<Op *>(nullptr), LDV, tid, [](int, float x) { return x; });
+                if (want_dg) {
+                    // the state-coupling term n gamma^n <dS'_{c+1}, S'_c>, float32
+                    const float wf = static_cast<float>(n) * __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int j = j0 + i;
-            const bool on = j <= t && j < n;
-            const float w = on ? sPow[t - j] : 0.f;
-            const float hv = h[i] * inv + dd;   // dO'_t . v'_j
-            av[i] = w * a[i];
-            gv[i] = w * hv;
-            if (want_dg) dl += static_cast<float>(t - j) * av[i] * hv;
-            av[i] *= inv;   // dV = (A / den)^T dO
-        }
-        st_group(sA + t * LDC + j0, Gp::make(av[0], av[1], av[2], av[3]));
-        const auto gh = Gp::make(gv[0], gv[1], gv[2], gv[3]);
-        st_group(sG + t * LDC + j0, gh);
-        if constexpr (SPLIT) {
-            float r[4];
-            Gp::unpack(gh, r);
-            st_group(sGl + t * LDC + j0, Gp::make(gv[0] - r[0], gv[1] - r[1], gv[2] - r[2], gv[3] - r[3]));
-        }
-    }
-    __syncthreads();
-
-    // ---- dq: tiles (key block cb, query block I) of dphiQ^T; a lane ends
-    // with four consecutive key channels of one query token
-    for (int u = wave; u < NCB * NB; u += kBwdWaves) {
-        const int cb = u % NCB, I = u / NCB;
-        const int t = 16 * I + lr;
-        f32x4 acc = zero4(), xs = zero4();
-        // G phiK over key blocks J <= I (split operands: Gh Kh + Gh Kl + Gl Kh)
-#pragma unroll
-        for (int J = 0; J < NB; J += 2) {
-            if (J + 1 <= I) {
-                const auto k0 = kt_group<0>(sK, LDK, 16 * J, 16 * cb, lane), k1 = kt_group<0>(sK, LDK, 16 * J + 16, 16 * cb, lane);
-                const auto g0 = ld_group(sG + t * LDC + 16 * J + 4 * lg), g1 = ld_group(sG + t * LDC + 16 * J + 16 + 4 * lg);
-                mma32(acc, k0, k1, g0, g1);
-                if constexpr (SPLIT) {
-                    mma32(acc, kt_group<0>(sKl, LDK, 16 * J, 16 * cb, lane), kt_group<0>(sKl, LDK, 16 * J + 16, 16 * cb, lane),
-                          g0, g1);
-                    mma32(acc, k0, k1, ld_group(sGl + t * LDC + 16 * J + 4 * lg),
-                          ld_group(sGl + t * LDC + 16 * J + 16 + 4 * lg));
-                }
-            } else if (J <= I) {
-                const auto k0 = kt_group<0>(sK, LDK, 16 * J, 16 * cb, lane);
-                const auto g0 = ld_group(sG + t * LDC + 16 * J + 4 * lg);
-                mma16(acc, k0, g0);
-                if constexpr (SPLIT) {
-                    mma16(acc, kt_group<0>(sKl, LDK, 16 * J, 16 * cb, lane), g0);
-                    mma16(acc, k0, ld_group(sGl + t * LDC + 16 * J + 4 * lg));
+                    for (int i = 0; i < pd.PER; ++i) {
+                        if (!((pd.valid >> i) & 1u)) continue;   // lanes past the tile re-read its last vector
+                        const uint4 a4 = pd.r[i], b4 = ps.r[i];
+                        dl += wf * (__uint_as_float(a4.x) * __uint_as_float(b4.x) + __uint_as_float(a4.y) * __uint_as_float(b4.y) +
+                                    __uint_as_float(a4.z) * __uint_as_float(b4.z) + __uint_as_float(a4.w) * __uint_as_float(b4.w));
+                    }
                 }
             }
+            if (norm)
+                for (int c = tid; c < DK; c += NTHR) {
+                    const float z = sf[static_cast<size_t>(DK) * DV + c], dz = sr[static_cast<size_t>(DK) * DV + c];
+                    sZ[c] = z;
+                    sdZ[c] = dz;
+                    if (want_dg) dl += static_cast<float>(n) * __builtin_amdgcn_exp2f(static_cast<float>(n) * l2g) * z * dz;
+                }
         }
-        if constexpr (!STAGE_S) {
-            // the entering state: S'_c (key-major rows, float32 in the
-            // workspace) times dO_t, on the float32 matrix cores (normalized:
-            // it nearly cancels against the normalizer term below)
-            const float *srow = sf + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
-#pragma unroll
-            for (int i0 = 0; i0 < DV; i0 += 16) {
-                float o4[4];
-                Gp::unpack(ld_group(sO + t * LDV + i0 + 4 * lg), o4);
-                mma16(xs, *reinterpret_cast<const float4 *>(srow + i0), make_float4(o4[0], o4[1], o4[2], o4[3]));
-            }
-        } else {
-            // retention, bf16: S_c rows from LDS times dO_t
-            const Op *srow = sS + (16 * cb + lr) * LDV + 4 * lg;
-            const Op *orow = sO + t * LDV + 4 * lg;
-#pragma unroll
-            for (int i0 = 0; i0 + 32 <= DV; i0 += 32)
-                mma32(xs, ld_group(srow + i0), ld_group(srow + i0 + 16), ld_group(orow + i0), ld_group(orow + i0 + 16));
-            if constexpr (DV % 32 == 16) mma16(xs, ld_group(srow + DV - 16), ld_group(orow + DV - 16));
-        }
-        if (t < n) {
-            const int c0 = 16 * cb + 4 * lg;
-            const float wq = sPow[t + 1], inv = norm ? sInv[t] : 1.f, dd = norm ? sDd[t] : 0.f;
-            float raw[4], g[4];
-            load4(qh + static_cast<size_t>(t) * DK + c0, raw);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float X = wq * (xs[r] * inv + (norm ? dd * sZ[c0 + r] : 0.f));
-                if (want_dg) dl += static_cast<float>(t + 1) * to_f32(sQ[t * LDK + c0 + r]) * X;
-                g[r] = (acc[r] + X) * dphi_rt(raw[r], elu);
-            }
-            store4(static_cast<IO *>(p.dq) + (tok0 + t) * DK + c0, g);
-        }
-    }
-
-    // ---- dk: tiles (key block cb, key-token block J) of dphiK^T
-    for (int u = wave; u < NCB * NB; u += kBwdWaves) {
-        const int cb = u % NCB, J = u / NCB;
-        const int j = 16 * J + lr;
-        f32x4 acc = zero4(), ys = zero4();
-        // G^T phiQ over query blocks I >= J
-#pragma unroll
-        for (int s = 0; s < NB; s += 2) {
-            const int I = J + s;
-            if (I + 1 < NB)
-                mma32(acc, kt_group<0>(sQ, LDK, 16 * I, 16 * cb, lane), kt_group<0>(sQ, LDK, 16 * I + 16, 16 * cb, lane),
-                      kt_group<0>(sG, LDC, 16 * I, 16 * J, lane), kt_group<0>(sG, LDC, 16 * I + 16, 16 * J, lane));
-            else if (I < NB)
-                mma16(acc, kt_group<0>(sQ, LDK, 16 * I, 16 * cb, lane), kt_group<0>(sG, LDC, 16 * I, 16 * J, lane));
-        }
-        const Op *vrow = sV + j * LDV + 4 * lg;
-        if constexpr (!STAGE_S) {
-            // the leaving cotangent: dS'_{c+1} rows (key-major, float32 in the
-            // workspace) times v_j, on the float32 matrix cores (normalized:
-            // it nearly cancels against dz below)
-            const float *drow = sr + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
-#pragma unroll
-            for (int i0 = 0; i0 < DV; i0 += 16) {
-                float v4[4];
-                Gp::unpack(ld_group(vrow + i0), v4);
-                mma16(ys, *reinterpret_cast<const float4 *>(drow + i0), make_float4(v4[0], v4[1], v4[2], v4[3]));
-            }
-        } else {
-            // retention, bf16: dS_{c+1} rows from LDS times v_j
-            const Op *drow = sdS + (16 * cb + lr) * LDV + 4 * lg;
-#pragma unroll
-            for (int i0 = 0; i0 + 32 <= DV; i0 += 32)
-                mma32(ys, ld_group(drow + i0), ld_group(drow + i0 + 16), ld_group(vrow + i0), ld_group(vrow + i0 + 16));
-            if constexpr (DV % 32 == 16) mma16(ys, ld_group(drow + DV - 16), ld_group(vrow + DV - 16));
-        }
-        if (j < n) {
-            const int c0 = 16 * cb + 4 * lg;
-            const float wk = sPow[n - 1 - j];
-            float raw[4], g[4];
-            load4(kh + static_cast<size_t>(j) * DK + c0, raw);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float Y = wk * (ys[r] + (norm ? sdZ[c0 + r] : 0.f));
-                if (want_dg)
-                    dl += static_cast<float>(n - 1 - j) *
-                          (to_f32(sK[j * LDK + c0 + r]) + (SPLIT ? to_f32(sKl[j * LDK + c0 + r]) : 0.f)) * Y;
-                g[r] = (acc[r] + Y) * dphi_rt(raw[r], elu);
-            }
-            store4(static_cast<IO *>(p.dk) + (tok0 + j) * DK + c0, g);
-        }
-    }
-
-    // ---- dv: tiles (value block ib, token block J) of dV^T
-    for (int u = wave; u < NIB * NB; u += kBwdWaves) {
-        const int ib = u % NIB, J = u / NIB;
-        const int j = 16 * J + lr;
-        f32x4 acc = zero4(), vs = zero4();
-        // (A / den)^T dO over query blocks I >= J
-#pragma unroll
-        for (int s = 0; s < NB; s += 2) {
-            const int I = J + s;
-            if (I + 1 < NB)
-                mma32(acc, kt_group<0>(sO, LDV, 16 * I, 16 * ib, lane), kt_group<0>(sO, LDV, 16 * I + 16, 16 * ib, lane),
-                      kt_group<0>(sA, LDC, 16 * I, 16 * J, lane), kt_group<0>(sA, LDC, 16 * I + 16, 16 * J, lane));
-            else if (I < NB)
-                mma16(acc, kt_group<0>(sO, LDV, 16 * I, 16 * ib, lane), kt_group<0>(sA, LDC, 16 * I, 16 * J, lane));
-        }
-        // dS_{c+1} phi(k_j): the cotangent's value rows by transposing reads
-        const Op *krow = sK + j * LDK + 4 * lg;
-#pragma unroll
-        for (int c0 = 0; c0 + 32 <= DK; c0 += 32)
-            mma32(vs, kt_group<0>(sdS, LDV, c0, 16 * ib, lane), kt_group<0>(sdS, LDV, c0 + 16, 16 * ib, lane),
-                  ld_group(krow + c0), ld_group(krow + c0 + 16));
-        if constexpr (DK % 32 == 16) mma16(vs, kt_group<0>(sdS, LDV, DK - 16, 16 * ib, lane), ld_group(krow + DK - 16));
-        if (j < n) {
-            const float wk = sPow[n - 1 - j];
-            float g[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) g[r] = acc[r] + wk * vs[r];
-            store4(static_cast<IO *>(p.dv) + (tok0 + j) * DV + 16 * ib + 4 * lg, g);
-        }
-    }
-
-    if (want_dg) {
-        dl = group_sum<64>(dl);
-        if (lane == 0) sRed[wave] = dl;
         __syncthreads();
-        if (tid == 0) {
-            float s = 0.f;
-            for (int w = 0; w < kBwdWaves; ++w) s += sRed[w];
-            p.part[static_cast<size_t>(bh) * N + ch] = s;
+        if (PF && job + static_cast<int>(gridDim.x) < jobs) load_job(job + gridDim.x);
+
+        // ---- score tiles A and G (16 x 16, lower block triangle), taken
+        // transposed so that a lane holds four consecutive keys j of one query t
+        for (int tt = wave; tt < NB * NB; tt += kBwdWaves) {
+            const int I = tt / NB, J = tt % NB;
+            const int t = 16 * I + lr, j0 = 16 * J + 4 * lg;
+            if (J > I) {
+                st_group(sA + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
+                st_group(sG + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
+                if constexpr (SPLIT) st_group(sGl + t * LDC + j0, Gp::make(0.f, 0.f, 0.f, 0.f));
+                continue;
+            }
+            f32x4 a = zero4(), h = zero4();
+            tile_mma_ll<DK>(a, sK + 16 * J * LDK, LDK, sQ + 16 * I * LDK, LDK, lane);
+            tile_mma_ll<DV>(h, sV + 16 * J * LDV, LDV, sO + 16 * I * LDV, LDV, lane);
+            const float inv = norm ? sInv[t] : 1.f, dd = norm ? sDd[t] : 0.f;
+            float av[4], gv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int j = j0 + i;
+                const bool on = j <= t && j < n;
+                const float w = on ? sPow[t - j] : 0.f;
+                const float hv = h[i] * inv + dd;   // dO'_t . v'_j
+                av[i] = w * a[i];
+                gv[i] = w * hv;
+                if (want_dg) dl += static_cast<float>(t - j) * av[i] * hv;
+                av[i] *= inv;   // dV = (A / den)^T dO
+            }
+            st_group(sA + t * LDC + j0, Gp::make(av[0], av[1], av[2], av[3]));
+            const auto gh = Gp::make(gv[0], gv[1], gv[2], gv[3]);
+            st_group(sG + t * LDC + j0, gh);
+            if constexpr (SPLIT) {
+                float r[4];
+                Gp::unpack(gh, r);
+                st_group(sGl + t * LDC + j0, Gp::make(gv[0] - r[0], gv[1] - r[1], gv[2] - r[2], gv[3] - r[3]));
+            }
         }
+        __syncthreads();
+
+        // ---- dq: tiles (key block cb, query block I) of dphiQ^T; a lane ends
+        // with four consecutive key channels of one query token
+        for (int u = wave; u < NCB * NB; u += kBwdWaves) {
+            const int cb = u % NCB, I = u / NCB;
+            const int t = 16 * I + lr;
+            f32x4 acc = zero4(), xs = zero4();
+            // G phiK over key blocks J <= I (split operands: Gh Kh + Gh Kl + Gl Kh)
+#pragma unroll
+            for (int J = 0; J < NB; J += 2) {
+                if (J + 1 <= I) {
+                    const auto k0 = kt_group<0>(sK, LDK, 16 * J, 16 * cb, lane), k1 = kt_group<0>(sK, LDK, 16 * J + 16, 16 * cb, lane);
+                    const auto g0 = ld_group(sG + t * LDC + 16 * J + 4 * lg), g1 = ld_group(sG + t * LDC + 16 * J + 16 + 4 * lg);
+                    mma32(acc, k0, k1, g0, g1);
+                    if constexpr (SPLIT) {
+                        mma32(acc, kt_group<0>(sKl, LDK, 16 * J, 16 * cb, lane), kt_group<0>(sKl, LDK, 16 * J + 16, 16 * cb, lane),
+                              g0, g1);
+                        mma32(acc, k0, k1, ld_group(sGl + t * LDC + 16 * J + 4 * lg),
+                              ld_group(sGl + t * LDC + 16 * J + 16 + 4 * lg));
+                    }
+                } else if (J <= I) {
+                    const auto k0 = kt_group<0>(sK, LDK, 16 * J, 16 * cb, lane);
+                    const auto g0 = ld_group(sG + t * LDC + 16 * J + 4 * lg);
+                    mma16(acc, k0, g0);
+                    if constexpr (SPLIT) {
+                        mma16(acc, kt_group<0>(sKl, LDK, 16 * J, 16 * cb, lane), g0);
+                        mma16(acc, k0, ld_group(sGl + t * LDC + 16 * J + 4 * lg));
+                    }
+                }
+            }
+            if constexpr (!STAGE_S) {
+                // the entering state: S'_c (key-major rows, float32 in the
+                // workspace) times dO_t, on the float32 matrix cores (normalized:
+                // it nearly cancels against the normalizer term below)
+                const float *srow = sf + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
+#pragma unroll
+                for (int i0 = 0; i0 < DV; i0 += 16) {
+                    float o4[4];
+                    Gp::unpack(ld_group(sO + t * LDV + i0 + 4 * lg), o4);
+                    mma16(xs, *reinterpret_cast<const float4 *>(srow + i0), make_float4(o4[0], o4[1], o4[2], o4[3]));
+                }
+            } else {
+                // retention, bf16: S_c rows from LDS times dO_t
+                const Op *srow = sS + (16 * cb + lr) * LDV + 4 * lg;
+                const Op *orow = sO + t * LDV + 4 * lg;
+#pragma unroll
+                for (int i0 = 0; i0 + 32 <= DV; i0 += 32)
+                    mma32(xs, ld_group(srow + i0), ld_group(srow + i0 + 16), ld_group(orow + i0), ld_group(orow + i0 + 16));
+                if constexpr (DV % 32 == 16) mma16(xs, ld_group(srow + DV - 16), ld_group(orow + DV - 16));
+            }
+            if (t < n) {
+                const int c0 = 16 * cb + 4 * lg;
+                const float wq = sPow[t + 1], inv = norm ? sInv[t] : 1.f, dd = norm ? sDd[t] : 0.f;
+                float dph[4], g[4];
+                if constexpr (PF) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dph[r] = elu ? fminf(to_f32(sQ[t * LDK + c0 + r]), 1.f) : 1.f;
+                } else {
+                    float raw[4];
+                    load4(qh + static_cast<size_t>(t) * DK + c0, raw);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dph[r] = dphi_rt(raw[r], elu);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float X = wq * (xs[r] * inv + (norm ? dd * sZ[c0 + r] : 0.f));
+                    if (want_dg) dl += static_cast<float>(t + 1) * to_f32(sQ[t * LDK + c0 + r]) * X;
+                    g[r] = (acc[r] + X) * dph[r];
+                }
+                store4(static_cast<IO *>(p.dq) + (tok0 + t) * DK + c0, g);
+            }
+        }
+
+        // ---- dk: tiles (key block cb, key-token block J) of dphiK^T
+        for (int u = wave; u < NCB * NB; u += kBwdWaves) {
+            const int cb = u % NCB, J = u / NCB;
+            const int j = 16 * J + lr;
+            f32x4 acc = zero4(), ys = zero4();
+            // G^T phiQ over query blocks I >= J
+#pragma unroll
+            for (int s = 0; s < NB; s += 2) {
+                const int I = J + s;
+                if (I + 1 < NB)
+                    mma32(acc, kt_group<0>(sQ, LDK, 16 * I, 16 * cb, lane), kt_group<0>(sQ, LDK, 16 * I + 16, 16 * cb, lane),
+                          kt_group<0>(sG, LDC, 16 * I, 16 * J, lane), kt_group<0>(sG, LDC, 16 * I + 16, 16 * J, lane));
+                else if (I < NB)
+                    mma16(acc, kt_group<0>(sQ, LDK, 16 * I, 16 * cb, lane), kt_group<0>(sG, LDC, 16 * I, 16 * J, lane));
+            }
+            const Op *vrow = sV + j * LDV + 4 * lg;
+            if constexpr (!STAGE_S) {
+                // the leaving cotangent: dS'_{c+1} rows (key-major, float32 in the
+                // workspace) times v_j, on the float32 matrix cores (normalized:
+                // it nearly cancels against dz below)
+                const float *drow = sr + static_cast<size_t>(16 * cb + lr) * DV + 4 * lg;
+#pragma unroll
+                for (int i0 = 0; i0 < DV; i0 += 16) {
+                    float v4[4];
+                    Gp::unpack(ld_group(vrow + i0), v4);
+                    mma16(ys, *reinterpret_cast<const float4 *>(drow + i0), make_float4(v4[0], v4[1], v4[2], v4[3]));
+                }
+            } else {
+                // retention, bf16: dS_{c+1} rows from LDS times v_j
+                const Op *drow = sdS + (16 * cb + lr) * LDV + 4 * lg;
+#pragma unroll
+                for (int i0 = 0; i0 + 32 <= DV; i0 += 32)
+                    mma32(ys, ld_group(drow + i0), ld_group(drow + i0 + 16), ld_group(vrow + i0), ld_group(vrow + i0 + 16));
+                if constexpr (DV % 32 == 16) mma16(ys, ld_group(drow + DV - 16), ld_group(vrow + DV - 16));
+            }
+            if (j < n) {
+                const int c0 = 16 * cb + 4 * lg;
+                const float wk = sPow[n - 1 - j];
+                float dph[4], g[4];
+                if constexpr (PF) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        dph[r] = elu ? fminf(to_f32(sK[j * LDK + c0 + r]) + (SPLIT ? to_f32(sKl[j * LDK + c0 + r]) : 0.f), 1.f) : 1.f;
+                } else {
+                    float raw[4];
+                    load4(kh + static_cast<size_t>(j) * DK + c0, raw);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dph[r] = dphi_rt(raw[r], elu);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float Y = wk * (ys[r] + (norm ? sdZ[c0 + r] : 0.f));
+                    if (want_dg)
+                        dl += static_cast<float>(n - 1 - j) *
+                              (to_f32(sK[j * LDK + c0 + r]) + (SPLIT ? to_f32(sKl[j * LDK + c0 + r]) : 0.f)) * Y;
+                    g[r] = (acc[r] + Y) * dph[r];
+                }
+                store4(static_cast<IO *>(p.dk) + (tok0 + j) * DK + c0, g);
+            }
+        }
+
+        // ---- dv: tiles (value block ib, token block J) of dV^T
+        for (int u = wave; u < NIB * NB; u += kBwdWaves) {
+            const int ib = u % NIB, J = u / NIB;
+            const int j = 16 * J + lr;
+            f32x4 acc = zero4(), vs = zero4();
+            // (A / den)^T dO over query blocks I >= J
+#pragma unroll
+            for (int s = 0; s < NB; s += 2) {
+                const int I = J + s;
+                if (I + 1 < NB)
+                    mma32(acc, kt_group<0>(sO, LDV, 16 * I, 16 * ib, lane), kt_group<0>(sO, LDV, 16 * I + 16, 16 * ib, lane),
+                          kt_group<0>(sA, LDC, 16 * I, 16 * J, lane), kt_group<0>(sA, LDC, 16 * I + 16, 16 * J, lane));
+                else if (I < NB)
+                    mma16(acc, kt_group<0>(sO, LDV, 16 * I, 16 * ib, lane), kt_group<0>(sA, LDC, 16 * I, 16 * J, lane));
+            }
+            // dS_{c+1} phi(k_j): the cotangent's value rows by transposing reads
+            const Op *krow = sK + j * LDK + 4 * lg;
+#pragma unroll
+            for (int c0 = 0; c0 + 32 <= DK; c0 += 32)
+                mma32(vs, kt_group<0>(sdS, LDV, c0, 16 * ib, lane), kt_group<0>(sdS, LDV, c0 + 16, 16 * ib, lane),
+                      ld_group(krow + c0), ld_group(krow + c0 + 16));
+            if constexpr (DK % 32 == 16) mma16(vs, kt_group<0>(sdS, LDV, DK - 16, 16 * ib, lane), ld_group(krow + DK - 16));
+            if (j < n) {
+                const float wk = sPow[n - 1 - j];
+                float g[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) g[r] = acc[r] + wk * vs[r];
+                store4(static_cast<IO *>(p.dv) + (tok0 + j) * DV + 16 * ib + 4 * lg, g);
+            }
+        }
+
+        if (want_dg) {
+            dl = group_sum<64>(dl);
+            if (lane == 0) sRed[wave] = dl;
+            __syncthreads();
+            if (tid == 0) {
+                float s = 0.f;
+                for (int w = 0; w < kBwdWaves; ++w) s += sRed[w];
+                p.part[static_cast<size_t>(bh) * N + ch] = s;
+            }
+        }
+        __syncthreads();   // the next chunk overwrites every LDS tile and sRed
     }
 }
 
@@ -1014,7 +1055,10 @@ hipError_t bwd_launch(const BwdArgs &a) {
         if (wgs) hipLaunchKernelGGL((bwd_increments_kernel<DT, DK, DV, C, false>), dim3(wgs), blk, 0, a.stream, p);
         hipLaunchKernelGGL(bwd_scan_kernel, dim3(scan_blocks), dim3(256), 0, a.stream, p, DK, DV, C, 3);
     }
-    if (wgs) hipLaunchKernelGGL((bwd_grad_kernel<DT, DK, DV, C, NORM>), dim3(wgs), blk, 0, a.stream, p);
+    // the retention bf16 gradient kernel is persistent: one workgroup per CU
+    // (its LDS allows one), each walking the chunks with a stride of the grid
+    const uint32_t grad_wgs = BwdLds<DT, DK, DV, C, NORM>::STAGE_S ? std::min<uint32_t>(wgs, kGradPersistWGs) : wgs;
+    if (wgs) hipLaunchKernelGGL((bwd_grad_kernel<DT, DK, DV, C, NORM>), dim3(grad_wgs), blk, 0, a.stream, p);
     if (a.dgate) hipLaunchKernelGGL(bwd_dgate_kernel, dim3(a.H), dim3(256), 0, a.stream, p);
     return hipGetLastError();
 }
