@@ -180,12 +180,14 @@ def test_bwd_retention_training_shape_sampled_heads():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("kind,H,dk,dv", [("ret", 3, 64, 64), ("ret_elu", 8, 128, 32), ("ret", 8, 32, 128)])
+@pytest.mark.parametrize("kind,H,dk,dv", [("ret", 3, 64, 64), ("ret_elu", 8, 128, 32), ("ret", 8, 32, 128),
+                                           ("ret_elu", 16, 64, 64)])
 def test_bwd_retention_many_chunks(kind, H, dk, dv, dtype):
     """Retention over many chunks (18 of 64 tokens, the last one ragged), where
     the chunk states come from one chain per head, direction and value block:
     every gradient against the oracle, with 3 heads and with 8 (the two
-    workgroup orders)."""
+    workgroup orders), and with 16 (288 chunk-heads: the persistent bf16
+    gradient kernel's 256 workgroups take two chunks each for some)."""
     T = 17 * 64 + 29
     w, inp, cot = _case(kind, dtype, dk, dv, 1, H, T, seed=251)
     print("bwd chain", kind, dtype, H, dk, dv, "T", T, flush=True)
