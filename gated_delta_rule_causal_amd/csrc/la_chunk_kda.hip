@@ -302,20 +302,34 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
 
     // ---- Q o e^b, K o e^{b_n - b}, e^{b_n} and P (its lower blocks)
     {
+        // four channels (tokens) per thread and store
         Op *qt = reinterpret_cast<Op *>(rec + R::QT);
         Op *kt = reinterpret_cast<Op *>(rec + R::KT);
-        for (int e = tid; e < C * DK; e += NTHR) {
-            const int t = e / DK, ch = e % DK;
-            const float b = sB[t * LDB + ch], bn = sB[(n - 1) * LDB + ch];
-            from_f32(qt[e], to_f32(sQ[t * LDQ + ch]) * __builtin_amdgcn_exp2f(b));
-            from_f32(kt[e], to_f32(sK[t * LDQ + ch]) * __builtin_amdgcn_exp2f(bn - b));
+        for (int e = tid; e < C * DK / 4; e += NTHR) {
+            const int t = e / (DK / 4), ch = (e % (DK / 4)) * 4;
+            const float4 b4 = *reinterpret_cast<const float4 *>(sB + t * LDB + ch);
+            const float4 n4 = *reinterpret_cast<const float4 *>(sB + (n - 1) * LDB + ch);
+            const float bb[4] = {b4.x, b4.y, b4.z, b4.w}, bn[4] = {n4.x, n4.y, n4.z, n4.w};
+            float xq[4], xk[4];
+            Gp::unpack(ld_group(sQ + t * LDQ + ch), xq);
+            Gp::unpack(ld_group(sK + t * LDQ + ch), xk);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xq[i] *= __builtin_amdgcn_exp2f(bb[i]);
+                xk[i] *= __builtin_amdgcn_exp2f(bn[i] - bb[i]);
+            }
+            st_group(qt + t * DK + ch, Gp::make(xq[0], xq[1], xq[2], xq[3]));
+            st_group(kt + t * DK + ch, Gp::make(xk[0], xk[1], xk[2], xk[3]));
         }
         float *ec = reinterpret_cast<float *>(rec + R::EC);
         for (int ch = tid; ch < DK; ch += NTHR) ec[ch] = __builtin_amdgcn_exp2f(sB[(n - 1) * LDB + ch]);
         Op *pt = reinterpret_cast<Op *>(rec + R::PT);
-        for (int e = tid; e < C * C; e += NTHR) {
-            const int t = e / C, j = e % C;
-            if (j / 16 <= t / 16) from_f32(pt[e], sP[t * LDA + j]);
+        for (int e = tid; e < C * C / 4; e += NTHR) {
+            const int t = e / (C / 4), j = (e % (C / 4)) * 4;
+            if (j / 16 <= t / 16) {
+                const float4 x = *reinterpret_cast<const float4 *>(sP + t * LDA + j);
+                st_group(pt + t * C + j, Gp::make(x.x, x.y, x.z, x.w));
+            }
         }
     }
 }
