@@ -416,14 +416,21 @@ __global__ void __launch_bounds__(NW * 64) kda_chain_kernel(const ChunkParams p,
         if (loader) {
             load(0);
             store(0);
+            // two buffers: the staging waves hold chunk c + 1 in registers from
+            // step c - 1 on, so its loads have a whole step to land
+            if (NBUF == 2 && nchunks > 1) load(1);
         }
         __syncthreads();
     }
     for (int c = 0; c < nchunks; ++c) {
         const int b = NBUF == 2 ? (c & 1) : 0;
-        if (loader && c + 1 < nchunks) {
-            load(c + 1);
-            if constexpr (NBUF == 2) store(b ^ 1);   // buffer b ^ 1 was last read in chunk c - 1
+        if constexpr (NBUF == 2) {
+            if (loader && c + 1 < nchunks) {
+                store(b ^ 1);                        // buffer b ^ 1 was last read in chunk c - 1
+                if (c + 2 < nchunks) load(c + 2);    // registers free once stored
+            }
+        } else {
+            if (loader && c + 1 < nchunks) load(c + 1);
         }
         if (state_wave) {
             const Op *sQc = sQt + b * C * LDK, *sWc = sWt + b * C * LDK, *sKc = sKt + b * C * LDK;
