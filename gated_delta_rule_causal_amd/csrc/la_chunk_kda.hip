@@ -76,6 +76,13 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     __shared__ __align__(16) float sP[C * LDA];      // P (lower), float32
     __shared__ __align__(16) float sT[NB * 16 * LDT]; // (I + A_II)^{-1}, float32
     __shared__ float sBeta[C];
+    // bf16 inputs: the solve's products take A (off-diagonal blocks) and the
+    // diagonal inverses as split operands x = hi + lo (both bf16), two bf16
+    // matrix-core steps per 16 x 16 x 16 product instead of four fp32 ones
+    constexpr bool SPL = sizeof(Op) == 2;
+    constexpr int LDA2 = C + 4, LDT2 = 16 + 4;        // bf16 rows, 2 mod 4 dwords apart
+    __shared__ __align__(16) Op sAh[SPL ? C * LDA2 : 4], sAl[SPL ? C * LDA2 : 4];
+    __shared__ __align__(16) Op sTh[SPL ? NB * 16 * LDT2 : 4], sTl[SPL ? NB * 16 * LDT2 : 4];
     constexpr int LDVV = DV + 16 / (int)sizeof(Op);
 
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -191,7 +198,16 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
             for (int i = 0; i < 4; ++i) {
                 const int tq = 16 * I + 4 * lg + i, jk = 16 * J + lr;
                 sP[tq * LDA + jk] = !diag || jk <= tq ? accP[i] : 0.f;
-                sA[tq * LDA + jk] = !diag || jk < tq ? sBeta[tq] * accA[i] : 0.f;
+                const float va = !diag || jk < tq ? sBeta[tq] * accA[i] : 0.f;
+                sA[tq * LDA + jk] = va;
+                if constexpr (SPL) {
+                    if (!diag) {
+                        Op h;
+                        from_f32(h, va);
+                        sAh[tq * LDA2 + jk] = h;
+                        from_f32(sAl[tq * LDA2 + jk], va - to_f32(h));
+                    }
+                }
             }
         } else {
             // diagonal block: exact.  Lane (j, cq): key token j of the block and
@@ -250,7 +266,15 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
                 x[i] = s0 + s1;
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sT[(16 * I + i) * LDT + lane] = x[i];
+            for (int i = 0; i < 16; ++i) {
+                sT[(16 * I + i) * LDT + lane] = x[i];
+                if constexpr (SPL) {
+                    Op h;
+                    from_f32(h, x[i]);
+                    sTh[(16 * I + i) * LDT2 + lane] = h;
+                    from_f32(sTl[(16 * I + i) * LDT2 + lane], x[i] - to_f32(h));
+                }
+            }
         }
     }
     __syncthreads();
@@ -259,7 +283,8 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
     // beta o V], by 16-token block rows: X_I = T_II (R_I - sum_{J<I} A_IJ X_J).
     // The columns are independent, so each wave solves its own 16-column tiles
     // with no barrier; a result tile (rows = tokens) is already the B operand
-    // of the next product.  float32 matrix cores throughout.
+    // of the next product.  float32 inputs: float32 matrix cores; bf16 inputs:
+    // split operands (hi hi + lo hi + hi lo), float32 accumulation.
     {
         const int lr = lane & 15, lg = lane >> 4;
         constexpr int NCT = (DK + DV) / 16;
@@ -267,6 +292,7 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
             const int col = 16 * ct + lr;
             const bool wcol = col < DK;
             f32x4 X[NB];
+            typename Gp::type xh[NB], xl[NB];   // SPL: X as split B operands
 #pragma unroll
             for (int I = 0; I < NB; ++I) {
                 f32x4 y;
@@ -281,14 +307,37 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
                     y[r] = wcol ? sBeta[t] * to_f32(sK[t * LDQ + col]) * __builtin_amdgcn_exp2f(sB[t * LDB + col])
                                 : sBeta[t] * vv;
                 }
-#pragma unroll
-                for (int J = 0; J < I; ++J) {
-                    const float4 a = *reinterpret_cast<const float4 *>(sA + (16 * I + lr) * LDA + 16 * J + 4 * lg);
-                    mma16(y, make_float4(-a.x, -a.y, -a.z, -a.w), make_float4(X[J][0], X[J][1], X[J][2], X[J][3]));
-                }
                 X[I] = zero4();
-                mma16(X[I], *reinterpret_cast<const float4 *>(sT + (16 * I + lr) * LDT + 4 * lg),
-                      make_float4(y[0], y[1], y[2], y[3]));
+                if constexpr (SPL) {
+                    // y - A_IJ X_J with -A_IJ (sign bits flipped), then T_II y
+#pragma unroll
+                    for (int J = 0; J < I; ++J) {
+                        uint2 ah = ld_group(sAh + (16 * I + lr) * LDA2 + 16 * J + 4 * lg);
+                        uint2 al = ld_group(sAl + (16 * I + lr) * LDA2 + 16 * J + 4 * lg);
+                        ah.x ^= 0x80008000u; ah.y ^= 0x80008000u; al.x ^= 0x80008000u; al.y ^= 0x80008000u;
+                        mma32(y, ah, al, xh[J], xh[J]);
+                        mma16(y, ah, xl[J]);
+                    }
+                    const uint2 th = ld_group(sTh + (16 * I + lr) * LDT2 + 4 * lg);
+                    const uint2 tl = ld_group(sTl + (16 * I + lr) * LDT2 + 4 * lg);
+                    float r[4];
+                    const uint2 yh = Gp::make(y[0], y[1], y[2], y[3]);
+                    Gp::unpack(yh, r);
+                    const uint2 yl = Gp::make(y[0] - r[0], y[1] - r[1], y[2] - r[2], y[3] - r[3]);
+                    mma32(X[I], th, tl, yh, yh);
+                    mma16(X[I], th, yl);
+                    xh[I] = Gp::make(X[I][0], X[I][1], X[I][2], X[I][3]);
+                    Gp::unpack(xh[I], r);
+                    xl[I] = Gp::make(X[I][0] - r[0], X[I][1] - r[1], X[I][2] - r[2], X[I][3] - r[3]);
+                } else {
+#pragma unroll
+                    for (int J = 0; J < I; ++J) {
+                        const float4 a = *reinterpret_cast<const float4 *>(sA + (16 * I + lr) * LDA + 16 * J + 4 * lg);
+                        mma16(y, make_float4(-a.x, -a.y, -a.z, -a.w), make_float4(X[J][0], X[J][1], X[J][2], X[J][3]));
+                    }
+                    mma16(X[I], *reinterpret_cast<const float4 *>(sT + (16 * I + lr) * LDT + 4 * lg),
+                          make_float4(y[0], y[1], y[2], y[3]));
+                }
             }
             // rows 16 I + 4 lg + r of column col, to the record
             Op *dst = wcol ? reinterpret_cast<Op *>(rec + R::WT) + col : reinterpret_cast<Op *>(rec + R::UP) + (col - DK);
