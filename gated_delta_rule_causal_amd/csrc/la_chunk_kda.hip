@@ -162,9 +162,8 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
         if (fast) {
             const int t = 16 * I + lr, j = 16 * J + lr;
             f32x4 accP = zero4(), accA = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < DK; k0 += 16) {
-                const int ch = k0 + 4 * lg;
+            // the scaled operands of channels ch .. ch + 3 (f32)
+            auto operands = [&](int ch, float (&qs)[4], float (&ks)[4], float (&kj)[4]) {
                 // four channels of each row at once (16-byte rows of b, 8- or
                 // 16-byte groups of q and k)
                 const float4 b4t = *reinterpret_cast<const float4 *>(sB + t * LDB + ch);
@@ -176,7 +175,6 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
                 Gp::unpack(ld_group(sK + j * LDQ + ch), xj);
                 const float bt[4] = {b4t.x, b4t.y, b4t.z, b4t.w}, bjv[4] = {b4j.x, b4j.y, b4j.z, b4j.w};
                 const float brv[4] = {b4r.x, b4r.y, b4r.z, b4r.w};
-                float qs[4], ks[4], kj[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float ft = __builtin_amdgcn_exp2f(bt[i] - brv[i]);
@@ -185,12 +183,43 @@ __global__ void __launch_bounds__(kKdaPrepThreads) kda_prep_kernel(const ChunkPa
                     ks[i] = xt[i] * ft;
                     kj[i] = xj[i] * fj;
                 }
-                // float32 operands whatever the input type: the scaled operands
-                // are not exact in bf16, and rounding them would be amplified
-                // where q.k cancels
-                const float4 gk = make_float4(kj[0], kj[1], kj[2], kj[3]);
-                mma16(accP, make_float4(qs[0], qs[1], qs[2], qs[3]), gk);
-                mma16(accA, make_float4(ks[0], ks[1], ks[2], ks[3]), gk);
+            };
+            // the scaled operands are not exact in bf16, and rounding them once
+            // would be amplified where q.k cancels: float32 operands for float32
+            // inputs; for bf16 inputs split operands x = hi + lo (both bf16,
+            // ~16 significant bits), hi hi + lo hi + hi lo on bf16 matrix cores
+            if constexpr (SPL && DK % 32 == 0) {
+                auto split = [&](const float (&x)[4], uint2 &h, uint2 &l) {
+                    float rr[4];
+                    h = Gp::make(x[0], x[1], x[2], x[3]);
+                    Gp::unpack(h, rr);
+                    l = Gp::make(x[0] - rr[0], x[1] - rr[1], x[2] - rr[2], x[3] - rr[3]);
+                };
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += 32) {
+                    float qs0[4], ks0[4], kj0[4], qs1[4], ks1[4], kj1[4];
+                    operands(k0 + 4 * lg, qs0, ks0, kj0);
+                    operands(k0 + 16 + 4 * lg, qs1, ks1, kj1);
+                    uint2 qh0, ql0, qh1, ql1, sh0, sl0, sh1, sl1, jh0, jl0, jh1, jl1;
+                    split(qs0, qh0, ql0); split(qs1, qh1, ql1);
+                    split(ks0, sh0, sl0); split(ks1, sh1, sl1);
+                    split(kj0, jh0, jl0); split(kj1, jh1, jl1);
+                    mma32(accP, qh0, qh1, jh0, jh1);
+                    mma32(accP, ql0, ql1, jh0, jh1);
+                    mma32(accP, qh0, qh1, jl0, jl1);
+                    mma32(accA, sh0, sh1, jh0, jh1);
+                    mma32(accA, sl0, sl1, jh0, jh1);
+                    mma32(accA, sh0, sh1, jl0, jl1);
+                }
+            } else {
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += 16) {
+                    float qs[4], ks[4], kj[4];
+                    operands(k0 + 4 * lg, qs, ks, kj);
+                    const float4 gk = make_float4(kj[0], kj[1], kj[2], kj[3]);
+                    mma16(accP, make_float4(qs[0], qs[1], qs[2], qs[3]), gk);
+                    mma16(accA, make_float4(ks[0], ks[1], ks[2], ks[3]), gk);
+                }
             }
             // result layout: lane holds rows (queries) 16 I + 4 lg + i of column
             // (key) 16 J + lr; on the diagonal keep j <= t (P) and j < t (A)
