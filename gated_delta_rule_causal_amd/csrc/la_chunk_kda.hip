@@ -26,9 +26,11 @@
 //     between query and key, so both operand factors are at most 1; on it
 //     exactly, from running products of the gates), the triangular solve for
 //     W and U' by 16-token blocks (the inverse of each diagonal block by
-//     forward substitution, then X_I = T_II (R_I - sum_{J<I} A_IJ X_J) on the
-//     float32 matrix cores, each wave solving its own 16-column tiles), and
-//     the scaled tiles, written to a workspace record per chunk;
+//     forward substitution, then X_I = T_II (R_I - sum_{J<I} A_IJ X_J), each
+//     wave solving its own 16-column tiles), and the scaled tiles, written to
+//     a workspace record per chunk.  The score and solve products take float32
+//     operands (float32 matrix cores) for float32 inputs and split bf16
+//     operands x = hi + lo (bf16 matrix cores) for bf16 inputs;
 //   kda_chain_kernel one workgroup per (head, block of value channels), the
 //     chunks in order: the state-dependent products only, the state slice of
 //     each wave held in matrix-core accumulators for the whole sequence.
